@@ -1,0 +1,152 @@
+"""Pins of the oracle's convolution, backward and forces: autograd of an
+independent forward, finite differences, linearity identities, closed forms on
+two-atom systems, and O(3), translation and permutation symmetry."""
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import conv, fd, nbr, paths, sh
+
+
+def _problem(k, csr=None, **over):
+    d = workloads.generate(k)
+    c = d["cfg"]
+    L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"])
+    pos, cell = over.get("pos", d["pos"]), over.get("cell", d["cell"])
+    rp, src, shift = csr if csr is not None else nbr.binned(d["pos"], d["cell"], c["r_cut"])
+    s = conv.scale_for(c, len(pos), rp[-1])
+    return conv.Problem(L, pos, cell, rp, src, shift, over.get("h", d["h"]), d["W"],
+                        c["r_cut"], s, d["G"]), d
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    prob, d = _problem(0)
+    return prob, d, prob.forward(), prob.backward()
+
+
+def test_backward_matches_autograd(tiny):
+    from oracle import autograd_check as ag
+    prob, d, out, b = tiny
+    a = ag.grads(prob.L, prob.pos, prob.cell, prob.row_ptr, prob.src, prob.shift,
+                 d["h"], d["W"], d["G"], prob.r_cut, prob.scale)
+    np.testing.assert_allclose(out, a["out"], rtol=0, atol=1e-13 * np.abs(out).max())
+    for k in ("dh", "dR", "dY", "F"):
+        np.testing.assert_allclose(b[k], a[k], rtol=0, atol=1e-12 * np.abs(a[k]).max())
+
+
+def test_forces_by_finite_differences(tiny):
+    prob, d, out, b = tiny
+    F = fd.fd_forces(prob, np.arange(len(prob.pos)), delta=1e-3)
+    assert np.abs(F - b["F"]).max() / np.abs(b["F"]).max() < 1e-7
+
+
+def test_linearity_identities(tiny):
+    # L is linear in each of h, R and Y separately
+    prob, d, out, b = tiny
+    Lval = float((d["G"] * out).sum())
+    _, _, Y, _, R = prob.edge_terms(np.arange(len(prob.src)))
+    assert abs(float((b["dh"] * d["h"]).sum()) - Lval) < 1e-12 * abs(Lval)
+    assert abs(float((b["dR"] * R).sum()) - Lval) < 1e-12 * abs(Lval)
+    assert abs(float((b["dY"] * Y).sum()) - Lval) < 1e-12 * abs(Lval)
+    np.testing.assert_allclose(b["F"].sum(0), 0.0, atol=1e-12 * np.abs(b["F"]).max())
+
+
+def _wigner_D(l, q):
+    v = np.random.default_rng(11).standard_normal((60, 3))
+    v /= np.linalg.norm(v, axis=1, keepdims=True)
+    s = slice(l * l, (l + 1) ** 2)
+    D, *_ = np.linalg.lstsq(sh.sh(v, l)[:, s], sh.sh(v @ q.T, l)[:, s], rcond=None)
+    return D.T
+
+
+def _rotate_feats(x, D_of_l, blocks):
+    y = x.copy()
+    for l, rows in blocks:
+        y[:, rows, :] = np.einsum("ab,nbu->nau", D_of_l(l), x[:, rows, :])
+    return y
+
+
+@pytest.mark.parametrize("improper", [False, True])
+def test_o3_equivariance(tiny, improper):
+    prob, d, out, _ = tiny
+    L = prob.L
+    q, _ = np.linalg.qr(np.random.default_rng(21).standard_normal((3, 3)))
+    q *= np.sign(np.linalg.det(q))
+    if improper:
+        q = -q                                   # includes the inversion
+    D = {l: _wigner_D(l, q) for l in range(4)}
+    if improper:                                 # natural parity: inversion acts as (-1)^l
+        for l in D:
+            np.testing.assert_allclose(_wigner_D(l, -np.eye(3)), (-1) ** l * np.eye(2 * l + 1), atol=1e-12)
+    in_blocks = [(l, list(range(l * l, (l + 1) ** 2))) for l in range(L.l1max + 1)]
+    h2 = _rotate_feats(d["h"], D.get, in_blocks)
+    csr = (prob.row_ptr, prob.src, prob.shift)
+    p2, _ = _problem(0, csr=csr, pos=d["pos"] @ q.T, cell=d["cell"] @ q.T, h=h2)
+    out2 = p2.forward()
+    # rotate the reference output block by block: rows of path p are (p, m3)
+    want = out.copy()
+    for p, (_, _, l3) in enumerate(L.paths):
+        rows = L.out_rows(p)
+        want[:, rows, :] = np.einsum("ab,nbu->nau", D[l3], out[:, rows, :])
+    np.testing.assert_allclose(out2, want, atol=1e-11 * np.abs(out).max())
+
+
+def test_translation_and_permutation(tiny):
+    prob, d, out, _ = tiny
+    csr = (prob.row_ptr, prob.src, prob.shift)
+    p_t, _ = _problem(0, csr=csr, pos=d["pos"] + np.array([0.3, -0.2, 0.1]))
+    np.testing.assert_allclose(p_t.forward(), out, atol=1e-12 * np.abs(out).max())
+    perm = np.random.default_rng(2).permutation(len(d["pos"]))
+    inv = np.argsort(perm)
+    csr_p = nbr.binned(d["pos"][perm], d["cell"], prob.r_cut)
+    p_p, _ = _problem(0, csr=csr_p, pos=d["pos"][perm], h=d["h"][perm])
+    np.testing.assert_allclose(p_p.forward()[inv], out, atol=1e-12 * np.abs(out).max())
+
+
+def _two_atoms(layout, h, d=1.7, rc=4.0):
+    pos = np.array([[10.0, 10.0, 10.0], [10.0 + d * 0.6, 10.0 - d * 0.8, 10.0]])
+    cell = np.eye(3) * 30.0
+    rp, src, shift = nbr.brute_force(pos, cell, rc)
+    rng = np.random.default_rng(3)
+    W = [rng.standard_normal((8, 16)) / math.sqrt(8), rng.standard_normal((16, layout.n_paths * layout.C)) / 4]
+    return conv.Problem(layout, pos, cell, rp, src, shift, h, W, rc, 1.0), pos
+
+
+def test_scalar_path_closed_form():
+    L = paths.Layout(0, 0, 0, 5)
+    h = np.random.default_rng(4).standard_normal((2, 1, 5))
+    prob, pos = _two_atoms(L, h)
+    out = prob.forward()
+    _, _, _, _, R = prob.edge_terms(np.arange(2))
+    # out_i = R_e h_j (Y_00 = 1, C^{000} = 1)
+    np.testing.assert_allclose(out[0, 0], R[0] * h[1, 0], rtol=1e-14)
+    np.testing.assert_allclose(out[1, 0], R[1] * h[0, 0], rtol=1e-14)
+    np.testing.assert_allclose(R[0], R[1], rtol=0, atol=0)
+
+
+def test_dot_product_path_closed_form():
+    L = paths.Layout(1, 1, 0, 4)
+    assert L.paths == [(0, 0, 0), (1, 1, 0)]
+    h = np.random.default_rng(5).standard_normal((2, 4, 4))
+    h[:, 0, :] = 0.0                              # only the 1o part
+    prob, pos = _two_atoms(L, h)
+    out = prob.forward()
+    _, _, _, _, R = prob.edge_terms(np.arange(2))
+    rhat = (pos[1] - pos[0]) / np.linalg.norm(pos[1] - pos[0])
+    rs = rhat[[1, 2, 0]]                           # (y, z, x) component order
+    row = L.out_rows(1)[0]
+    np.testing.assert_allclose(out[0, row], R[0, 4:8] * np.einsum("a,au->u", rs, h[1, 1:4]), rtol=1e-13)
+    np.testing.assert_allclose(out[1, row], R[1, 4:8] * np.einsum("a,au->u", -rs, h[0, 1:4]), rtol=1e-13)
+
+
+@pytest.mark.slow
+def test_medium_slice_finite_differences():
+    """Forces on atoms 0-63 of the medium system against 5-point differences."""
+    prob, d = _problem(3)
+    atoms = np.arange(64)
+    F = prob.forces_atoms(atoms)
+    Ffd = fd.fd_forces(prob, atoms, delta=1e-3)
+    assert np.abs(F - Ffd).max() / np.abs(F).max() < 1e-7

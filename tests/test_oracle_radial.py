@@ -1,0 +1,64 @@
+"""Pins of the oracle's radial pieces: closed forms, a library routine,
+boundary conditions and derivatives."""
+import numpy as np
+import scipy.special as sps
+
+from oracle import radial
+
+
+def test_envelope_boundary_conditions():
+    assert radial.envelope(0.0) == 1.0
+    assert abs(radial.envelope(1.0)) < 1e-15
+    assert abs(radial.envelope_dx(1.0)) < 1e-13
+    # second derivative at 1 by the analytic polynomial: 2nd derivative of
+    # 1 - 21 x^5 + 35 x^6 - 15 x^7
+    d2 = -21 * 20 + 35 * 30 - 15 * 42
+    assert d2 == 0
+    x = np.linspace(0.0, 1.0, 11)
+    np.testing.assert_allclose(radial.envelope(x), 1 - 21 * x**5 + 35 * x**6 - 15 * x**7, atol=1e-15)
+
+
+def test_bessel_is_scaled_spherical_j0():
+    rc = 5.0
+    r = np.linspace(0.3, 4.99, 37)
+    b = radial.bessel(r, rc)
+    for n in range(1, 9):
+        k = n * np.pi / rc
+        ref = np.sqrt(2.0 / rc) * k * sps.spherical_jn(0, k * r)
+        np.testing.assert_allclose(b[:, n - 1], ref, rtol=1e-13)
+
+
+def test_derivatives_by_central_differences():
+    rc = 6.0
+    r = np.linspace(0.8, 5.9, 23)
+    e = 1e-6
+    np.testing.assert_allclose(radial.bessel_dr(r, rc),
+                               (radial.bessel(r + e, rc) - radial.bessel(r - e, rc)) / (2 * e), atol=1e-7)
+    np.testing.assert_allclose(radial.edge_features_dr(r, rc),
+                               (radial.edge_features(r + e, rc) - radial.edge_features(r - e, rc)) / (2 * e),
+                               atol=1e-7)
+    z = np.linspace(-6, 6, 25)
+    np.testing.assert_allclose(radial.silu_dz(z), (radial.silu(z + e) - radial.silu(z - e)) / (2 * e), atol=1e-8)
+
+
+def test_weights_vanish_at_the_cutoff():
+    # bias-free MLP with SiLU(0) = 0 and ef(r_c) = 0  =>  R(r_c) = 0
+    rng = np.random.default_rng(0)
+    W = [rng.standard_normal((8, 16)), rng.standard_normal((16, 16)), rng.standard_normal((16, 40))]
+    R, _ = radial.mlp_forward(radial.edge_features(np.array([4.0]), 4.0), W)
+    assert np.abs(R).max() < 1e-13
+
+
+def test_mlp_input_gradient_by_differences():
+    rng = np.random.default_rng(1)
+    W = [rng.standard_normal((8, 16)) / 3, rng.standard_normal((16, 16)) / 4, rng.standard_normal((16, 40)) / 4]
+    ef = rng.standard_normal((5, 8))
+    dR = rng.standard_normal((5, 40))
+    g = radial.mlp_input_grad(dR, ef, W)
+    e = 1e-6
+    for k in range(8):
+        d = np.zeros(8)
+        d[k] = e
+        fp = (radial.mlp_forward(ef + d, W)[0] * dR).sum(1)
+        fm = (radial.mlp_forward(ef - d, W)[0] * dR).sum(1)
+        np.testing.assert_allclose(g[:, k], (fp - fm) / (2 * e), atol=1e-7)
