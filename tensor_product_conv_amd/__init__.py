@@ -1,0 +1,322 @@
+"""MI355X (gfx950) equivariant interaction convolution: Python binding.
+
+A thin ctypes layer over ``libtpconv.so`` (C ABI in ``include/tpconv.h``).
+PyTorch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+
+    import tensor_product_conv_amd as tpc
+    ctx = tpc.Context(tpc.Spec(dtype="float32", channels=128, node_lmax=2,
+                               sh_lmax=3, out_lmax=3, r_cut=6.0,
+                               layer_dims=[8, 64, 64, 64, 17 * 128]))
+    nl = ctx.nbr_build(pos, cell)                    # receiver-sorted CSR
+    out, saved = ctx.conv_fwd(pos, cell, nl, h, W, scale)
+    dh, dR, forces = ctx.conv_bwd(nl, h, W, scale, G, saved)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+__all__ = ["Spec", "Context", "NeighbourList", "EdgeBuffers", "TpcError", "library",
+           "nbr_build", "conv_fwd", "conv_bwd", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpconv.so")
+
+TPC_MAX_LAYERS = 8
+TPC_MAX_PATHS = 32
+OP_NBR, OP_FWD, OP_BWD = 0, 1, 2
+STATUS = {0: "ok", 1: "invalid", 2: "unsupported", 3: "capacity", 4: "precondition",
+          5: "workspace", 6: "device"}
+
+
+class TpcError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"tpconv {STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class _Spec(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("channels", ctypes.c_int), ("node_lmax", ctypes.c_int),
+                ("sh_lmax", ctypes.c_int), ("out_lmax", ctypes.c_int), ("n_bessel", ctypes.c_int),
+                ("poly_p", ctypes.c_int), ("n_species", ctypes.c_int), ("r_cut", ctypes.c_double),
+                ("n_layers", ctypes.c_int), ("layer_dims", ctypes.c_int * (TPC_MAX_LAYERS + 1)),
+                ("validate", ctypes.c_int)]
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [("n_paths", ctypes.c_int), ("d_in", ctypes.c_int), ("d_sh", ctypes.c_int),
+                ("d_out", ctypes.c_int), ("r_width", ctypes.c_int), ("nnz_cg", ctypes.c_int),
+                ("paths", (ctypes.c_int * 3) * TPC_MAX_PATHS)]
+
+
+class _EdgeBuffers(ctypes.Structure):
+    _fields_ = [("Y", ctypes.c_void_p), ("ef", ctypes.c_void_p), ("rv", ctypes.c_void_p),
+                ("R", ctypes.c_void_p)]
+
+
+_LIB = None
+_VP = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def library():
+    """Load libtpconv.so (built in-tree by ``python -m tensor_product_conv_amd.build``)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m tensor_product_conv_amd.build` (needs ROCm hipcc)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.tpc_ctx_create.argtypes = [ctypes.POINTER(_Spec), ctypes.POINTER(_VP)]
+    lib.tpc_ctx_destroy.argtypes = [_VP]
+    lib.tpc_ctx_destroy.restype = None
+    lib.tpc_ctx_info.argtypes = [_VP, ctypes.POINTER(_Info)]
+    lib.tpc_cg_table.argtypes = [_VP, ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.c_size_t]
+    lib.tpc_workspace_query.argtypes = [_VP, ctypes.c_int, _I64, _I64,
+                                        ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_size_t)]
+    lib.tpc_nbr_build.argtypes = [_VP, _I64, _VP, ctypes.POINTER(ctypes.c_double), _VP, _I64,
+                                  _VP, _VP, _VP, _VP, ctypes.POINTER(_I64), _VP, ctypes.c_size_t, _VP]
+    lib.tpc_conv_fwd.argtypes = [_VP, _I64, _VP, ctypes.POINTER(ctypes.c_double), _VP, _VP, _VP,
+                                 _I64, _I64, _I64, _I64, _VP, ctypes.POINTER(_VP), ctypes.c_double,
+                                 _VP, ctypes.POINTER(_EdgeBuffers), _VP, ctypes.c_size_t, _VP]
+    lib.tpc_conv_bwd.argtypes = [_VP, _I64, _I64, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _VP,
+                                 ctypes.POINTER(_VP), ctypes.c_double, _VP,
+                                 ctypes.POINTER(_EdgeBuffers), _VP, _VP, _VP, _VP, _VP,
+                                 ctypes.c_size_t, _VP]
+    lib.tpc_status_string.argtypes = [ctypes.c_int]
+    lib.tpc_status_string.restype = ctypes.c_char_p
+    lib.tpc_last_error.argtypes = []
+    lib.tpc_last_error.restype = ctypes.c_char_p
+    for name in ("tpc_ctx_create", "tpc_ctx_info", "tpc_cg_table", "tpc_workspace_query",
+                 "tpc_nbr_build", "tpc_conv_fwd", "tpc_conv_bwd"):
+        getattr(lib, name).restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        raise TpcError(status, library().tpc_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _cell_arg(cell):
+    import numpy as np
+    c = np.ascontiguousarray(np.asarray(cell.cpu() if hasattr(cell, "cpu") else cell,
+                                        dtype=np.float64).reshape(9))
+    return (ctypes.c_double * 9)(*c.tolist())
+
+
+@dataclass
+class Spec:
+    """Python mirror of ``tpc_spec``."""
+    channels: int
+    node_lmax: int
+    sh_lmax: int
+    out_lmax: int
+    r_cut: float
+    layer_dims: list
+    dtype: str = "float32"
+    n_species: int = 128
+    n_bessel: int = 8
+    poly_p: int = 5
+    validate: bool = False
+
+    def to_c(self):
+        s = _Spec()
+        s.dtype = {"float32": 0, "float64": 1}[self.dtype]
+        s.channels = self.channels
+        s.node_lmax, s.sh_lmax, s.out_lmax = self.node_lmax, self.sh_lmax, self.out_lmax
+        s.n_bessel, s.poly_p, s.n_species = self.n_bessel, self.poly_p, self.n_species
+        s.r_cut = float(self.r_cut)
+        s.n_layers = len(self.layer_dims) - 1
+        for k, d in enumerate(self.layer_dims[:TPC_MAX_LAYERS + 1]):
+            s.layer_dims[k] = int(d)
+        s.validate = int(bool(self.validate))
+        return s
+
+
+@dataclass
+class NeighbourList:
+    row_ptr: object       # int32 [N+1]
+    src: object           # int32 [E]
+    shift: object         # int32 [E, 3]
+    rev: object           # int32 [E]
+    n_edges: int
+
+
+@dataclass
+class EdgeBuffers:
+    Y: object
+    ef: object
+    rv: object
+    R: object
+    edge_begin: int = 0
+    edge_end: int = 0
+    row_begin: int = 0
+    row_end: int = 0
+
+    def to_c(self):
+        return _EdgeBuffers(_ptr(self.Y), _ptr(self.ef), _ptr(self.rv), _ptr(self.R))
+
+
+class Context:
+    """A ``tpc_ctx``: immutable spec plus the coupling tables built from it."""
+
+    def __init__(self, spec: Spec):
+        self.spec = spec
+        lib = library()
+        self._h = ctypes.c_void_p()
+        self._spec_c = spec.to_c()
+        _check(lib.tpc_ctx_create(ctypes.byref(self._spec_c), ctypes.byref(self._h)))
+        info = _Info()
+        _check(lib.tpc_ctx_info(self._h, ctypes.byref(info)))
+        self.n_paths, self.d_in, self.d_sh, self.d_out = info.n_paths, info.d_in, info.d_sh, info.d_out
+        self.r_width, self.nnz_cg = info.r_width, info.nnz_cg
+        self.paths = [tuple(info.paths[p]) for p in range(info.n_paths)]
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and h.value and _LIB is not None:
+            _LIB.tpc_ctx_destroy(h)
+            self._h = None
+
+    @property
+    def dtype(self):
+        t = _torch()
+        return t.float64 if self.spec.dtype == "float64" else t.float32
+
+    def cg_table(self, p):
+        import numpy as np
+        l1, l2, l3 = self.paths[p]
+        n = (2 * l1 + 1) * (2 * l2 + 1) * (2 * l3 + 1)
+        buf = (ctypes.c_double * n)()
+        _check(library().tpc_cg_table(self._h, p, buf, n))
+        return np.array(buf[:], dtype=np.float64).reshape(2 * l1 + 1, 2 * l2 + 1, 2 * l3 + 1)
+
+    def workspace_bytes(self, op, n_atoms=0, n_edges=0, cell=None):
+        out = ctypes.c_size_t()
+        c = _cell_arg(cell) if cell is not None else None
+        _check(library().tpc_workspace_query(self._h, op, n_atoms, n_edges, c, ctypes.byref(out)))
+        return out.value
+
+    def _workspace(self, nbytes, device):
+        t = _torch()
+        return t.empty(max(int(nbytes), 256), dtype=t.uint8, device=device)
+
+    # ---- neighbour list ---------------------------------------------------
+    def nbr_build(self, pos, cell, species=None, edge_cap=None):
+        """Receiver-sorted CSR; grows the edge buffers once if the first guess is short."""
+        t = _torch()
+        N = pos.shape[0]
+        dev = pos.device
+        ws = self._workspace(self.workspace_bytes(OP_NBR, N, 0, cell), dev)
+        c = _cell_arg(cell)
+        cap = int(edge_cap) if edge_cap is not None else max(64, N * 64)
+        row_ptr = t.empty(N + 1, dtype=t.int32, device=dev)
+        for _ in range(2):
+            src = t.empty(cap, dtype=t.int32, device=dev)
+            shift = t.empty((cap, 3), dtype=t.int32, device=dev)
+            rev = t.empty(cap, dtype=t.int32, device=dev)
+            ne = _I64()
+            st = library().tpc_nbr_build(self._h, N, _ptr(pos), c, _ptr(species), cap, _ptr(row_ptr),
+                                         _ptr(src), _ptr(shift), _ptr(rev), ctypes.byref(ne), _ptr(ws),
+                                         ws.numel(), _stream())
+            if st == 3 and edge_cap is None:     # capacity: reallocate and call again
+                cap = ne.value
+                continue
+            _check(st)
+            E = ne.value
+            return NeighbourList(row_ptr, src[:E], shift[:E], rev[:E], E)
+        _check(st)
+
+    # ---- forward ------------------------------------------------------------
+    def alloc_edge_buffers(self, n_edges, device):
+        t = _torch()
+        return EdgeBuffers(Y=t.empty((n_edges, self.d_sh), dtype=self.dtype, device=device),
+                           ef=t.empty((n_edges, 8), dtype=self.dtype, device=device),
+                           rv=t.empty((n_edges, 4), dtype=self.dtype, device=device),
+                           R=t.empty((n_edges, self.r_width), dtype=self.dtype, device=device))
+
+    def conv_fwd(self, pos, cell, nl: NeighbourList, h, W, scale=1.0, out=None, eb=None,
+                 rows=None, edges=None):
+        """out [N, d_out, C]; returns (out, edge buffers for conv_bwd)."""
+        t = _torch()
+        N = pos.shape[0]
+        rb, re_ = rows if rows is not None else (0, N)
+        eb_, ee = edges if edges is not None else (0, nl.n_edges)
+        if out is None:
+            out = t.empty((N, self.d_out, self.spec.channels), dtype=self.dtype, device=h.device)
+        if eb is None:
+            eb = self.alloc_edge_buffers(ee - eb_, h.device)
+        eb.edge_begin, eb.edge_end, eb.row_begin, eb.row_end = eb_, ee, rb, re_
+        wp = (_VP * len(W))(*[w.data_ptr() for w in W])
+        ebc = eb.to_c()
+        ws = self._workspace(self.workspace_bytes(OP_FWD, N, ee - eb_), h.device)
+        _check(library().tpc_conv_fwd(self._h, N, _ptr(pos), _cell_arg(cell), _ptr(nl.row_ptr),
+                                      _ptr(nl.src), _ptr(nl.shift), rb, re_, eb_, ee, _ptr(h), wp,
+                                      float(scale), _ptr(out), ctypes.byref(ebc), _ptr(ws), ws.numel(),
+                                      _stream()))
+        return out, eb
+
+    # ---- backward -------------------------------------------------------------
+    def conv_bwd(self, nl: NeighbourList, h, W, scale, G, eb: EdgeBuffers, dh=None, dR=None,
+                 g_edge=None, want_dR=True, want_forces=True, forces=None):
+        """Returns (dh, dR or None, forces or None, g_edge)."""
+        t = _torch()
+        N = h.shape[0]
+        ne = eb.edge_end - eb.edge_begin
+        if dh is None:
+            dh = t.empty_like(h)
+        if want_dR and dR is None:
+            dR = t.empty((ne, self.r_width), dtype=self.dtype, device=h.device)
+        if g_edge is None:
+            g_edge = t.empty((nl.n_edges, 3), dtype=self.dtype, device=h.device)
+        if want_forces and forces is None:
+            forces = t.empty((N, 3), dtype=self.dtype, device=h.device)
+        if not want_forces:
+            forces = None
+        wp = (_VP * len(W))(*[w.data_ptr() for w in W])
+        ebc = eb.to_c()
+        ws = self._workspace(self.workspace_bytes(OP_BWD, N, ne), h.device)
+        _check(library().tpc_conv_bwd(self._h, N, nl.n_edges, _ptr(nl.row_ptr), _ptr(nl.src),
+                                      _ptr(nl.rev), eb.row_begin, eb.row_end, eb.edge_begin,
+                                      eb.edge_end, _ptr(h), wp, float(scale), _ptr(G), ctypes.byref(ebc),
+                                      _ptr(dh), _ptr(dR), _ptr(g_edge), _ptr(forces), _ptr(ws),
+                                      ws.numel(), _stream()))
+        return dh, dR, forces, g_edge
+
+
+def nbr_build(ctx: Context, *a, **k):
+    return ctx.nbr_build(*a, **k)
+
+
+def conv_fwd(ctx: Context, *a, **k):
+    return ctx.conv_fwd(*a, **k)
+
+
+def conv_bwd(ctx: Context, *a, **k):
+    return ctx.conv_bwd(*a, **k)
+
+
+def spec_for(cfg, validate=False):
+    """Spec of a workload configuration dict (see ``workloads.config``)."""
+    return Spec(channels=cfg["C"], node_lmax=cfg["l1max"], sh_lmax=cfg["sh_lmax"],
+                out_lmax=cfg["out_lmax"], r_cut=cfg["r_cut"], layer_dims=list(cfg["layer_dims"]),
+                dtype=cfg["dtype"], validate=validate)

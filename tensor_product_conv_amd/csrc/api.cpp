@@ -1,0 +1,666 @@
+// Host side of the C ABI declared in include/tpconv.h: spec validation, the
+// context, workspace planning, argument checks and kernel sequencing.
+//
+// Every check runs before any device work, so a failing call enqueues nothing,
+// and every failed check is reported (the "PlanRefused lists every reason"
+// convention of the FastMACE page "Rewrites and precision options").
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/tpconv.h"
+#include "common.hpp"
+#include "kernels.hpp"
+#include "nbr.hpp"
+#include "tables.hpp"
+
+struct tpc_ctx {
+  tpc_spec spec;
+  tpc::Table tab;
+  int hidden;    // hidden width H
+  int n_hidden;  // number of hidden layers
+  size_t tsize;  // bytes per feature value
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct Errors {
+  std::vector<std::string> msgs;
+  tpc_status status = TPC_OK;
+  void add(tpc_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    msgs.emplace_back(buf);
+    // INVALID outranks UNSUPPORTED, which outranks the rest
+    if (status == TPC_OK || s == TPC_ERR_INVALID ||
+        (s == TPC_ERR_UNSUPPORTED && status != TPC_ERR_INVALID))
+      status = s;
+  }
+  tpc_status finish() {
+    if (status == TPC_OK) {
+      g_last_error.clear();
+      return TPC_OK;
+    }
+    std::string all;
+    for (auto& m : msgs) {
+      if (!all.empty()) all += "; ";
+      all += m;
+    }
+    g_last_error = all;
+    return status;
+  }
+};
+
+tpc_status device_error(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return TPC_ERR_DEVICE;
+}
+
+#define TPC_HIP(call, where)                                  \
+  do {                                                        \
+    hipError_t _e = (call);                                   \
+    if (_e != hipSuccess) return device_error(_e, where);     \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Bin grid for the neighbour build from a host cell.
+bool make_grid(const double* cell, double r_cut, tpc::NbrGrid* g, std::string* why) {
+  double A[3][3];
+  for (int r = 0; r < 3; ++r)
+    for (int c = 0; c < 3; ++c) A[r][c] = cell[3 * r + c];
+  const double det = A[0][0] * (A[1][1] * A[2][2] - A[1][2] * A[2][1]) -
+                     A[0][1] * (A[1][0] * A[2][2] - A[1][2] * A[2][0]) +
+                     A[0][2] * (A[1][0] * A[2][1] - A[1][1] * A[2][0]);
+  if (!std::isfinite(det) || std::fabs(det) < 1e-12) {
+    *why = "cell is singular or not finite";
+    return false;
+  }
+  // inverse (adjugate / det); f = x . inv
+  double inv[3][3];
+  inv[0][0] = (A[1][1] * A[2][2] - A[1][2] * A[2][1]) / det;
+  inv[0][1] = (A[0][2] * A[2][1] - A[0][1] * A[2][2]) / det;
+  inv[0][2] = (A[0][1] * A[1][2] - A[0][2] * A[1][1]) / det;
+  inv[1][0] = (A[1][2] * A[2][0] - A[1][0] * A[2][2]) / det;
+  inv[1][1] = (A[0][0] * A[2][2] - A[0][2] * A[2][0]) / det;
+  inv[1][2] = (A[0][2] * A[1][0] - A[0][0] * A[1][2]) / det;
+  inv[2][0] = (A[1][0] * A[2][1] - A[1][1] * A[2][0]) / det;
+  inv[2][1] = (A[0][1] * A[2][0] - A[0][0] * A[2][1]) / det;
+  inv[2][2] = (A[0][0] * A[1][1] - A[0][1] * A[1][0]) / det;
+  const double vol = std::fabs(det);
+  int64_t total = 1;
+  for (int k = 0; k < 3; ++k) {
+    const double* u = A[(k + 1) % 3];
+    const double* v = A[(k + 2) % 3];
+    const double cx = u[1] * v[2] - u[2] * v[1], cy = u[2] * v[0] - u[0] * v[2],
+                 cz = u[0] * v[1] - u[1] * v[0];
+    const double h = vol / std::sqrt(cx * cx + cy * cy + cz * cz);
+    const double w = r_cut * (1.0 + 1e-6);
+    int nb = (int)std::floor(h / w);
+    if (nb < 1) nb = 1;
+    if (nb > 1024) nb = 1024;
+    const int K = (int)std::ceil(w * nb / h);
+    if (K > 16) {
+      *why = "cell is too thin for the cutoff (more than 16 images per direction)";
+      return false;
+    }
+    g->nb[k] = nb;
+    g->K[k] = K;
+    total *= nb;
+  }
+  if (total > (int64_t)1 << 24) {
+    *why = "too many bins";
+    return false;
+  }
+  for (int r = 0; r < 3; ++r)
+    for (int c = 0; c < 3; ++c) {
+      g->a[r][c] = A[r][c];
+      g->inv[r][c] = inv[r][c];
+    }
+  g->rc2 = r_cut * r_cut;
+  return true;
+}
+
+struct NbrWs {
+  size_t bin_of, bin_start, cursor, bin_atoms, partials, status, total;
+};
+
+NbrWs nbr_layout(int64_t n, int64_t nbin) {
+  NbrWs w{};
+  size_t off = 0;
+  w.bin_of = off;
+  off += align_up(sizeof(int32_t) * (size_t)n);
+  w.bin_start = off;
+  off += align_up(sizeof(int32_t) * (size_t)(nbin + 1));
+  w.cursor = off;
+  off += align_up(sizeof(int32_t) * (size_t)nbin);
+  w.bin_atoms = off;
+  off += align_up(sizeof(int32_t) * (size_t)n);
+  w.partials = off;
+  const int64_t m = n > nbin ? n : nbin;
+  off += align_up(sizeof(int64_t) * (size_t)tpc::scan_partials_len(m + 1));
+  w.status = off;
+  off += align_up(sizeof(int32_t) * 8);
+  w.total = off;
+  return w;
+}
+
+struct BwdWs {
+  size_t dR, dY, d_ef, status, total, total_without_dR;
+};
+
+BwdWs bwd_layout(const tpc_ctx* c, int64_t ne) {
+  BwdWs w{};
+  const size_t T = c->tsize;
+  size_t off = 0;
+  w.dY = off;
+  off += align_up(T * (size_t)ne * c->tab.dsh);
+  w.d_ef = off;
+  off += align_up(T * (size_t)ne * 8);
+  w.status = off;
+  off += align_up(sizeof(int32_t) * 8);
+  w.total_without_dR = off;
+  w.dR = off;
+  off += align_up(T * (size_t)ne * c->tab.np * c->spec.channels);
+  w.total = off;
+  return w;
+}
+
+void flag_messages(int flags, Errors& E) {
+  if (flags & tpc::kFlagUnwrapped)
+    E.add(TPC_ERR_PRECONDITION, "positions are not wrapped: a fractional coordinate lies outside [0,1)");
+  if (flags & tpc::kFlagSpecies) E.add(TPC_ERR_INVALID, "a species id lies outside [0, n_species)");
+  if (flags & tpc::kFlagDegree)
+    E.add(TPC_ERR_UNSUPPORTED, "a row has more than %d neighbours", tpc::kMaxDegree);
+  if (flags & tpc::kFlagNoReverse) E.add(TPC_ERR_PRECONDITION, "an edge has no reverse edge");
+  if (flags & tpc::kFlagCsrOrder)
+    E.add(TPC_ERR_PRECONDITION, "CSR is not receiver-sorted (row pointers or row order)");
+  if (flags & tpc::kFlagCsrRange) E.add(TPC_ERR_PRECONDITION, "CSR holds an invalid sender");
+  if (flags & tpc::kFlagShiftRange) E.add(TPC_ERR_PRECONDITION, "an image shift lies outside [-127,127]");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tpc_status_string(tpc_status s) {
+  switch (s) {
+    case TPC_OK: return "ok";
+    case TPC_ERR_INVALID: return "invalid argument";
+    case TPC_ERR_UNSUPPORTED: return "unsupported";
+    case TPC_ERR_CAPACITY: return "edge capacity too small";
+    case TPC_ERR_PRECONDITION: return "precondition violated";
+    case TPC_ERR_WORKSPACE: return "workspace too small";
+    case TPC_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* tpc_last_error(void) { return g_last_error.c_str(); }
+
+tpc_status tpc_ctx_create(const tpc_spec* spec, tpc_ctx** out) {
+  Errors E;
+  if (!spec || !out) {
+    E.add(TPC_ERR_INVALID, "spec and ctx must be non-null");
+    return E.finish();
+  }
+  const tpc_spec& s = *spec;
+  if (s.dtype != TPC_F32 && s.dtype != TPC_F64) E.add(TPC_ERR_INVALID, "dtype must be TPC_F32 or TPC_F64");
+  if (s.channels < 1) E.add(TPC_ERR_INVALID, "channels must be >= 1");
+  bool lok = true;
+  if (s.node_lmax < 0 || s.node_lmax > 3) { E.add(TPC_ERR_UNSUPPORTED, "node_lmax must be 0..3"); lok = false; }
+  if (s.sh_lmax < 0 || s.sh_lmax > 3) { E.add(TPC_ERR_UNSUPPORTED, "sh_lmax must be 0..3"); lok = false; }
+  if (s.out_lmax < 0 || s.out_lmax > 3) { E.add(TPC_ERR_UNSUPPORTED, "out_lmax must be 0..3"); lok = false; }
+  if (s.n_bessel != 8) E.add(TPC_ERR_UNSUPPORTED, "n_bessel must be 8");
+  if (s.poly_p != 5) E.add(TPC_ERR_UNSUPPORTED, "poly_p must be 5");
+  if (s.n_species < 1) E.add(TPC_ERR_INVALID, "n_species must be >= 1");
+  if (!(s.r_cut > 0.0) || !std::isfinite(s.r_cut)) E.add(TPC_ERR_INVALID, "r_cut must be finite and > 0");
+  tpc::Table tab{};
+  if (lok) {
+    tab = tpc::make_table(s.node_lmax, s.sh_lmax, s.out_lmax);
+    if (tab.np == 0) E.add(TPC_ERR_INVALID, "no admissible path for these l ranges");
+  }
+  int H = 0, NH = 0;
+  if (s.n_layers < 2 || s.n_layers > TPC_MAX_LAYERS) {
+    E.add(TPC_ERR_INVALID, "n_layers must be 2..%d", TPC_MAX_LAYERS);
+  } else {
+    if (s.layer_dims[0] != 8) E.add(TPC_ERR_INVALID, "layer_dims[0] must equal n_bessel (8)");
+    H = s.layer_dims[1];
+    NH = s.n_layers - 1;
+    for (int k = 1; k < s.n_layers; ++k)
+      if (s.layer_dims[k] != H) E.add(TPC_ERR_UNSUPPORTED, "hidden widths must all be equal");
+    if (!tpc::radial_supported(H, NH))
+      E.add(TPC_ERR_UNSUPPORTED, "radial MLP needs 1..3 hidden layers of width 16, 32 or 64 (got %d x %d)", NH, H);
+    if (lok && tab.np > 0 && s.layer_dims[s.n_layers] != tab.np * s.channels)
+      E.add(TPC_ERR_INVALID, "layer_dims[n_layers] must equal paths*channels = %d", tab.np * s.channels);
+  }
+  if (lok && s.channels >= 1 && (s.dtype == TPC_F32 || s.dtype == TPC_F64) &&
+      !tpc::tp_supported(s.dtype, s.node_lmax, s.sh_lmax, s.out_lmax, s.channels))
+    E.add(TPC_ERR_UNSUPPORTED,
+          "no fused kernel for dtype=%d node_lmax=%d sh_lmax=%d out_lmax=%d channels=%d "
+          "(built: float32 (1,2,1),(1,3,3),(2,3,3) with C<=64 or C=128, (3,3,3) with C<=64; "
+          "float64 (1,2,1),(1,3,3),(2,3,3),(3,3,3) with C<=64)",
+          s.dtype, s.node_lmax, s.sh_lmax, s.out_lmax, s.channels);
+  tpc_status st = E.finish();
+  if (st != TPC_OK) return st;
+  tpc_ctx* c = new tpc_ctx;
+  c->spec = s;
+  c->tab = tab;
+  c->hidden = H;
+  c->n_hidden = NH;
+  c->tsize = s.dtype == TPC_F64 ? 8 : 4;
+  *out = c;
+  return TPC_OK;
+}
+
+void tpc_ctx_destroy(tpc_ctx* c) { delete c; }
+
+tpc_status tpc_ctx_info(const tpc_ctx* c, tpc_info* info) {
+  Errors E;
+  if (!c || !info) {
+    E.add(TPC_ERR_INVALID, "ctx and info must be non-null");
+    return E.finish();
+  }
+  std::memset(info, 0, sizeof(*info));
+  info->n_paths = c->tab.np;
+  info->d_in = c->tab.din;
+  info->d_sh = c->tab.dsh;
+  info->d_out = c->tab.dout;
+  info->r_width = c->tab.np * c->spec.channels;
+  info->nnz_cg = c->tab.nnz;
+  for (int p = 0; p < c->tab.np; ++p) {
+    info->paths[p][0] = c->tab.path[p].l1;
+    info->paths[p][1] = c->tab.path[p].l2;
+    info->paths[p][2] = c->tab.path[p].l3;
+  }
+  return E.finish();
+}
+
+tpc_status tpc_cg_table(const tpc_ctx* c, int path, double* out, size_t n) {
+  Errors E;
+  if (!c || !out) {
+    E.add(TPC_ERR_INVALID, "ctx and out must be non-null");
+    return E.finish();
+  }
+  if (path < 0 || path >= c->tab.np) {
+    E.add(TPC_ERR_INVALID, "path index out of range");
+    return E.finish();
+  }
+  const tpc::Path& P = c->tab.path[path];
+  const size_t need = (size_t)(2 * P.l1 + 1) * (2 * P.l2 + 1) * (2 * P.l3 + 1);
+  if (n < need) {
+    E.add(TPC_ERR_INVALID, "out holds %zu values, path needs %zu", n, need);
+    return E.finish();
+  }
+  size_t k = 0;
+  for (int a = 0; a <= 2 * P.l1; ++a)
+    for (int b = 0; b <= 2 * P.l2; ++b)
+      for (int d = 0; d <= 2 * P.l3; ++d) out[k++] = c->tab.cg[path][a][b][d];
+  return TPC_OK;
+}
+
+tpc_status tpc_workspace_query(const tpc_ctx* c, int op, int64_t n_atoms, int64_t n_edges,
+                               const double* cell, size_t* bytes) {
+  Errors E;
+  if (!c || !bytes) {
+    E.add(TPC_ERR_INVALID, "ctx and bytes must be non-null");
+    return E.finish();
+  }
+  if (n_atoms < 0 || n_edges < 0) E.add(TPC_ERR_INVALID, "sizes must be >= 0");
+  if (op == TPC_OP_NBR) {
+    if (!cell) {
+      E.add(TPC_ERR_INVALID, "the neighbour build needs the cell");
+      return E.finish();
+    }
+    tpc::NbrGrid g{};
+    std::string why;
+    if (!make_grid(cell, c->spec.r_cut, &g, &why)) E.add(TPC_ERR_INVALID, "%s", why.c_str());
+    if (E.status != TPC_OK) return E.finish();
+    *bytes = nbr_layout(n_atoms, (int64_t)g.nb[0] * g.nb[1] * g.nb[2]).total;
+  } else if (op == TPC_OP_FWD) {
+    *bytes = align_up(sizeof(int32_t) * 8);
+  } else if (op == TPC_OP_BWD) {
+    *bytes = bwd_layout(c, n_edges).total;
+  } else {
+    E.add(TPC_ERR_INVALID, "unknown op %d", op);
+  }
+  return E.finish();
+}
+
+tpc_status tpc_nbr_build(const tpc_ctx* c, int64_t n, const double* pos, const double* cell,
+                         const int32_t* species, int64_t edge_cap, int32_t* row_ptr,
+                         int32_t* src, int32_t* shift, int32_t* rev, int64_t* n_edges,
+                         void* ws, size_t ws_bytes, void* stream) {
+  Errors E;
+  if (!c) {
+    E.add(TPC_ERR_INVALID, "ctx must be non-null");
+    return E.finish();
+  }
+  if (n < 0) E.add(TPC_ERR_INVALID, "n_atoms must be >= 0");
+  if (n > (int64_t)1 << 24) E.add(TPC_ERR_UNSUPPORTED, "n_atoms above 2^24");
+  if (edge_cap < 0) E.add(TPC_ERR_INVALID, "edge_cap must be >= 0");
+  if (!cell) E.add(TPC_ERR_INVALID, "cell (host double[9]) must be non-null");
+  if (!row_ptr) E.add(TPC_ERR_INVALID, "row_ptr must be non-null");
+  if (!n_edges) E.add(TPC_ERR_INVALID, "n_edges must be non-null");
+  if (n > 0 && !pos) E.add(TPC_ERR_INVALID, "pos must be non-null");
+  if (pos && !aligned(pos, 8)) E.add(TPC_ERR_INVALID, "pos must be 8-byte aligned");
+  if (edge_cap > 0 && (!src || !shift || !rev)) E.add(TPC_ERR_INVALID, "src, shift and rev must be non-null when edge_cap > 0");
+  if (!ws && n > 0) E.add(TPC_ERR_INVALID, "workspace must be non-null");
+  if (ws && !aligned(ws, 256)) E.add(TPC_ERR_INVALID, "workspace must be 256-byte aligned");
+  tpc::NbrGrid g{};
+  int64_t nbin = 0;
+  if (cell) {
+    std::string why;
+    for (int k = 0; k < 9; ++k)
+      if (!std::isfinite(cell[k])) why = "cell is not finite";
+    if (why.empty() && make_grid(cell, c->spec.r_cut, &g, &why))
+      nbin = (int64_t)g.nb[0] * g.nb[1] * g.nb[2];
+    else
+      E.add(TPC_ERR_INVALID, "%s", why.c_str());
+  }
+  NbrWs L{};
+  if (E.status == TPC_OK) {
+    L = nbr_layout(n, nbin);
+    if (n > 0 && ws_bytes < L.total)
+      E.add(TPC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  }
+  tpc_status st = E.finish();
+  if (st != TPC_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n == 0) {
+    TPC_HIP(tpc::launch_fill_i32(row_ptr, 1, 0, s), "nbr_build");
+    *n_edges = 0;
+    return TPC_OK;
+  }
+  char* w = static_cast<char*>(ws);
+  int32_t* bin_of = reinterpret_cast<int32_t*>(w + L.bin_of);
+  int32_t* bin_start = reinterpret_cast<int32_t*>(w + L.bin_start);
+  int32_t* cursor = reinterpret_cast<int32_t*>(w + L.cursor);
+  int32_t* bin_atoms = reinterpret_cast<int32_t*>(w + L.bin_atoms);
+  int32_t* partials = reinterpret_cast<int32_t*>(w + L.partials);
+  int32_t* status = reinterpret_cast<int32_t*>(w + L.status);
+
+  TPC_HIP(tpc::launch_fill_i32(status, 8, 0, s), "nbr_build: clear status");
+  TPC_HIP(tpc::launch_fill_i32(bin_start, nbin + 1, 0, s), "nbr_build: clear bins");
+  TPC_HIP(tpc::launch_fill_i32(cursor, nbin, 0, s), "nbr_build: clear cursors");
+  TPC_HIP(tpc::launch_nbr_bin(n, pos, g, species, c->spec.n_species, bin_of, bin_start, status, s),
+          "nbr_build: bin");
+  TPC_HIP(tpc::launch_scan_exclusive(bin_start, nbin, partials, s), "nbr_build: bin scan");
+  TPC_HIP(tpc::launch_nbr_scatter(n, bin_of, bin_start, cursor, bin_atoms, s), "nbr_build: scatter");
+  TPC_HIP(tpc::launch_nbr_count(n, pos, g, bin_of, bin_start, bin_atoms, row_ptr, status, s),
+          "nbr_build: count");
+  TPC_HIP(tpc::launch_scan_exclusive(row_ptr, n, partials, s), "nbr_build: row scan");
+  // one wait: edge total and flags
+  int32_t host_status[2] = {0, 0};
+  TPC_HIP(hipMemcpyAsync(&host_status[0], status, sizeof(int32_t), hipMemcpyDeviceToHost, s),
+          "nbr_build: read status");
+  TPC_HIP(hipMemcpyAsync(&host_status[1], row_ptr + n, sizeof(int32_t), hipMemcpyDeviceToHost, s),
+          "nbr_build: read edge count");
+  TPC_HIP(hipStreamSynchronize(s), "nbr_build: wait");
+  if (host_status[0]) {
+    flag_messages(host_status[0], E);
+    return E.finish();
+  }
+  if (host_status[1] < 0) {
+    E.add(TPC_ERR_UNSUPPORTED, "more than 2^31-1 edges");
+    return E.finish();
+  }
+  const int64_t ne = host_status[1];
+  *n_edges = ne;
+  if (ne > edge_cap) {
+    E.add(TPC_ERR_CAPACITY, "the list needs %lld edges, edge_cap is %lld", (long long)ne,
+          (long long)edge_cap);
+    return E.finish();
+  }
+  TPC_HIP(tpc::launch_nbr_fill(n, pos, g, bin_of, bin_start, bin_atoms, row_ptr, src, shift, s),
+          "nbr_build: fill");
+  TPC_HIP(tpc::launch_nbr_reverse(n, row_ptr, src, shift, rev, status, s), "nbr_build: reverse");
+  if (c->spec.validate) {
+    TPC_HIP(hipMemcpyAsync(&host_status[0], status, sizeof(int32_t), hipMemcpyDeviceToHost, s),
+            "nbr_build: read status");
+    TPC_HIP(hipStreamSynchronize(s), "nbr_build: wait");
+    if (host_status[0]) {
+      flag_messages(host_status[0], E);
+      return E.finish();
+    }
+  }
+  g_last_error.clear();
+  return TPC_OK;
+}
+
+namespace {
+
+void check_chunk(const tpc_ctx* c, int64_t n, int64_t row_begin, int64_t row_end,
+                 int64_t edge_begin, int64_t edge_end, Errors& E) {
+  if (n < 0) E.add(TPC_ERR_INVALID, "n_atoms must be >= 0");
+  if (row_begin < 0 || row_end < row_begin || row_end > n)
+    E.add(TPC_ERR_INVALID, "need 0 <= row_begin <= row_end <= n_atoms");
+  if (edge_begin < 0 || edge_end < edge_begin) E.add(TPC_ERR_INVALID, "need 0 <= edge_begin <= edge_end");
+  if (edge_end > INT32_MAX) E.add(TPC_ERR_UNSUPPORTED, "edge indices above 2^31-1");
+  (void)c;
+}
+
+void need_ptr(const void* p, const char* name, size_t align, Errors& E) {
+  if (!p)
+    E.add(TPC_ERR_INVALID, "%s must be non-null", name);
+  else if (!aligned(p, align))
+    E.add(TPC_ERR_INVALID, "%s must be %zu-byte aligned", name, align);
+}
+
+tpc_status run_csr_check(int64_t n, int64_t n_edges, const int32_t* row_ptr, const int32_t* src,
+                         const int32_t* shift, int64_t rb, int64_t re, int64_t eb, int64_t ee,
+                         int32_t* status, hipStream_t s) {
+  TPC_HIP(tpc::launch_fill_i32(status, 1, 0, s), "csr check");
+  TPC_HIP(tpc::launch_csr_check(n, n_edges, row_ptr, src, shift, rb, re, eb, ee, status, s),
+          "csr check");
+  int32_t h = 0;
+  TPC_HIP(hipMemcpyAsync(&h, status, sizeof(int32_t), hipMemcpyDeviceToHost, s), "csr check");
+  TPC_HIP(hipStreamSynchronize(s), "csr check");
+  if (h) {
+    Errors E;
+    flag_messages(h, E);
+    return E.finish();
+  }
+  return TPC_OK;
+}
+
+}  // namespace
+
+tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const double* cell,
+                        const int32_t* row_ptr, const int32_t* src, const int32_t* shift,
+                        int64_t row_begin, int64_t row_end, int64_t edge_begin, int64_t edge_end,
+                        const void* h, const void* const* weights, double scale, void* out,
+                        const tpc_edge_buffers* eb, void* ws, size_t ws_bytes, void* stream) {
+  Errors E;
+  if (!c) {
+    E.add(TPC_ERR_INVALID, "ctx must be non-null");
+    return E.finish();
+  }
+  check_chunk(c, n, row_begin, row_end, edge_begin, edge_end, E);
+  if (!cell) E.add(TPC_ERR_INVALID, "cell (host double[9]) must be non-null");
+  if (!std::isfinite(scale)) E.add(TPC_ERR_INVALID, "scale must be finite");
+  const size_t va = 16;
+  need_ptr(row_ptr, "row_ptr", 4, E);
+  if (row_end > row_begin) {
+    need_ptr(pos, "pos", 8, E);
+    need_ptr(h, "h", va, E);
+    need_ptr(out, "out", va, E);
+  }
+  if (edge_end > edge_begin) {
+    need_ptr(src, "src", 4, E);
+    need_ptr(shift, "shift", 4, E);
+  }
+  if (!eb) {
+    E.add(TPC_ERR_INVALID, "edge buffers must be non-null");
+  } else if (edge_end > edge_begin) {
+    need_ptr(eb->Y, "eb.Y", va, E);
+    need_ptr(eb->ef, "eb.ef", va, E);
+    need_ptr(eb->rv, "eb.rv", va, E);
+    need_ptr(eb->R, "eb.R", va, E);
+  }
+  if (!weights) {
+    E.add(TPC_ERR_INVALID, "weights must be non-null");
+  } else {
+    for (int k = 0; k < c->spec.n_layers; ++k)
+      if (!weights[k]) E.add(TPC_ERR_INVALID, "weights[%d] must be non-null", k);
+  }
+  const size_t need = align_up(sizeof(int32_t) * 8);
+  if (c->spec.validate && (!ws || ws_bytes < need))
+    E.add(TPC_ERR_WORKSPACE, "validation needs a workspace of %zu bytes", need);
+  if (ws && !aligned(ws, 256)) E.add(TPC_ERR_INVALID, "workspace must be 256-byte aligned");
+  tpc_status st = E.finish();
+  if (st != TPC_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (c->spec.validate) {
+    st = run_csr_check(n, edge_end, row_ptr, src, shift, row_begin, row_end, edge_begin, edge_end,
+                       static_cast<int32_t*>(ws), s);
+    if (st != TPC_OK) return st;
+  }
+  const int dt = c->spec.dtype;
+  tpc::GeomArgs ga{};
+  ga.pos = pos;
+  for (int r = 0; r < 3; ++r)
+    for (int k = 0; k < 3; ++k) ga.cell[r][k] = cell[3 * r + k];
+  ga.row_ptr = row_ptr;
+  ga.src = src;
+  ga.shift = shift;
+  ga.row_begin = row_begin;
+  ga.row_end = row_end;
+  ga.edge_begin = edge_begin;
+  ga.edge_end = edge_end;
+  ga.r_cut = c->spec.r_cut;
+  const int64_t ne = edge_end - edge_begin;
+  if (ne > 0) {
+    TPC_HIP(tpc::launch_geom_fwd(dt, c->spec.sh_lmax, ga, eb->Y, eb->ef, eb->rv, s), "conv_fwd: geometry");
+    TPC_HIP(tpc::launch_radial_fwd(dt, c->hidden, c->n_hidden, ne, c->tab.np * c->spec.channels,
+                                   eb->ef, weights, eb->R, s),
+            "conv_fwd: radial MLP");
+  }
+  tpc::TPArgs ta{};
+  ta.row_ptr = row_ptr;
+  ta.src = src;
+  ta.row_begin = row_begin;
+  ta.row_end = row_end;
+  ta.edge_begin = edge_begin;
+  ta.C = c->spec.channels;
+  ta.scale = scale;
+  ta.h = h;
+  ta.Y = eb ? eb->Y : nullptr;
+  ta.R = eb ? eb->R : nullptr;
+  ta.out = out;
+  TPC_HIP(tpc::launch_tp_fwd(dt, c->spec.node_lmax, c->spec.sh_lmax, c->spec.out_lmax, ta, s),
+          "conv_fwd: tensor product");
+  g_last_error.clear();
+  return TPC_OK;
+}
+
+tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int32_t* row_ptr,
+                        const int32_t* src, const int32_t* rev, int64_t row_begin, int64_t row_end,
+                        int64_t edge_begin, int64_t edge_end, const void* h,
+                        const void* const* weights, double scale, const void* grad_out,
+                        const tpc_edge_buffers* eb, void* dh, void* dR, void* g_edge, void* forces,
+                        void* ws, size_t ws_bytes, void* stream) {
+  Errors E;
+  if (!c) {
+    E.add(TPC_ERR_INVALID, "ctx must be non-null");
+    return E.finish();
+  }
+  check_chunk(c, n, row_begin, row_end, edge_begin, edge_end, E);
+  if (n_edges < edge_end) E.add(TPC_ERR_INVALID, "n_edges must be >= edge_end");
+  if (!std::isfinite(scale)) E.add(TPC_ERR_INVALID, "scale must be finite");
+  const size_t va = 16;
+  need_ptr(row_ptr, "row_ptr", 4, E);
+  if (row_end > row_begin) {
+    need_ptr(h, "h", va, E);
+    need_ptr(grad_out, "grad_out", va, E);
+    need_ptr(dh, "dh", va, E);
+  }
+  if (edge_end > edge_begin) need_ptr(src, "src", 4, E);
+  if (n_edges > 0) need_ptr(g_edge, "g_edge", 8, E);
+  if (forces) {
+    need_ptr(forces, "forces", 8, E);
+    if (n_edges > 0) need_ptr(rev, "rev", 4, E);
+  }
+  if (dR && !aligned(dR, va)) E.add(TPC_ERR_INVALID, "dR must be 16-byte aligned");
+  if (!eb) {
+    E.add(TPC_ERR_INVALID, "edge buffers must be non-null");
+  } else if (edge_end > edge_begin) {
+    need_ptr(eb->Y, "eb.Y", va, E);
+    need_ptr(eb->ef, "eb.ef", va, E);
+    need_ptr(eb->rv, "eb.rv", va, E);
+    need_ptr(eb->R, "eb.R", va, E);
+  }
+  if (!weights) {
+    E.add(TPC_ERR_INVALID, "weights must be non-null");
+  } else {
+    for (int k = 0; k < c->spec.n_layers; ++k)
+      if (!weights[k]) E.add(TPC_ERR_INVALID, "weights[%d] must be non-null", k);
+  }
+  const int64_t ne = edge_end - edge_begin;
+  const BwdWs L = bwd_layout(c, ne > 0 ? ne : 0);
+  const size_t need = dR ? L.total_without_dR : L.total;
+  if (!ws) E.add(TPC_ERR_INVALID, "workspace must be non-null");
+  else if (!aligned(ws, 256)) E.add(TPC_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (ws && ws_bytes < need) E.add(TPC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  tpc_status st = E.finish();
+  if (st != TPC_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  int32_t* status = reinterpret_cast<int32_t*>(w + L.status);
+  if (c->spec.validate) {
+    st = run_csr_check(n, n_edges, row_ptr, src, nullptr, row_begin, row_end, edge_begin, edge_end,
+                       status, s);
+    if (st != TPC_OK) return st;
+  }
+  const int dt = c->spec.dtype;
+  const int L1 = c->spec.node_lmax, L2 = c->spec.sh_lmax, L3 = c->spec.out_lmax;
+  void* dRp = dR ? dR : static_cast<void*>(w + L.dR);
+  void* dY = w + L.dY;
+  void* d_ef = w + L.d_ef;
+  tpc::TPArgs ta{};
+  ta.row_ptr = row_ptr;
+  ta.src = src;
+  ta.row_begin = row_begin;
+  ta.row_end = row_end;
+  ta.edge_begin = edge_begin;
+  ta.C = c->spec.channels;
+  ta.scale = scale;
+  ta.h = h;
+  ta.Y = eb->Y;
+  ta.R = eb->R;
+  ta.G = grad_out;
+  ta.dR = dRp;
+  ta.dY = dY;
+  ta.out = dh;
+  if (ne > 0) {
+    TPC_HIP(tpc::launch_tp_bwd_edge(dt, L1, L2, L3, ta, s), "conv_bwd: tensor product (edges)");
+    TPC_HIP(tpc::launch_radial_bwd(dt, c->hidden, c->n_hidden, ne, c->tab.np * c->spec.channels,
+                                   eb->ef, dRp, weights, d_ef, s),
+            "conv_bwd: radial MLP");
+    TPC_HIP(tpc::launch_geom_bwd(dt, L2, ne, edge_begin, c->spec.r_cut, eb->rv, dY, d_ef, g_edge, s),
+            "conv_bwd: geometry");
+  }
+  TPC_HIP(tpc::launch_tp_bwd_node(dt, L1, L2, L3, ta, s), "conv_bwd: tensor product (nodes)");
+  if (forces)
+    TPC_HIP(tpc::launch_forces(dt, n, row_ptr, rev, g_edge, forces, s), "conv_bwd: forces");
+  g_last_error.clear();
+  return TPC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+// Compile-time coupling tables for the channelwise tensor-product convolution.
+//
+// Paths (FlashCart paper, section 2 "Irreducible Cartesian tensors"): a path
+// (l1, l2) -> l3 is admissible when |l1-l2| <= l3 <= l1+l2 and l1+l2+l3 is even
+// (natural parity).  Node irreps are l1 = 0..L1, edge harmonics l2 = 0..L2,
+// outputs l3 = 0..L3; paths are ordered lexicographically by (l1, l2, l3).
+//
+// Coefficients: for an admissible path the equivariant bilinear maps form a
+// one-dimensional space (same section), so any non-zero equivariant coupling
+// fixes them up to a scale.  This file builds the real Gaunt coefficients
+//   integral of S_{l1 m1} S_{l2 m2} S_{l3 m3} over the sphere
+// of the real harmonics S (z polar axis, m<0 <-> sin(|m| phi), m>0 <-> cos(m phi),
+// no Condon-Shortley phase) from the closed form of the complex Gaunt integral
+// as a product of two Wigner 3j symbols, each evaluated with the Racah sum, and
+// the unitary map from complex to real harmonics.  Each path's tensor is then
+// scaled to unit Frobenius norm (sign fixed by the integral).
+//
+// Everything is constexpr: the kernels unroll over the non-zero pattern with the
+// coefficients as literals, and the host exposes the same tables for inspection.
+#pragma once
+
+#include <cstdint>
+
+namespace tpc {
+
+constexpr int kMaxL = 3;
+constexpr int kMaxPaths = 32;
+
+constexpr double cx_sqrt(double x) {
+  if (x <= 0.0) return 0.0;
+  double g = x > 1.0 ? x : 1.0;
+  for (int i = 0; i < 200; ++i) {
+    double n = 0.5 * (g + x / g);
+    if (n == g) break;
+    g = n;
+  }
+  // one correction step toward the correctly rounded root
+  double r = g;
+  double e1 = r * r - x;
+  double up = r + r * 2.220446049250313e-16, dn = r - r * 2.220446049250313e-16;
+  double e_up = up * up - x, e_dn = dn * dn - x;
+  auto ab = [](double v) { return v < 0 ? -v : v; };
+  if (ab(e_up) < ab(e1)) r = up;
+  if (ab(e_dn) < ab(r * r - x)) r = dn;
+  return r;
+}
+
+constexpr double cx_fact(int n) {
+  double f = 1.0;
+  for (int i = 2; i <= n; ++i) f *= double(i);
+  return f;
+}
+
+// Wigner 3j symbol (j1 j2 j3; m1 m2 m3) by the Racah formula.
+constexpr double wigner3j(int j1, int j2, int j3, int m1, int m2, int m3) {
+  if (m1 + m2 + m3 != 0) return 0.0;
+  if (j3 < (j1 > j2 ? j1 - j2 : j2 - j1) || j3 > j1 + j2) return 0.0;
+  if (m1 < -j1 || m1 > j1 || m2 < -j2 || m2 > j2 || m3 < -j3 || m3 > j3) return 0.0;
+  double tri = cx_fact(j1 + j2 - j3) * cx_fact(j1 - j2 + j3) * cx_fact(-j1 + j2 + j3) /
+               cx_fact(j1 + j2 + j3 + 1);
+  double pre = cx_sqrt(tri * cx_fact(j1 + m1) * cx_fact(j1 - m1) * cx_fact(j2 + m2) *
+                       cx_fact(j2 - m2) * cx_fact(j3 + m3) * cx_fact(j3 - m3));
+  double sum = 0.0;
+  for (int k = 0; k <= j1 + j2 + j3; ++k) {
+    int a = j3 - j2 + k + m1, b = j3 - j1 + k - m2, c = j1 + j2 - j3 - k, d = j1 - k - m1,
+        e = j2 - k + m2;
+    if (a < 0 || b < 0 || c < 0 || d < 0 || e < 0) continue;
+    double t = 1.0 / (cx_fact(k) * cx_fact(a) * cx_fact(b) * cx_fact(c) * cx_fact(d) * cx_fact(e));
+    sum += (k % 2 ? -t : t);
+  }
+  int ph = j1 - j2 - m3;
+  double sgn = ((ph % 2) + 2) % 2 ? -1.0 : 1.0;
+  return sgn * pre * sum;
+}
+
+struct cplx {
+  double re, im;
+};
+constexpr cplx cmul(cplx a, cplx b) { return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re}; }
+
+// Coefficient of the complex harmonic Y_l^mu in the real harmonic S_{l m}.
+constexpr cplx u_real(int m, int mu) {
+  const double r2 = 0.70710678118654752440;  // 1/sqrt(2)
+  int a = m < 0 ? -m : m;
+  double sa = (a % 2) ? -1.0 : 1.0;           // (-1)^a
+  if (m == 0) return {mu == 0 ? 1.0 : 0.0, 0.0};
+  if (m > 0) {
+    if (mu == m) return {sa * r2, 0.0};
+    if (mu == -m) return {r2, 0.0};
+    return {0.0, 0.0};
+  }
+  if (mu == -a) return {0.0, r2};
+  if (mu == a) return {0.0, -sa * r2};
+  return {0.0, 0.0};
+}
+
+// Real Gaunt integral (up to a common positive factor per path).
+constexpr double real_gaunt(int l1, int l2, int l3, int m1, int m2, int m3) {
+  double w000 = wigner3j(l1, l2, l3, 0, 0, 0);
+  double re = 0.0;
+  for (int a = -l1; a <= l1; ++a)
+    for (int b = -l2; b <= l2; ++b) {
+      int c = -a - b;
+      if (c < -l3 || c > l3) continue;
+      cplx u = cmul(cmul(u_real(m1, a), u_real(m2, b)), u_real(m3, c));
+      if (u.re == 0.0 && u.im == 0.0) continue;
+      double g = w000 * wigner3j(l1, l2, l3, a, b, c);
+      re += u.re * g;
+    }
+  return re;
+}
+
+struct Path {
+  int l1, l2, l3;
+  int q;         // rank among the paths with the same l3
+  int nq;        // number of paths with this l3
+  int out_base;  // first output row of the l3 block
+};
+
+struct Table {
+  int L1, L2, L3;
+  int np;
+  int din, dsh, dout;
+  int nnz;
+  Path path[kMaxPaths];
+  double cg[kMaxPaths][7][7][7];
+
+  constexpr int out_row(int p, int m3) const {
+    return path[p].out_base + m3 * path[p].nq + path[p].q;
+  }
+};
+
+constexpr bool admissible(int l1, int l2, int l3) {
+  int d = l1 > l2 ? l1 - l2 : l2 - l1;
+  return d <= l3 && l3 <= l1 + l2 && ((l1 + l2 + l3) % 2 == 0);
+}
+
+constexpr Table make_table(int L1, int L2, int L3) {
+  Table t{};
+  t.L1 = L1;
+  t.L2 = L2;
+  t.L3 = L3;
+  t.din = (L1 + 1) * (L1 + 1);
+  t.dsh = (L2 + 1) * (L2 + 1);
+  int np = 0;
+  for (int l1 = 0; l1 <= L1; ++l1)
+    for (int l2 = 0; l2 <= L2; ++l2)
+      for (int l3 = 0; l3 <= L3; ++l3)
+        if (admissible(l1, l2, l3) && np < kMaxPaths) {
+          t.path[np] = Path{l1, l2, l3, 0, 0, 0};
+          ++np;
+        }
+  t.np = np;
+  int base = 0;
+  for (int l3 = 0; l3 <= L3; ++l3) {
+    int nq = 0;
+    for (int p = 0; p < np; ++p)
+      if (t.path[p].l3 == l3) ++nq;
+    int q = 0;
+    for (int p = 0; p < np; ++p)
+      if (t.path[p].l3 == l3) {
+        t.path[p].q = q++;
+        t.path[p].nq = nq;
+        t.path[p].out_base = base;
+      }
+    base += nq * (2 * l3 + 1);
+  }
+  t.dout = base;
+  int nnz = 0;
+  for (int p = 0; p < np; ++p) {
+    const int l1 = t.path[p].l1, l2 = t.path[p].l2, l3 = t.path[p].l3;
+    double nrm = 0.0;
+    for (int a = 0; a < 7; ++a)
+      for (int b = 0; b < 7; ++b)
+        for (int c = 0; c < 7; ++c) t.cg[p][a][b][c] = 0.0;
+    for (int a = 0; a <= 2 * l1; ++a)
+      for (int b = 0; b <= 2 * l2; ++b)
+        for (int c = 0; c <= 2 * l3; ++c) {
+          double g = real_gaunt(l1, l2, l3, a - l1, b - l2, c - l3);
+          t.cg[p][a][b][c] = g;
+          nrm += g * g;
+        }
+    nrm = cx_sqrt(nrm);
+    for (int a = 0; a <= 2 * l1; ++a)
+      for (int b = 0; b <= 2 * l2; ++b)
+        for (int c = 0; c <= 2 * l3; ++c) {
+          double v = t.cg[p][a][b][c] / nrm;
+          double av = v < 0 ? -v : v;
+          t.cg[p][a][b][c] = av < 1e-12 ? 0.0 : v;
+          if (av >= 1e-12) ++nnz;
+        }
+  }
+  t.nnz = nnz;
+  return t;
+}
+
+template <int L1, int L2, int L3>
+inline constexpr Table kTable = make_table(L1, L2, L3);
+
+// Non-zero test for the pattern (m1, m3) of path p: is any C[m1][m2][m3] != 0.
+constexpr bool m13_nonzero(const Table& t, int p, int a, int c) {
+  for (int b = 0; b <= 2 * t.path[p].l2; ++b)
+    if (t.cg[p][a][b][c] != 0.0) return true;
+  return false;
+}
+
+}  // namespace tpc

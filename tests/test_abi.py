@@ -1,0 +1,145 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every declared symbol, validates specs and arguments before any device work,
+and its compile-time coupling tables match the oracle's."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import tensor_product_conv_amd as tpc
+import workloads
+from oracle import cg, paths
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpconv.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(tpc_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_symbols_are_exported():
+    lib = tpc.library()
+    names = _declared()
+    assert {"tpc_nbr_build", "tpc_conv_fwd", "tpc_conv_bwd"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_no_symbol_outside_the_header():
+    out = os.popen(f"nm -D --defined-only {tpc.LIB_PATH}").read()
+    exported = {l.split()[-1] for l in out.splitlines() if l.split()[-2:-1] == ["T"]}
+    ours = {n for n in exported if n.startswith("tpc_")}
+    assert ours == set(_declared())
+
+
+@pytest.mark.parametrize("k", [0, 1, 2, 4])
+def test_context_sizes_match_configs(k):
+    c = workloads.config(k)
+    ctx = tpc.Context(tpc.spec_for(c))
+    L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"])
+    assert ctx.paths == L.paths
+    assert (ctx.n_paths, ctx.d_in, ctx.d_sh, ctx.d_out) == (c["n_paths"], c["d_in"], c["d_sh"], c["d_out"])
+    assert ctx.r_width == c["n_paths"] * c["C"]
+
+
+def test_coupling_tables_match_the_oracle():
+    c = workloads.config(4)
+    ctx = tpc.Context(tpc.spec_for(c))
+    nnz = 0
+    for p, (l1, l2, l3) in enumerate(ctx.paths):
+        t = ctx.cg_table(p)
+        np.testing.assert_allclose(t, cg.coupling(l1, l2, l3), atol=1e-14, rtol=0)
+        nnz += int(np.count_nonzero(t))
+    assert nnz == ctx.nnz_cg == 353
+
+
+def _spec(**over):
+    c = workloads.config(1)
+    s = tpc.spec_for(c)
+    for k, v in over.items():
+        setattr(s, k, v)
+    return s
+
+
+@pytest.mark.parametrize("over,status,needle", [
+    (dict(dtype="float32", channels=0), 1, "channels"),
+    (dict(node_lmax=4), 2, "node_lmax"),
+    (dict(n_bessel=6), 2, "n_bessel"),
+    (dict(poly_p=6), 2, "poly_p"),
+    (dict(r_cut=-1.0), 1, "r_cut"),
+    (dict(channels=96, layer_dims=[8, 64, 64, 64, 960]), 2, "no fused kernel"),
+    (dict(layer_dims=[8, 64, 64, 64, 999]), 1, "paths*channels"),
+    (dict(layer_dims=[8, 48, 1280]), 2, "radial MLP"),
+    (dict(layer_dims=[7, 64, 1280]), 1, "layer_dims[0]"),
+])
+def test_spec_validation(over, status, needle):
+    with pytest.raises(tpc.TpcError) as ei:
+        tpc.Context(_spec(**over))
+    assert ei.value.status == status
+    assert needle in ei.value.message
+
+
+def test_every_failed_check_is_listed():
+    with pytest.raises(tpc.TpcError) as ei:
+        tpc.Context(_spec(n_bessel=6, poly_p=7, r_cut=0.0))
+    m = ei.value.message
+    assert "n_bessel" in m and "poly_p" in m and "r_cut" in m
+    assert ei.value.status == 1        # INVALID outranks UNSUPPORTED
+
+
+def test_workspace_query():
+    c = workloads.config(2)
+    ctx = tpc.Context(tpc.spec_for(c))
+    cell = np.eye(3) * 68.94
+    nb = ctx.workspace_bytes(tpc.OP_NBR, 32768, 0, cell)
+    assert nb >= 2 * 4 * 32768
+    bw = ctx.workspace_bytes(tpc.OP_BWD, 32768, 1000)
+    assert bw >= 1000 * (16 + 8 + 17 * 128) * 4
+    with pytest.raises(tpc.TpcError) as ei:
+        ctx.workspace_bytes(tpc.OP_NBR, 10, 0, np.zeros((3, 3)))
+    assert "singular" in ei.value.message
+
+
+def _raw(ctx):
+    return tpc.library(), ctx._h
+
+
+def test_nbr_build_argument_checks_run_before_device_work():
+    lib, h = _raw(tpc.Context(_spec()))
+    ne = ctypes.c_int64()
+    cell = (ctypes.c_double * 9)(*([0.0] * 9))
+    st = lib.tpc_nbr_build(h, 10, None, cell, None, 5, None, None, None, None, ctypes.byref(ne),
+                           None, 0, None)
+    assert st == 1
+    m = lib.tpc_last_error().decode()
+    for needle in ("row_ptr", "pos", "src, shift and rev", "workspace", "singular"):
+        assert needle in m
+
+
+def test_conv_argument_checks_run_before_device_work():
+    lib, h = _raw(tpc.Context(_spec()))
+    eb = tpc._EdgeBuffers()
+    cell = (ctypes.c_double * 9)(*np.eye(3).reshape(-1).tolist())
+    st = lib.tpc_conv_fwd(h, 10, None, cell, None, None, None, 0, 11, 0, 5, None, None, 1.0, None,
+                          ctypes.byref(eb), None, 0, None)
+    assert st == 1
+    m = lib.tpc_last_error().decode()
+    for needle in ("row_begin <= row_end <= n_atoms", "row_ptr", "eb.Y", "weights"):
+        assert needle in m
+    st = lib.tpc_conv_bwd(h, 10, 3, None, None, None, 0, 5, 0, 5, None, None, float("nan"), None,
+                          ctypes.byref(eb), None, None, None, None, None, 0, None)
+    assert st == 1
+    m = lib.tpc_last_error().decode()
+    for needle in ("n_edges must be >= edge_end", "scale", "g_edge", "workspace"):
+        assert needle in m
+
+
+def test_status_strings():
+    lib = tpc.library()
+    assert lib.tpc_status_string(3) == b"edge capacity too small"
+    assert lib.tpc_status_string(99) == b"unknown status"

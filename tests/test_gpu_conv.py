@@ -1,0 +1,164 @@
+"""GPU convolution forward and backward against the oracle, element by element
+on full outputs (tiny, small) or sampled rows (medium, large), plus
+determinism, chunking, preconditions and invariants that hold at any size."""
+import numpy as np
+import pytest
+
+import tensor_product_conv_amd as tpc
+from _gpu import TOL, Case, np_csr, rel, run_chunked, say, torch
+from oracle import conv
+
+pytestmark = pytest.mark.gpu
+
+
+def _prob(case, nl):
+    rp, src, shift, _ = np_csr(nl)
+    return case.oracle((rp, src, shift))
+
+
+@pytest.mark.parametrize("k", [0, 1])
+def test_full_parity(k):
+    case = Case(k)
+    nl = case.nbr()
+    tol = TOL[case.cfg["dtype"]]
+    res = run_chunked(case, nl, chunks=1, keep_edges=np.arange(nl.n_edges))
+    prob = _prob(case, nl)
+    say(f"[cpu] oracle cfg={k}")
+    out_ref = prob.forward()
+    b = prob.backward()
+    assert rel(res["out"].cpu().numpy(), out_ref) < tol
+    assert rel(res["dh"].cpu().numpy(), b["dh"]) < tol
+    dR = np.stack([res["dR"][e] for e in range(nl.n_edges)])
+    assert rel(dR, b["dR"]) < tol
+    assert rel(res["g_edge"].cpu().numpy(), b["g"]) < tol
+    assert rel(res["forces"].cpu().numpy(), b["F"]) < tol
+    # per-edge intermediates
+    _, _, Y, ef, R = prob.edge_terms(np.arange(nl.n_edges))
+    assert rel(res["eb"].Y.cpu().numpy(), Y) < tol
+    assert rel(res["eb"].ef.cpu().numpy(), ef) < tol
+    assert rel(res["eb"].R.cpu().numpy(), R) < tol
+
+
+def _sampled_check(case, nl, res, rows, atoms, edges):
+    prob = _prob(case, nl)
+    tol = TOL[case.cfg["dtype"]]
+    say(f"[cpu] oracle sampled cfg={case.k}: {len(rows)} rows, {len(atoms)} atoms, {len(edges)} edges")
+    out_ref = prob.forward_rows(rows)
+    assert rel(res["out"][rows].cpu().numpy(), out_ref) < tol
+    b = prob.edge_backward(edges)
+    dR = np.stack([res["dR"][int(e)] for e in edges])
+    assert rel(dR, b["dR"]) < tol
+    assert rel(res["g_edge"][edges].cpu().numpy(), b["g"]) < tol
+    assert rel(res["dh"][atoms].cpu().numpy(), prob.dh_atoms(atoms)) < tol
+    assert rel(res["forces"][atoms].cpu().numpy(), prob.forces_atoms(atoms)) < tol
+
+
+def _samples(nl, N, n_rows, seed):
+    rp = nl.row_ptr.cpu().numpy()
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, n_rows, replace=False)]))
+    edges = np.concatenate([np.arange(rp[i], rp[i + 1]) for i in rows[:16]])
+    return rows, edges
+
+
+def test_medium_parity_sampled():
+    case = Case(3)
+    nl = case.nbr()
+    rows, edges = _samples(nl, case.N, 96, 11)
+    atoms = np.unique(np.concatenate([np.arange(64), rows[:32]]))   # includes the 0-63 slice
+    res = run_chunked(case, nl, chunks=1, keep_edges=edges)
+    _sampled_check(case, nl, res, rows, atoms, edges)
+
+
+def test_large_parity_sampled_chunked():
+    case = Case(4)
+    nl = case.nbr()
+    rows, edges = _samples(nl, case.N, 40, 12)
+    res = run_chunked(case, nl, chunks=3, keep_edges=edges)
+    _sampled_check(case, nl, res, rows, rows[:24], edges)
+
+
+def test_chunked_equals_unchunked():
+    case = Case(1)
+    nl = case.nbr()
+    a = run_chunked(case, nl, chunks=1)
+    b = run_chunked(case, nl, chunks=5)
+    for key in ("out", "dh", "forces", "g_edge"):
+        assert torch().equal(a[key], b[key]), key
+
+
+def test_bitwise_deterministic():
+    case = Case(2)
+    nl = case.nbr()
+    a = run_chunked(case, nl, keep_edges=np.arange(0, nl.n_edges, 997))
+    b = run_chunked(case, nl, keep_edges=np.arange(0, nl.n_edges, 997))
+    for key in ("out", "dh", "forces", "g_edge"):
+        assert torch().equal(a[key], b[key]), key
+    for e in a["dR"]:
+        np.testing.assert_array_equal(a["dR"][e], b["dR"][e])
+
+
+def test_invariants_at_medium_size():
+    """Sum of forces vanishes; L is linear in h: <dh, h> = L."""
+    case = Case(3)
+    nl = case.nbr()
+    res = run_chunked(case, nl)
+    t = torch()
+    F = res["forces"].double()
+    assert float(F.sum(0).abs().max()) < 1e-4 * float(F.abs().max()) * np.sqrt(case.N)
+    GO = case.G.double() * res["out"].double()
+    L = float(GO.sum())
+    hdh = float((case.h.double() * res["dh"].double()).sum())
+    assert abs(L - hdh) <= 1e-4 * float(GO.abs().sum())
+
+
+def test_validation_refuses_an_unsorted_csr():
+    case = Case(0, validate=True)
+    nl = case.nbr()
+    rp = nl.row_ptr.cpu().numpy()
+    i = int(np.argmax(np.diff(rp) >= 2))
+    bad = nl.src.clone()
+    a, b = int(rp[i]), int(rp[i]) + 1
+    bad[a], bad[b] = nl.src[b].item(), nl.src[a].item()
+    if int(bad[a]) == int(bad[b]):            # same sender: swap shifts instead
+        pytest.skip("first multi-edge row has a repeated sender")
+    bad_nl = tpc.NeighbourList(nl.row_ptr, bad, nl.shift, nl.rev, nl.n_edges)
+    say("[gpu] conv_fwd with validate on an unsorted row")
+    with pytest.raises(tpc.TpcError) as ei:
+        case.ctx.conv_fwd(case.pos, case.cell, bad_nl, case.h, case.W, 1.0)
+    assert ei.value.status == 4
+    # the sorted list passes
+    out, _ = case.ctx.conv_fwd(case.pos, case.cell, nl, case.h, case.W, 1.0)
+    torch().cuda.synchronize()
+
+
+def test_empty_rows_and_zero_edges():
+    t = torch()
+    case = Case(0)
+    ctx = case.ctx
+    pos = t.tensor([[1.0, 1.0, 1.0], [7.0, 7.0, 7.0], [1.5, 1.0, 1.0]], dtype=t.float64, device="cuda")
+    cell = np.eye(3) * 20.0
+    nl = ctx.nbr_build(pos, cell)
+    assert nl.row_ptr.cpu().tolist() == [0, 1, 1, 2]
+    h = case.h[:3].contiguous()
+    G = case.G[:3].contiguous()
+    out, eb = ctx.conv_fwd(pos, cell, nl, h, case.W, 1.0)
+    dh, dR, F, g = ctx.conv_bwd(nl, h, case.W, 1.0, G, eb)
+    t.cuda.synchronize()
+    assert float(out[1].abs().max()) == 0.0 and float(dh[1].abs().max()) == 0.0
+    assert float(F[1].abs().max()) == 0.0
+    prob = conv.Problem(case.layout, pos.cpu().numpy(), cell, *[x.cpu().numpy() for x in
+                        (nl.row_ptr, nl.src, nl.shift)], h.cpu().numpy(), case.d["W"], 4.0, 1.0,
+                        G.cpu().numpy())
+    assert rel(out.cpu().numpy(), prob.forward()) < 1e-10
+    b = prob.backward()
+    assert rel(F.cpu().numpy(), b["F"]) < 1e-10
+    # no edges at all
+    pos2 = t.tensor([[1.0, 1.0, 1.0], [9.0, 9.0, 9.0]], dtype=t.float64, device="cuda")
+    nl2 = ctx.nbr_build(pos2, cell)
+    assert nl2.n_edges == 0
+    out2, eb2 = ctx.conv_fwd(pos2, cell, nl2, h[:2].contiguous(), case.W, 1.0)
+    dh2, _, F2, _ = ctx.conv_bwd(nl2, h[:2].contiguous(), case.W, 1.0, G[:2].contiguous(), eb2)
+    t.cuda.synchronize()
+    assert float(out2.abs().max()) == 0.0 and float(dh2.abs().max()) == 0.0
+    assert float(F2.abs().max()) == 0.0
