@@ -1,0 +1,270 @@
+"""Benchmark of the equivariant interaction convolution on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload medium]
+
+One step is the whole hot path over the synthetic medium water system
+(32,768 atoms, C = 128, node irreps 0e+1o+2e, harmonics l <= 3, outputs
+l <= 3, radial MLP 8-64-64-64-2176, about 2.97 M directed edges): the
+periodic neighbour build, the forward convolution and its backward
+(dL/dh, dL/dR, forces).  Inputs are resident in HBM before timing starts.
+The metric is directed edges per second through that step.
+
+Per-kernel durations come from HIP events the library records around each
+launch on the launch stream during the timed steps; the dominant kernel's
+algorithmic bytes (or flops) per launch divided by its average duration gives
+the roofline line.  HBM traffic from rocprofv3 counters is read from
+profiles/traffic.json when it was measured on the current kernel sources.
+The CPU baseline times the float64 oracle on a bounded sample of receivers.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_F32_PEAK = 157.3e12   # flop/s, dense fp32 matrix
+VALU_F32_PEAK = 78.6e12    # flop/s, fp32 FMA without packed math: 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz
+
+KERNEL_SOURCES = {
+    "tp_fwd": ["tp_impl.hpp", "tp_fwd.hip", "tables.hpp"],
+    "tp_bwd_edge": ["tp_impl.hpp", "tp_bwd_edge.hip", "tables.hpp"],
+    "tp_bwd_node": ["tp_impl.hpp", "tp_bwd_node.hip", "tables.hpp"],
+    "radial_fwd": ["radial.hip"],
+    "radial_bwd": ["radial.hip"],
+    "geom_fwd": ["geom.hip"],
+    "geom_bwd": ["geom.hip"],
+}
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "tensor_product_conv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(kernel, N, E, cfg, ctx):
+    """(bytes, flops) one launch of ``kernel`` must move / compute (fp32)."""
+    T = 4
+    C, P = cfg["C"], ctx.n_paths
+    din, dsh, dout, PC = ctx.d_in, ctx.d_sh, ctx.d_out, ctx.r_width
+    H = cfg["hidden"][0]
+    NH = len(cfg["hidden"])
+    tabs = [ctx.cg_table(p) for p in range(ctx.n_paths)]       # the library's own tables
+    nnz = sum(int((t != 0).sum()) for t in tabs)
+    m13 = sum(int((t != 0).any(axis=1).sum()) for t in tabs)
+    csr = 4 * (N + 1) + 4 * E
+    if kernel == "tp_fwd":
+        return (E * (T * PC + T * dsh) + N * T * C * (din + dout) + csr,
+                E * (2 * nnz + C * (2 * m13 + 2 * dout)))
+    if kernel == "tp_bwd_edge":
+        return (E * (2 * T * PC + 2 * T * dsh) + N * T * C * (din + dout) + csr,
+                E * (4 * nnz + C * (4 * m13 + 3 * dout)))
+    if kernel == "tp_bwd_node":
+        return (E * (T * PC + T * dsh) + N * T * C * (dout + din) + csr,
+                E * (2 * nnz + C * (2 * m13 + dout)))
+    hidden = 2 * (8 * H + (NH - 1) * H * H)
+    if kernel == "radial_fwd":
+        return E * (8 * T + T * PC), E * (hidden + 2 * H * PC)
+    if kernel == "radial_bwd":
+        return E * (8 * T + T * PC + 8 * T), E * (2 * hidden + 2 * H * PC)
+    return None, None
+
+
+def roofline_for(kernel, per_launch_s, N, E, cfg, ctx):
+    nbytes, flops = algorithmic(kernel, N, E, cfg, ctx)
+    if nbytes is None:
+        return None
+    if kernel.startswith("radial"):
+        ach = flops / per_launch_s
+        r = dict(bound="mfma", achieved=ach / 1e12, peak=MFMA_F32_PEAK / 1e12, unit="TFLOP/s",
+                 frac=ach / MFMA_F32_PEAK, algorithmic_flops_per_launch=flops)
+    else:
+        ach = nbytes / per_launch_s
+        r = dict(bound="hbm", achieved=ach / 1e9, peak=HBM_PEAK / 1e9, unit="GB/s",
+                 frac=ach / HBM_PEAK, algorithmic_bytes_per_launch=nbytes,
+                 vector_alu_frac=(flops / per_launch_s) / VALU_F32_PEAK)
+    r["kernel"] = kernel
+    r["traffic"] = measured_traffic(kernel)
+    return r
+
+
+def measured_traffic(kernel):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    rec = t.get(kernel)
+    if not rec or rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case_data, nl_np, budget_s=15.0):
+    """Oracle conv forward + backward on a sample of receiver rows (1 thread)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import conv, paths
+
+    d = case_data
+    c = d["cfg"]
+    rp, src, shift = nl_np
+    L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"])
+    prob = conv.Problem(L, d["pos"], d["cell"], rp, src, shift, d["h"], d["W"], c["r_cut"],
+                        conv.scale_for(c, len(d["pos"]), rp[-1]), d["G"])
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(d["pos"]))
+    done_edges, used, t_total = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        batch = 16
+        while t_total < budget_s and used < len(order):
+            rows = np.sort(order[used:used + batch])
+            used += batch
+            e, _ = conv.edges_of_rows(rp, rows)
+            t0 = time.perf_counter()
+            prob.forward_rows(rows)
+            prob.edge_backward(e)
+            t_total += time.perf_counter() - t0
+            done_edges += len(e)
+            batch = min(256, batch * 2)
+    return dict(value=done_edges / t_total, unit="edges/s", cores=1, kind="oracle",
+                sample=f"{used} random receiver rows ({done_edges} edges) of the same system: "
+                       f"float64 oracle forward + per-edge backward (dR, dY, dh contributions, "
+                       f"edge gradients), one thread, {t_total:.1f} s; neighbour build not included")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="medium", choices=["medium", "small"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    a = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE={world}); "
+              "the convolution is benchmarked at N=1 and no multi-GPU path is built", flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import tensor_product_conv_amd as tpc
+    import workloads
+
+    k = {"small": 1, "medium": 3}[a.workload]
+    d = workloads.generate(k)
+    cfg = d["cfg"]
+    dev = "cuda"
+    ctx = tpc.Context(tpc.spec_for(cfg))
+    pos = torch.from_numpy(d["pos"]).to(dev)
+    species = torch.from_numpy(d["species"]).to(dev)
+    h = torch.from_numpy(d["h"]).to(dev)
+    W = [torch.from_numpy(w).to(dev) for w in d["W"]]
+    G = torch.from_numpy(d["G"]).to(dev)
+    cell = d["cell"]
+    N = cfg["N"]
+
+    nl = ctx.nbr_build(pos, cell, species)
+    E = nl.n_edges
+    scale = float(N) / E if cfg["scale"] == "inv_avg_neighbors" else 1.0
+    out = torch.empty((N, ctx.d_out, cfg["C"]), dtype=ctx.dtype, device=dev)
+    eb = ctx.alloc_edge_buffers(E, dev)
+    dh = torch.empty_like(h)
+    dR = torch.empty((E, ctx.r_width), dtype=ctx.dtype, device=dev)
+    g_edge = torch.empty((E, 3), dtype=ctx.dtype, device=dev)
+    forces = torch.empty((N, 3), dtype=ctx.dtype, device=dev)
+    ws_n = ctx._workspace(ctx.workspace_bytes(tpc.OP_NBR, N, 0, cell), dev)
+    ws_f = ctx._workspace(ctx.workspace_bytes(tpc.OP_FWD, N, E), dev)
+    ws_b = ctx._workspace(ctx.workspace_bytes(tpc.OP_BWD, N, E), dev)
+
+    def step():
+        nl2 = ctx.nbr_build(pos, cell, species, edge_cap=E, into=nl, workspace=ws_n)
+        ctx.conv_fwd(pos, cell, nl2, h, W, scale, out=out, eb=eb, workspace=ws_f)
+        ctx.conv_bwd(nl2, h, W, scale, G, eb, dh=dh, dR=dR, g_edge=g_edge, forces=forces,
+                     workspace=ws_b)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    tpc.timing_collect()
+    tpc.timing_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(a.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tpc.timing_enable(False)
+    kt = tpc.timing_collect()
+    ms_per_step = start.elapsed_time(stop) / a.steps
+    value = E / (ms_per_step * 1e-3)
+
+    per_kernel = {n: dict(avg_ms=tot / cnt, launches_per_step=cnt / a.steps, ms_per_step=tot / a.steps)
+                  for n, (tot, cnt) in kt.items()}
+    fwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0) for n in ("geom_fwd", "radial_fwd", "tp_fwd"))
+    bwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0)
+                 for n in ("tp_bwd_edge", "radial_bwd", "geom_bwd", "tp_bwd_node", "forces"))
+    nbr_ms = sum(v["ms_per_step"] for n, v in per_kernel.items() if n.startswith("nbr"))
+    dominant = max((n for n in per_kernel if n in KERNEL_SOURCES), key=lambda n: per_kernel[n]["ms_per_step"])
+    roof = roofline_for(dominant, per_kernel[dominant]["avg_ms"] * 1e-3, N, E, cfg, ctx)
+    kernels = {}
+    for n, v in per_kernel.items():
+        r = roofline_for(n, v["avg_ms"] * 1e-3, N, E, cfg, ctx) if n in KERNEL_SOURCES else None
+        kernels[n] = dict(avg_ms=round(v["avg_ms"], 4), launches_per_step=v["launches_per_step"],
+                          **({"bound": r["bound"], "frac": round(r["frac"], 4)} if r else {}))
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        rp, src, shift = (nl.row_ptr.cpu().numpy(), nl.src.cpu().numpy(), nl.shift.cpu().numpy())
+        cpu = cpu_baseline(d, (rp, src, shift), a.cpu_budget)
+
+    line = {
+        "metric": "edges/s fwd and fwd+bwd, 128ch sh l<=3 TP conv; % of HBM roofline",
+        "value": value,
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg['name']} ({'water' if k == 3 else cfg['geometry']}) "
+                               f"N={N} E={E} C={cfg['C']} node_lmax={cfg['l1max']} "
+                               f"sh_lmax={cfg['sh_lmax']} out_lmax={cfg['out_lmax']} "
+                               f"mlp={'-'.join(map(str, cfg['layer_dims']))}: "
+                               "nbr_build + conv_fwd + conv_bwd (forces)",
+                   "n_atoms": N, "n_edges": E, "channels": cfg["C"], "paths": ctx.n_paths,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "fwd_edges_per_s": E / (fwd_ms * 1e-3) if fwd_ms else None,
+        "fwd_bwd_edges_per_s": E / ((fwd_ms + bwd_ms) * 1e-3) if fwd_ms else None,
+        "nbr_build_ms": nbr_ms,
+        "kernels": kernels,
+        "wall_s": wall,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -213,6 +213,21 @@ tpc_status tpc_conv_bwd(const tpc_ctx* ctx, int64_t n_atoms, int64_t n_edges,
                         void* dh, void* dR, void* g_edge, void* forces, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* Per-kernel timing with HIP events, for benchmarks and profiling.  While
+ * enabled on a thread, every kernel the library launches from that thread is
+ * bracketed by two hipEventRecord calls on the launch stream.
+ * tpc_timing_collect waits for the recorded events, writes one entry per
+ * kernel name (total milliseconds and launch count, in first-launch order,
+ * at most `max` entries), sets *n and clears the record.  Events come from a
+ * per-thread pool created on first use; no device memory is allocated. */
+typedef struct tpc_kernel_time {
+  char name[32];
+  double total_ms;
+  int64_t launches;
+} tpc_kernel_time;
+tpc_status tpc_timing_enable(int on);
+tpc_status tpc_timing_collect(tpc_kernel_time* out, int max, int* n);
+
 const char* tpc_status_string(tpc_status status);
 
 /* Messages of the last failed call on this thread ("" if none). */

@@ -20,7 +20,7 @@ import os
 from dataclasses import dataclass, field
 
 __all__ = ["Spec", "Context", "NeighbourList", "EdgeBuffers", "TpcError", "library",
-           "nbr_build", "conv_fwd", "conv_bwd", "LIB_PATH"]
+           "nbr_build", "conv_fwd", "conv_bwd", "timing_enable", "timing_collect", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpconv.so")
 
@@ -50,6 +50,10 @@ class _Info(ctypes.Structure):
     _fields_ = [("n_paths", ctypes.c_int), ("d_in", ctypes.c_int), ("d_sh", ctypes.c_int),
                 ("d_out", ctypes.c_int), ("r_width", ctypes.c_int), ("nnz_cg", ctypes.c_int),
                 ("paths", (ctypes.c_int * 3) * TPC_MAX_PATHS)]
+
+
+class _KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("total_ms", ctypes.c_double), ("launches", ctypes.c_int64)]
 
 
 class _EdgeBuffers(ctypes.Structure):
@@ -87,12 +91,16 @@ def library():
                                  ctypes.POINTER(_VP), ctypes.c_double, _VP,
                                  ctypes.POINTER(_EdgeBuffers), _VP, _VP, _VP, _VP, _VP,
                                  ctypes.c_size_t, _VP]
+    lib.tpc_timing_enable.argtypes = [ctypes.c_int]
+    lib.tpc_timing_collect.argtypes = [ctypes.POINTER(_KernelTime), ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_int)]
     lib.tpc_status_string.argtypes = [ctypes.c_int]
     lib.tpc_status_string.restype = ctypes.c_char_p
     lib.tpc_last_error.argtypes = []
     lib.tpc_last_error.restype = ctypes.c_char_p
     for name in ("tpc_ctx_create", "tpc_ctx_info", "tpc_cg_table", "tpc_workspace_query",
-                 "tpc_nbr_build", "tpc_conv_fwd", "tpc_conv_bwd"):
+                 "tpc_nbr_build", "tpc_conv_fwd", "tpc_conv_bwd", "tpc_timing_enable",
+                 "tpc_timing_collect"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -101,6 +109,19 @@ def library():
 def _check(status):
     if status != 0:
         raise TpcError(status, library().tpc_last_error().decode())
+
+
+def timing_enable(on=True):
+    """Record HIP events around every kernel the library launches (this thread)."""
+    _check(library().tpc_timing_enable(int(bool(on))))
+
+
+def timing_collect():
+    """{kernel name: (total ms, launches)} since the last collect; waits for the events."""
+    buf = (_KernelTime * 64)()
+    n = ctypes.c_int()
+    _check(library().tpc_timing_collect(buf, 64, ctypes.byref(n)))
+    return {buf[k].name.decode(): (buf[k].total_ms, buf[k].launches) for k in range(n.value)}
 
 
 def _torch():
@@ -221,19 +242,27 @@ class Context:
         return t.empty(max(int(nbytes), 256), dtype=t.uint8, device=device)
 
     # ---- neighbour list ---------------------------------------------------
-    def nbr_build(self, pos, cell, species=None, edge_cap=None):
-        """Receiver-sorted CSR; grows the edge buffers once if the first guess is short."""
+    def nbr_build(self, pos, cell, species=None, edge_cap=None, into=None, workspace=None):
+        """Receiver-sorted CSR; grows the edge buffers once if the first guess is short.
+
+        ``into`` (a NeighbourList whose arrays hold ``edge_cap`` edges) reuses
+        existing buffers; ``workspace`` reuses a workspace tensor.
+        """
         t = _torch()
         N = pos.shape[0]
         dev = pos.device
-        ws = self._workspace(self.workspace_bytes(OP_NBR, N, 0, cell), dev)
+        ws = workspace if workspace is not None else \
+            self._workspace(self.workspace_bytes(OP_NBR, N, 0, cell), dev)
         c = _cell_arg(cell)
         cap = int(edge_cap) if edge_cap is not None else max(64, N * 64)
-        row_ptr = t.empty(N + 1, dtype=t.int32, device=dev)
+        row_ptr = into.row_ptr if into is not None else t.empty(N + 1, dtype=t.int32, device=dev)
         for _ in range(2):
-            src = t.empty(cap, dtype=t.int32, device=dev)
-            shift = t.empty((cap, 3), dtype=t.int32, device=dev)
-            rev = t.empty(cap, dtype=t.int32, device=dev)
+            if into is not None:
+                src, shift, rev = into.src, into.shift, into.rev
+            else:
+                src = t.empty(cap, dtype=t.int32, device=dev)
+                shift = t.empty((cap, 3), dtype=t.int32, device=dev)
+                rev = t.empty(cap, dtype=t.int32, device=dev)
             ne = _I64()
             st = library().tpc_nbr_build(self._h, N, _ptr(pos), c, _ptr(species), cap, _ptr(row_ptr),
                                          _ptr(src), _ptr(shift), _ptr(rev), ctypes.byref(ne), _ptr(ws),
@@ -255,7 +284,7 @@ class Context:
                            R=t.empty((n_edges, self.r_width), dtype=self.dtype, device=device))
 
     def conv_fwd(self, pos, cell, nl: NeighbourList, h, W, scale=1.0, out=None, eb=None,
-                 rows=None, edges=None):
+                 rows=None, edges=None, workspace=None):
         """out [N, d_out, C]; returns (out, edge buffers for conv_bwd)."""
         t = _torch()
         N = pos.shape[0]
@@ -268,7 +297,8 @@ class Context:
         eb.edge_begin, eb.edge_end, eb.row_begin, eb.row_end = eb_, ee, rb, re_
         wp = (_VP * len(W))(*[w.data_ptr() for w in W])
         ebc = eb.to_c()
-        ws = self._workspace(self.workspace_bytes(OP_FWD, N, ee - eb_), h.device)
+        ws = workspace if workspace is not None else \
+            self._workspace(self.workspace_bytes(OP_FWD, N, ee - eb_), h.device)
         _check(library().tpc_conv_fwd(self._h, N, _ptr(pos), _cell_arg(cell), _ptr(nl.row_ptr),
                                       _ptr(nl.src), _ptr(nl.shift), rb, re_, eb_, ee, _ptr(h), wp,
                                       float(scale), _ptr(out), ctypes.byref(ebc), _ptr(ws), ws.numel(),
@@ -277,7 +307,7 @@ class Context:
 
     # ---- backward -------------------------------------------------------------
     def conv_bwd(self, nl: NeighbourList, h, W, scale, G, eb: EdgeBuffers, dh=None, dR=None,
-                 g_edge=None, want_dR=True, want_forces=True, forces=None):
+                 g_edge=None, want_dR=True, want_forces=True, forces=None, workspace=None):
         """Returns (dh, dR or None, forces or None, g_edge)."""
         t = _torch()
         N = h.shape[0]
@@ -294,7 +324,8 @@ class Context:
             forces = None
         wp = (_VP * len(W))(*[w.data_ptr() for w in W])
         ebc = eb.to_c()
-        ws = self._workspace(self.workspace_bytes(OP_BWD, N, ne), h.device)
+        ws = workspace if workspace is not None else \
+            self._workspace(self.workspace_bytes(OP_BWD, N, ne), h.device)
         _check(library().tpc_conv_bwd(self._h, N, nl.n_edges, _ptr(nl.row_ptr), _ptr(nl.src),
                                       _ptr(nl.rev), eb.row_begin, eb.row_end, eb.edge_begin,
                                       eb.edge_end, _ptr(h), wp, float(scale), _ptr(G), ctypes.byref(ebc),

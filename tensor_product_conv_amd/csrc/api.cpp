@@ -72,6 +72,45 @@ tpc_status device_error(hipError_t e, const char* where) {
     if (_e != hipSuccess) return device_error(_e, where);     \
   } while (0)
 
+// Optional per-kernel event timing (tpc_timing_enable / tpc_timing_collect).
+struct KernelMark {
+  const char* name;
+  hipEvent_t start, stop;
+};
+thread_local bool g_timing = false;
+thread_local std::vector<KernelMark> g_marks;
+thread_local std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pooled_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch `call` (a hipError_t expression enqueuing on stream s); time it when
+// timing is on.
+#define TPC_LAUNCH(name, s, call, where)                                   \
+  do {                                                                     \
+    hipEvent_t _a = nullptr;                                               \
+    if (g_timing && (_a = pooled_event())) hipEventRecord(_a, s);          \
+    hipError_t _e = (call);                                                \
+    if (_e != hipSuccess) return device_error(_e, where);                  \
+    if (_a) {                                                              \
+      hipEvent_t _b = pooled_event();                                      \
+      if (_b) {                                                            \
+        hipEventRecord(_b, s);                                             \
+        g_marks.push_back(KernelMark{name, _a, _b});                       \
+      } else {                                                             \
+        g_event_pool.push_back(_a);                                        \
+      }                                                                    \
+    }                                                                      \
+  } while (0)
+
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -210,6 +249,45 @@ const char* tpc_status_string(tpc_status s) {
 }
 
 const char* tpc_last_error(void) { return g_last_error.c_str(); }
+
+tpc_status tpc_timing_enable(int on) {
+  g_timing = on != 0;
+  return TPC_OK;
+}
+
+tpc_status tpc_timing_collect(tpc_kernel_time* out, int max, int* n) {
+  Errors E;
+  if (!n || (max > 0 && !out)) {
+    E.add(TPC_ERR_INVALID, "out and n must be non-null");
+    return E.finish();
+  }
+  std::vector<tpc_kernel_time> agg;
+  hipError_t err = hipSuccess;
+  for (auto& m : g_marks) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(m.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, m.start, m.stop);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    size_t k = 0;
+    while (k < agg.size() && std::strcmp(agg[k].name, m.name) != 0) ++k;
+    if (k == agg.size()) {
+      tpc_kernel_time t{};
+      std::snprintf(t.name, sizeof(t.name), "%s", m.name);
+      agg.push_back(t);
+    }
+    agg[k].total_ms += ms;
+    agg[k].launches += 1;
+    g_event_pool.push_back(m.start);
+    g_event_pool.push_back(m.stop);
+  }
+  g_marks.clear();
+  if (err != hipSuccess) return device_error(err, "timing");
+  const int cnt = (int)agg.size() < max ? (int)agg.size() : max;
+  for (int k = 0; k < cnt; ++k) out[k] = agg[k];
+  *n = cnt;
+  g_last_error.clear();
+  return TPC_OK;
+}
 
 tpc_status tpc_ctx_create(const tpc_spec* spec, tpc_ctx** out) {
   Errors E;
@@ -397,13 +475,13 @@ tpc_status tpc_nbr_build(const tpc_ctx* c, int64_t n, const double* pos, const d
   TPC_HIP(tpc::launch_fill_i32(status, 8, 0, s), "nbr_build: clear status");
   TPC_HIP(tpc::launch_fill_i32(bin_start, nbin + 1, 0, s), "nbr_build: clear bins");
   TPC_HIP(tpc::launch_fill_i32(cursor, nbin, 0, s), "nbr_build: clear cursors");
-  TPC_HIP(tpc::launch_nbr_bin(n, pos, g, species, c->spec.n_species, bin_of, bin_start, status, s),
-          "nbr_build: bin");
-  TPC_HIP(tpc::launch_scan_exclusive(bin_start, nbin, partials, s), "nbr_build: bin scan");
-  TPC_HIP(tpc::launch_nbr_scatter(n, bin_of, bin_start, cursor, bin_atoms, s), "nbr_build: scatter");
-  TPC_HIP(tpc::launch_nbr_count(n, pos, g, bin_of, bin_start, bin_atoms, row_ptr, status, s),
-          "nbr_build: count");
-  TPC_HIP(tpc::launch_scan_exclusive(row_ptr, n, partials, s), "nbr_build: row scan");
+  TPC_LAUNCH("nbr_bin", s, tpc::launch_nbr_bin(n, pos, g, species, c->spec.n_species, bin_of, bin_start, status, s),
+             "nbr_build: bin");
+  TPC_LAUNCH("nbr_scan", s, tpc::launch_scan_exclusive(bin_start, nbin, partials, s), "nbr_build: bin scan");
+  TPC_LAUNCH("nbr_scatter", s, tpc::launch_nbr_scatter(n, bin_of, bin_start, cursor, bin_atoms, s), "nbr_build: scatter");
+  TPC_LAUNCH("nbr_count", s, tpc::launch_nbr_count(n, pos, g, bin_of, bin_start, bin_atoms, row_ptr, status, s),
+             "nbr_build: count");
+  TPC_LAUNCH("nbr_scan", s, tpc::launch_scan_exclusive(row_ptr, n, partials, s), "nbr_build: row scan");
   // one wait: edge total and flags
   int32_t host_status[2] = {0, 0};
   TPC_HIP(hipMemcpyAsync(&host_status[0], status, sizeof(int32_t), hipMemcpyDeviceToHost, s),
@@ -426,9 +504,9 @@ tpc_status tpc_nbr_build(const tpc_ctx* c, int64_t n, const double* pos, const d
           (long long)edge_cap);
     return E.finish();
   }
-  TPC_HIP(tpc::launch_nbr_fill(n, pos, g, bin_of, bin_start, bin_atoms, row_ptr, src, shift, s),
-          "nbr_build: fill");
-  TPC_HIP(tpc::launch_nbr_reverse(n, row_ptr, src, shift, rev, status, s), "nbr_build: reverse");
+  TPC_LAUNCH("nbr_fill", s, tpc::launch_nbr_fill(n, pos, g, bin_of, bin_start, bin_atoms, row_ptr, src, shift, s),
+             "nbr_build: fill");
+  TPC_LAUNCH("nbr_reverse", s, tpc::launch_nbr_reverse(n, row_ptr, src, shift, rev, status, s), "nbr_build: reverse");
   if (c->spec.validate) {
     TPC_HIP(hipMemcpyAsync(&host_status[0], status, sizeof(int32_t), hipMemcpyDeviceToHost, s),
             "nbr_build: read status");
@@ -546,10 +624,11 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
   ga.r_cut = c->spec.r_cut;
   const int64_t ne = edge_end - edge_begin;
   if (ne > 0) {
-    TPC_HIP(tpc::launch_geom_fwd(dt, c->spec.sh_lmax, ga, eb->Y, eb->ef, eb->rv, s), "conv_fwd: geometry");
-    TPC_HIP(tpc::launch_radial_fwd(dt, c->hidden, c->n_hidden, ne, c->tab.np * c->spec.channels,
-                                   eb->ef, weights, eb->R, s),
-            "conv_fwd: radial MLP");
+    TPC_LAUNCH("geom_fwd", s, tpc::launch_geom_fwd(dt, c->spec.sh_lmax, ga, eb->Y, eb->ef, eb->rv, s), "conv_fwd: geometry");
+    TPC_LAUNCH("radial_fwd", s,
+               tpc::launch_radial_fwd(dt, c->hidden, c->n_hidden, ne, c->tab.np * c->spec.channels,
+                                      eb->ef, weights, eb->R, s),
+               "conv_fwd: radial MLP");
   }
   tpc::TPArgs ta{};
   ta.row_ptr = row_ptr;
@@ -563,8 +642,8 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
   ta.Y = eb ? eb->Y : nullptr;
   ta.R = eb ? eb->R : nullptr;
   ta.out = out;
-  TPC_HIP(tpc::launch_tp_fwd(dt, c->spec.node_lmax, c->spec.sh_lmax, c->spec.out_lmax, ta, s),
-          "conv_fwd: tensor product");
+  TPC_LAUNCH("tp_fwd", s, tpc::launch_tp_fwd(dt, c->spec.node_lmax, c->spec.sh_lmax, c->spec.out_lmax, ta, s),
+             "conv_fwd: tensor product");
   g_last_error.clear();
   return TPC_OK;
 }
@@ -649,16 +728,18 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
   ta.dY = dY;
   ta.out = dh;
   if (ne > 0) {
-    TPC_HIP(tpc::launch_tp_bwd_edge(dt, L1, L2, L3, ta, s), "conv_bwd: tensor product (edges)");
-    TPC_HIP(tpc::launch_radial_bwd(dt, c->hidden, c->n_hidden, ne, c->tab.np * c->spec.channels,
-                                   eb->ef, dRp, weights, d_ef, s),
-            "conv_bwd: radial MLP");
-    TPC_HIP(tpc::launch_geom_bwd(dt, L2, ne, edge_begin, c->spec.r_cut, eb->rv, dY, d_ef, g_edge, s),
-            "conv_bwd: geometry");
+    TPC_LAUNCH("tp_bwd_edge", s, tpc::launch_tp_bwd_edge(dt, L1, L2, L3, ta, s), "conv_bwd: tensor product (edges)");
+    TPC_LAUNCH("radial_bwd", s,
+               tpc::launch_radial_bwd(dt, c->hidden, c->n_hidden, ne, c->tab.np * c->spec.channels,
+                                      eb->ef, dRp, weights, d_ef, s),
+               "conv_bwd: radial MLP");
+    TPC_LAUNCH("geom_bwd", s,
+               tpc::launch_geom_bwd(dt, L2, ne, edge_begin, c->spec.r_cut, eb->rv, dY, d_ef, g_edge, s),
+               "conv_bwd: geometry");
   }
-  TPC_HIP(tpc::launch_tp_bwd_node(dt, L1, L2, L3, ta, s), "conv_bwd: tensor product (nodes)");
+  TPC_LAUNCH("tp_bwd_node", s, tpc::launch_tp_bwd_node(dt, L1, L2, L3, ta, s), "conv_bwd: tensor product (nodes)");
   if (forces)
-    TPC_HIP(tpc::launch_forces(dt, n, row_ptr, rev, g_edge, forces, s), "conv_bwd: forces");
+    TPC_LAUNCH("forces", s, tpc::launch_forces(dt, n, row_ptr, rev, g_edge, forces, s), "conv_bwd: forces");
   g_last_error.clear();
   return TPC_OK;
 }
