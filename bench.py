@@ -36,7 +36,7 @@ VALU_F32_PEAK = 78.6e12    # flop/s, fp32 FMA without packed math: 256 CU x 4 SI
 KERNEL_SOURCES = {
     "tp_fwd": ["tp_impl.hpp", "tp_fwd.hip", "tables.hpp"],
     "tp_bwd_edge": ["tp_impl.hpp", "tp_bwd_edge.hip", "tables.hpp"],
-    "tp_bwd_node": ["tp_impl.hpp", "tp_bwd_node.hip", "tables.hpp"],
+    "dh_gather": ["tp_impl.hpp", "tp_bwd_edge.hip"],
     "radial_fwd": ["radial.hip"],
     "radial_bwd": ["radial.hip"],
     "geom_fwd": ["geom.hip"],
@@ -67,11 +67,12 @@ def algorithmic(kernel, N, E, cfg, ctx):
         return (E * (T * PC + T * dsh) + N * T * C * (din + dout) + csr,
                 E * (2 * nnz + C * (2 * m13 + 2 * dout)))
     if kernel == "tp_bwd_edge":
-        return (E * (2 * T * PC + 2 * T * dsh) + N * T * C * (din + dout) + csr,
-                E * (4 * nnz + C * (4 * m13 + 3 * dout)))
-    if kernel == "tp_bwd_node":
-        return (E * (T * PC + T * dsh) + N * T * C * (dout + din) + csr,
-                E * (2 * nnz + C * (2 * m13 + dout)))
+        # reads R, Y, h (once per atom), G (once per atom); writes dR, dY and
+        # the per-edge dh contributions
+        return (E * (2 * T * PC + 2 * T * dsh + T * C * din) + N * T * C * (din + dout) + csr,
+                E * C * (2 * nnz + 4 * m13 + 2 * din + 2 * dout))
+    if kernel == "dh_gather":
+        return (E * T * C * din + N * T * C * din + 4 * (N + 1), E * C * din)
     hidden = 2 * (8 * H + (NH - 1) * H * H)
     if kernel == "radial_fwd":
         return E * (8 * T + T * PC), E * (hidden + 2 * H * PC)
@@ -185,6 +186,7 @@ def main(argv=None):
     dh = torch.empty_like(h)
     dR = torch.empty((E, ctx.r_width), dtype=ctx.dtype, device=dev)
     g_edge = torch.empty((E, 3), dtype=ctx.dtype, device=dev)
+    dh_edge = torch.empty((E, ctx.d_in, cfg["C"]), dtype=ctx.dtype, device=dev)
     forces = torch.empty((N, 3), dtype=ctx.dtype, device=dev)
     ws_n = ctx._workspace(ctx.workspace_bytes(tpc.OP_NBR, N, 0, cell), dev)
     ws_f = ctx._workspace(ctx.workspace_bytes(tpc.OP_FWD, N, E), dev)
@@ -193,8 +195,8 @@ def main(argv=None):
     def step():
         nl2 = ctx.nbr_build(pos, cell, species, edge_cap=E, into=nl, workspace=ws_n)
         ctx.conv_fwd(pos, cell, nl2, h, W, scale, out=out, eb=eb, workspace=ws_f)
-        ctx.conv_bwd(nl2, h, W, scale, G, eb, dh=dh, dR=dR, g_edge=g_edge, forces=forces,
-                     workspace=ws_b)
+        ctx.conv_bwd(nl2, h, W, scale, G, eb, dh=dh, dR=dR, g_edge=g_edge, dh_edge=dh_edge,
+                     forces=forces, workspace=ws_b)
 
     for _ in range(a.warmup):
         step()
@@ -219,7 +221,7 @@ def main(argv=None):
                   for n, (tot, cnt) in kt.items()}
     fwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0) for n in ("geom_fwd", "radial_fwd", "tp_fwd"))
     bwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0)
-                 for n in ("tp_bwd_edge", "radial_bwd", "geom_bwd", "tp_bwd_node", "forces"))
+                 for n in ("tp_bwd_edge", "radial_bwd", "geom_bwd", "dh_gather", "forces"))
     nbr_ms = sum(v["ms_per_step"] for n, v in per_kernel.items() if n.startswith("nbr"))
     dominant = max((n for n in per_kernel if n in KERNEL_SOURCES), key=lambda n: per_kernel[n]["ms_per_step"])
     roof = roofline_for(dominant, per_kernel[dominant]["avg_ms"] * 1e-3, N, E, cfg, ctx)

@@ -192,26 +192,33 @@ tpc_status tpc_conv_fwd(const tpc_ctx* ctx, int64_t n_atoms, const double* pos,
                         void* stream);
 
 /* Backward of L = sum(G * out) for receivers [row_begin, row_end).
- *   n_edges   total edges of the list (g_edge and rev span all of them)
- *   rev       [n_edges] int32 from tpc_nbr_build (needed when forces != NULL)
+ *   n_edges   total edges of the list (g_edge, dh_edge and rev span all of them)
+ *   rev       [n_edges] int32 from tpc_nbr_build
  *   grad_out  G [n_atoms][d_out][C], device
  *   eb        per-edge buffers of the same chunk, as written by tpc_conv_fwd
- *   dh        [n_atoms][d_in][C], device; rows [row_begin,row_end) written.
- *             Because the list is symmetric, dh of an atom is gathered over
- *             its own row (the reverse edges), so no atomics are needed.
- *   dR        [E_chunk][P*C] device, nullable (then kept in the workspace)
+ *   dR        [E_chunk][P*C] device, nullable (then kept in the workspace):
+ *             dL/dR, the inner product of G with the unweighted product
+ *             (FlashCart section 3, "Symbolic derivatives")
  *   g_edge    [n_edges][3] device, out: dL/d(edge vector), absolute edge index
- *   forces    [n_atoms][3] device, nullable: F = -dL/dx.  Computed from g_edge
- *             of every edge, so pass it only on the call that finishes the
- *             last chunk (all chunks' g_edge written earlier on this stream).
+ *   dh_edge   [n_edges][d_in][C] device, out: each edge's contribution to dL/dh
+ *             of its sender, stored at the reverse edge's slot (so the
+ *             contributions to atom j fill row j of the list)
+ *   dh        [n_atoms][d_in][C] device, nullable: dL/dh = s * row sums of
+ *             dh_edge, for every atom
+ *   forces    [n_atoms][3] device, nullable: F = -dL/dx from g_edge of every
+ *             edge
+ * dh and forces read the per-edge outputs of every edge, so pass them only on
+ * the call that finishes the last chunk (all chunks' per-edge outputs written
+ * earlier on this stream); an unchunked call passes everything at once.
+ * No atomics: every sum runs in a fixed order.
  */
 tpc_status tpc_conv_bwd(const tpc_ctx* ctx, int64_t n_atoms, int64_t n_edges,
                         const int32_t* row_ptr, const int32_t* src, const int32_t* rev,
                         int64_t row_begin, int64_t row_end, int64_t edge_begin,
                         int64_t edge_end, const void* h, const void* const* weights,
                         double scale, const void* grad_out, const tpc_edge_buffers* eb,
-                        void* dh, void* dR, void* g_edge, void* forces, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        void* dR, void* g_edge, void* dh_edge, void* dh, void* forces,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-kernel timing with HIP events, for benchmarks and profiling.  While
  * enabled on a thread, every kernel the library launches from that thread is

@@ -89,7 +89,7 @@ def library():
                                  _VP, ctypes.POINTER(_EdgeBuffers), _VP, ctypes.c_size_t, _VP]
     lib.tpc_conv_bwd.argtypes = [_VP, _I64, _I64, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _VP,
                                  ctypes.POINTER(_VP), ctypes.c_double, _VP,
-                                 ctypes.POINTER(_EdgeBuffers), _VP, _VP, _VP, _VP, _VP,
+                                 ctypes.POINTER(_EdgeBuffers), _VP, _VP, _VP, _VP, _VP, _VP,
                                  ctypes.c_size_t, _VP]
     lib.tpc_timing_enable.argtypes = [ctypes.c_int]
     lib.tpc_timing_collect.argtypes = [ctypes.POINTER(_KernelTime), ctypes.c_int,
@@ -307,17 +307,29 @@ class Context:
 
     # ---- backward -------------------------------------------------------------
     def conv_bwd(self, nl: NeighbourList, h, W, scale, G, eb: EdgeBuffers, dh=None, dR=None,
-                 g_edge=None, want_dR=True, want_forces=True, forces=None, workspace=None):
-        """Returns (dh, dR or None, forces or None, g_edge)."""
+                 g_edge=None, dh_edge=None, want_dR=True, want_dh=True, want_forces=True,
+                 forces=None, workspace=None):
+        """Backward of L = sum(G * out) for the chunk in ``eb``.
+
+        Returns (dh, dR, forces, g_edge).  dh and forces are sums over every
+        edge, so a chunked caller asks for them (want_dh / want_forces) only on
+        the last chunk, after every chunk's per-edge outputs (g_edge and
+        dh_edge, shared full-size buffers) are written.
+        """
         t = _torch()
         N = h.shape[0]
         ne = eb.edge_end - eb.edge_begin
-        if dh is None:
+        if want_dh and dh is None:
             dh = t.empty_like(h)
+        if not want_dh:
+            dh = None
         if want_dR and dR is None:
             dR = t.empty((ne, self.r_width), dtype=self.dtype, device=h.device)
         if g_edge is None:
             g_edge = t.empty((nl.n_edges, 3), dtype=self.dtype, device=h.device)
+        if dh_edge is None:
+            dh_edge = t.empty((nl.n_edges, self.d_in, self.spec.channels), dtype=self.dtype,
+                              device=h.device)
         if want_forces and forces is None:
             forces = t.empty((N, 3), dtype=self.dtype, device=h.device)
         if not want_forces:
@@ -329,8 +341,8 @@ class Context:
         _check(library().tpc_conv_bwd(self._h, N, nl.n_edges, _ptr(nl.row_ptr), _ptr(nl.src),
                                       _ptr(nl.rev), eb.row_begin, eb.row_end, eb.edge_begin,
                                       eb.edge_end, _ptr(h), wp, float(scale), _ptr(G), ctypes.byref(ebc),
-                                      _ptr(dh), _ptr(dR), _ptr(g_edge), _ptr(forces), _ptr(ws),
-                                      ws.numel(), _stream()))
+                                      _ptr(dR), _ptr(g_edge), _ptr(dh_edge), _ptr(dh), _ptr(forces),
+                                      _ptr(ws), ws.numel(), _stream()))
         return dh, dR, forces, g_edge
 
 

@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtpconv.so")
 
 SOURCES = ["api.cpp", "nbr.hip", "scan.hip", "geom.hip", "radial.hip", "tp_fwd.hip",
-           "tp_bwd_edge.hip", "tp_bwd_node.hip", "forces.hip"]
+           "tp_bwd_edge.hip", "forces.hip"]
 HEADERS = ["common.hpp", "kernels.hpp", "nbr.hpp", "tables.hpp", "tp_impl.hpp"]
 
 ARCH = "gfx950"

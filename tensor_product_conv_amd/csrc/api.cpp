@@ -201,12 +201,14 @@ struct BwdWs {
   size_t dR, dY, d_ef, status, total, total_without_dR;
 };
 
+int waves_per_row(int C) { return C <= 64 ? 1 : C / 64; }
+
 BwdWs bwd_layout(const tpc_ctx* c, int64_t ne) {
   BwdWs w{};
   const size_t T = c->tsize;
   size_t off = 0;
-  w.dY = off;
-  off += align_up(T * (size_t)ne * c->tab.dsh);
+  w.dY = off;  // one partial dY slice per 64-channel wave of a row
+  off += align_up(T * (size_t)ne * c->tab.dsh * waves_per_row(c->spec.channels));
   w.d_ef = off;
   off += align_up(T * (size_t)ne * 8);
   w.status = off;
@@ -329,8 +331,8 @@ tpc_status tpc_ctx_create(const tpc_spec* spec, tpc_ctx** out) {
       !tpc::tp_supported(s.dtype, s.node_lmax, s.sh_lmax, s.out_lmax, s.channels))
     E.add(TPC_ERR_UNSUPPORTED,
           "no fused kernel for dtype=%d node_lmax=%d sh_lmax=%d out_lmax=%d channels=%d "
-          "(built: float32 (1,2,1),(1,3,3),(2,3,3) with C<=64 or C=128, (3,3,3) with C<=64; "
-          "float64 (1,2,1),(1,3,3),(2,3,3),(3,3,3) with C<=64)",
+          "(built: (node_lmax, sh_lmax, out_lmax) in (1,2,1),(1,3,3),(2,3,3),(3,3,3), float32 "
+          "or float64, channels 1..64 or 128)",
           s.dtype, s.node_lmax, s.sh_lmax, s.out_lmax, s.channels);
   tpc_status st = E.finish();
   if (st != TPC_OK) return st;
@@ -624,7 +626,8 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
   ga.r_cut = c->spec.r_cut;
   const int64_t ne = edge_end - edge_begin;
   if (ne > 0) {
-    TPC_LAUNCH("geom_fwd", s, tpc::launch_geom_fwd(dt, c->spec.sh_lmax, ga, eb->Y, eb->ef, eb->rv, s), "conv_fwd: geometry");
+    TPC_LAUNCH("geom_fwd", s, tpc::launch_geom_fwd(dt, c->spec.sh_lmax, ga, eb->Y, eb->ef, eb->rv, s),
+               "conv_fwd: geometry");
     TPC_LAUNCH("radial_fwd", s,
                tpc::launch_radial_fwd(dt, c->hidden, c->n_hidden, ne, c->tab.np * c->spec.channels,
                                       eb->ef, weights, eb->R, s),
@@ -641,6 +644,7 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
   ta.h = h;
   ta.Y = eb ? eb->Y : nullptr;
   ta.R = eb ? eb->R : nullptr;
+  ta.n_chunk_edges = edge_end - edge_begin;
   ta.out = out;
   TPC_LAUNCH("tp_fwd", s, tpc::launch_tp_fwd(dt, c->spec.node_lmax, c->spec.sh_lmax, c->spec.out_lmax, ta, s),
              "conv_fwd: tensor product");
@@ -652,8 +656,8 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
                         const int32_t* src, const int32_t* rev, int64_t row_begin, int64_t row_end,
                         int64_t edge_begin, int64_t edge_end, const void* h,
                         const void* const* weights, double scale, const void* grad_out,
-                        const tpc_edge_buffers* eb, void* dh, void* dR, void* g_edge, void* forces,
-                        void* ws, size_t ws_bytes, void* stream) {
+                        const tpc_edge_buffers* eb, void* dR, void* g_edge, void* dh_edge, void* dh,
+                        void* forces, void* ws, size_t ws_bytes, void* stream) {
   Errors E;
   if (!c) {
     E.add(TPC_ERR_INVALID, "ctx must be non-null");
@@ -667,10 +671,16 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
   if (row_end > row_begin) {
     need_ptr(h, "h", va, E);
     need_ptr(grad_out, "grad_out", va, E);
-    need_ptr(dh, "dh", va, E);
   }
-  if (edge_end > edge_begin) need_ptr(src, "src", 4, E);
-  if (n_edges > 0) need_ptr(g_edge, "g_edge", 8, E);
+  if (edge_end > edge_begin) {
+    need_ptr(src, "src", 4, E);
+    need_ptr(rev, "rev", 4, E);
+  }
+  if (n_edges > 0) {
+    need_ptr(g_edge, "g_edge", 8, E);
+    need_ptr(dh_edge, "dh_edge", va, E);
+  }
+  if (dh) need_ptr(dh, "dh", va, E);
   if (forces) {
     need_ptr(forces, "forces", 8, E);
     if (n_edges > 0) need_ptr(rev, "rev", 4, E);
@@ -715,6 +725,7 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
   tpc::TPArgs ta{};
   ta.row_ptr = row_ptr;
   ta.src = src;
+  ta.rev = rev;
   ta.row_begin = row_begin;
   ta.row_end = row_end;
   ta.edge_begin = edge_begin;
@@ -723,10 +734,11 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
   ta.h = h;
   ta.Y = eb->Y;
   ta.R = eb->R;
+  ta.n_chunk_edges = ne;
   ta.G = grad_out;
   ta.dR = dRp;
   ta.dY = dY;
-  ta.out = dh;
+  ta.dh_edge = dh_edge;
   if (ne > 0) {
     TPC_LAUNCH("tp_bwd_edge", s, tpc::launch_tp_bwd_edge(dt, L1, L2, L3, ta, s), "conv_bwd: tensor product (edges)");
     TPC_LAUNCH("radial_bwd", s,
@@ -734,10 +746,14 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
                                       eb->ef, dRp, weights, d_ef, s),
                "conv_bwd: radial MLP");
     TPC_LAUNCH("geom_bwd", s,
-               tpc::launch_geom_bwd(dt, L2, ne, edge_begin, c->spec.r_cut, eb->rv, dY, d_ef, g_edge, s),
+               tpc::launch_geom_bwd(dt, L2, ne, edge_begin, c->spec.r_cut, eb->rv, dY,
+                                    waves_per_row(c->spec.channels), d_ef, g_edge, s),
                "conv_bwd: geometry");
   }
-  TPC_LAUNCH("tp_bwd_node", s, tpc::launch_tp_bwd_node(dt, L1, L2, L3, ta, s), "conv_bwd: tensor product (nodes)");
+  if (dh)
+    TPC_LAUNCH("dh_gather", s,
+               tpc::launch_dh_gather(dt, n, c->tab.din * c->spec.channels, row_ptr, scale, dh_edge, dh, s),
+               "conv_bwd: dh row sums");
   if (forces)
     TPC_LAUNCH("forces", s, tpc::launch_forces(dt, n, row_ptr, rev, g_edge, forces, s), "conv_bwd: forces");
   g_last_error.clear();

@@ -169,7 +169,7 @@ k_geom_fwd(GeomArgs a, T* __restrict__ Y, T* __restrict__ ef, T* __restrict__ rv
 template <typename T, int L2>
 __global__ void __launch_bounds__(256)
 k_geom_bwd(int64_t ne, int64_t edge_begin, double r_cut, const T* __restrict__ rv,
-           const T* __restrict__ dY, const T* __restrict__ d_ef, T* __restrict__ g) {
+           const T* __restrict__ dY, int n_parts, const T* __restrict__ d_ef, T* __restrict__ g) {
   const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (t >= ne) return;
   constexpr int DSH = (L2 + 1) * (L2 + 1);
@@ -179,6 +179,9 @@ k_geom_bwd(int64_t ne, int64_t edge_begin, double r_cut, const T* __restrict__ r
   T w[DSH];
 #pragma unroll
   for (int k = 0; k < DSH; ++k) w[k] = dY[t * DSH + k];
+  for (int part = 1; part < n_parts; ++part)
+#pragma unroll
+    for (int k = 0; k < DSH; ++k) w[k] += dY[(part * ne + t) * DSH + k];
   T q[3];
   harmonics_grad_dot<T, L2>(ux, uy, uz, w, q);
   const T uq = ux * q[0] + uy * q[1] + uz * q[2];
@@ -222,16 +225,6 @@ hipError_t geom_fwd_impl(const GeomArgs& a, void* Y, void* ef, void* rv, hipStre
   return hipGetLastError();
 }
 
-template <typename T, int L2>
-hipError_t geom_bwd_impl(int64_t ne, int64_t edge_begin, double r_cut, const void* rv,
-                         const void* dY, const void* d_ef, void* g, hipStream_t s) {
-  if (ne <= 0) return hipSuccess;
-  k_geom_bwd<T, L2><<<(unsigned)((ne + 255) / 256), 256, 0, s>>>(
-      ne, edge_begin, r_cut, static_cast<const T*>(rv), static_cast<const T*>(dY),
-      static_cast<const T*>(d_ef), static_cast<T*>(g));
-  return hipGetLastError();
-}
-
 template <typename T>
 hipError_t geom_fwd_t(int L2, const GeomArgs& a, void* Y, void* ef, void* rv, hipStream_t s) {
   switch (L2) {
@@ -243,14 +236,24 @@ hipError_t geom_fwd_t(int L2, const GeomArgs& a, void* Y, void* ef, void* rv, hi
   return hipErrorInvalidValue;
 }
 
+template <typename T, int L2>
+hipError_t geom_bwd_impl(int64_t ne, int64_t edge_begin, double r_cut, const void* rv,
+                         const void* dY, int n_parts, const void* d_ef, void* g, hipStream_t s) {
+  if (ne <= 0) return hipSuccess;
+  k_geom_bwd<T, L2><<<(unsigned)((ne + 255) / 256), 256, 0, s>>>(
+      ne, edge_begin, r_cut, static_cast<const T*>(rv), static_cast<const T*>(dY), n_parts,
+      static_cast<const T*>(d_ef), static_cast<T*>(g));
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t geom_bwd_t(int L2, int64_t ne, int64_t eb, double rc, const void* rv, const void* dY,
-                      const void* d_ef, void* g, hipStream_t s) {
+                      int n_parts, const void* d_ef, void* g, hipStream_t s) {
   switch (L2) {
-    case 0: return geom_bwd_impl<T, 0>(ne, eb, rc, rv, dY, d_ef, g, s);
-    case 1: return geom_bwd_impl<T, 1>(ne, eb, rc, rv, dY, d_ef, g, s);
-    case 2: return geom_bwd_impl<T, 2>(ne, eb, rc, rv, dY, d_ef, g, s);
-    case 3: return geom_bwd_impl<T, 3>(ne, eb, rc, rv, dY, d_ef, g, s);
+    case 0: return geom_bwd_impl<T, 0>(ne, eb, rc, rv, dY, n_parts, d_ef, g, s);
+    case 1: return geom_bwd_impl<T, 1>(ne, eb, rc, rv, dY, n_parts, d_ef, g, s);
+    case 2: return geom_bwd_impl<T, 2>(ne, eb, rc, rv, dY, n_parts, d_ef, g, s);
+    case 3: return geom_bwd_impl<T, 3>(ne, eb, rc, rv, dY, n_parts, d_ef, g, s);
   }
   return hipErrorInvalidValue;
 }
@@ -263,10 +266,10 @@ hipError_t launch_geom_fwd(int dtype, int L2, const GeomArgs& a, void* Y, void* 
 }
 
 hipError_t launch_geom_bwd(int dtype, int L2, int64_t ne, int64_t edge_begin, double r_cut,
-                           const void* rv, const void* dY, const void* d_ef, void* g,
+                           const void* rv, const void* dY, int n_parts, const void* d_ef, void* g,
                            hipStream_t s) {
-  return dtype == 1 ? geom_bwd_t<double>(L2, ne, edge_begin, r_cut, rv, dY, d_ef, g, s)
-                    : geom_bwd_t<float>(L2, ne, edge_begin, r_cut, rv, dY, d_ef, g, s);
+  return dtype == 1 ? geom_bwd_t<double>(L2, ne, edge_begin, r_cut, rv, dY, n_parts, d_ef, g, s)
+                    : geom_bwd_t<float>(L2, ne, edge_begin, r_cut, rv, dY, n_parts, d_ef, g, s);
 }
 
 }  // namespace tpc

@@ -122,11 +122,22 @@ struct Table {
   int np;
   int din, dsh, dout;
   int nnz;
+  int nm;    // non-zero (p, m1, m3) entries of the per-edge coupling matrices
+  int nms;   // row stride of the per-edge coupling-matrix buffer (nm rounded up to 4)
   Path path[kMaxPaths];
   double cg[kMaxPaths][7][7][7];
+  // index of entry (p, m1, m3) in an edge's coupling-matrix row, -1 if zero;
+  // entries are ordered path-major, then m3, then m1
+  int midx[kMaxPaths][7][7];
 
   constexpr int out_row(int p, int m3) const {
     return path[p].out_base + m3 * path[p].nq + path[p].q;
+  }
+  // does any C^p[m1][m2][m3] differ from zero for this (m1, m2)
+  constexpr bool m12nz(int p, int m1, int m2) const {
+    for (int c = 0; c < 7; ++c)
+      if (cg[p][m1][m2][c] != 0.0) return true;
+    return false;
   }
 };
 
@@ -191,11 +202,63 @@ constexpr Table make_table(int L1, int L2, int L3) {
         }
   }
   t.nnz = nnz;
+  int nm = 0;
+  for (int p = 0; p < np; ++p)
+    for (int c = 0; c < 7; ++c)
+      for (int a = 0; a < 7; ++a) t.midx[p][a][c] = -1;
+  for (int p = 0; p < np; ++p)
+    for (int c = 0; c <= 2 * t.path[p].l3; ++c)
+      for (int a = 0; a <= 2 * t.path[p].l1; ++a) {
+        bool any = false;
+        for (int b = 0; b <= 2 * t.path[p].l2; ++b)
+          if (t.cg[p][a][b][c] != 0.0) any = true;
+        if (any) t.midx[p][a][c] = nm++;
+      }
+  t.nm = nm;
+  t.nms = (nm + 3) / 4 * 4;
   return t;
 }
 
 template <int L1, int L2, int L3>
 inline constexpr Table kTable = make_table(L1, L2, L3);
+
+// Balanced split of the paths over NG waves of one receiver row: greedy by
+// descending per-wave work (coupling-matrix terms plus per-channel FMAs).
+struct Groups {
+  int group[kMaxPaths];
+};
+
+constexpr Groups make_groups(const Table& t, int ng, int cpl) {
+  Groups g{};
+  int cost[kMaxPaths] = {};
+  bool done[kMaxPaths] = {};
+  int load[8] = {};
+  for (int p = 0; p < t.np; ++p) {
+    int m13 = 0, nnz = 0;
+    for (int a = 0; a < 7; ++a)
+      for (int c = 0; c < 7; ++c) {
+        if (t.midx[p][a][c] >= 0) ++m13;
+        for (int b = 0; b < 7; ++b)
+          if (t.cg[p][a][b][c] != 0.0) ++nnz;
+      }
+    cost[p] = cpl * (m13 + 2 * t.path[p].l1 + 1) + nnz;
+  }
+  for (int it = 0; it < t.np; ++it) {
+    int best = -1;
+    for (int p = 0; p < t.np; ++p)
+      if (!done[p] && (best < 0 || cost[p] > cost[best])) best = p;
+    int gl = 0;
+    for (int k = 1; k < ng; ++k)
+      if (load[k] < load[gl]) gl = k;
+    g.group[best] = gl;
+    load[gl] += cost[best];
+    done[best] = true;
+  }
+  return g;
+}
+
+template <int L1, int L2, int L3, int NG, int CPL>
+inline constexpr Groups kGroups = make_groups(kTable<L1, L2, L3>, NG, CPL);
 
 // Non-zero test for the pattern (m1, m3) of path p: is any C[m1][m2][m3] != 0.
 constexpr bool m13_nonzero(const Table& t, int p, int a, int c) {

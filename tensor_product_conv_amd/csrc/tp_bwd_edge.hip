@@ -1,4 +1,5 @@
-// Instantiations of the receiver-side backward kernel (dR and dY).
+// Instantiations of the receiver-side backward kernel (dR, partial dY and
+// the per-edge dh contributions).
 #include "tp_impl.hpp"
 
 namespace tpc {
@@ -6,18 +7,37 @@ namespace tpc {
 hipError_t launch_tp_bwd_edge(int dtype, int L1, int L2, int L3, const TPArgs& a, hipStream_t s) {
   const int64_t rows = a.row_end - a.row_begin;
   if (rows <= 0) return hipSuccess;
-  const int cpl = tp_cpl(a.C);
-#define TPC_X(T, A, B, D, K)                                                                   \
-  if (dtype == tp_detail::dtype_id<T>() && L1 == A && L2 == B && L3 == D && cpl == K) {        \
-    k_tp_bwd_edge<T, A, B, D, K><<<tp_blocks(rows), kTPWave * kTPWavesPerBlock, 0, s>>>(       \
-        a.row_ptr, a.src, a.row_begin, a.row_end, a.edge_begin, a.C, (T)a.scale,               \
-        static_cast<const T*>(a.h), static_cast<const T*>(a.Y), static_cast<const T*>(a.R),  \
-        static_cast<const T*>(a.G), static_cast<T*>(a.dR), static_cast<T*>(a.dY));           \
-    return hipGetLastError();                                                                 \
+  const int nw = tp_nw(a.C);
+#define TPC_LAUNCH_BE(T, A, B, D, F)                                                             \
+  k_tp_bwd_edge<T, A, B, D, F><<<tp_blocks(rows, a.C), kTPWave * kTPWavesPerBlock, 0, s>>>(       \
+      a.row_ptr, a.src, a.rev, a.row_begin, a.row_end, a.edge_begin, a.n_chunk_edges, a.C,      \
+      (T)a.scale, static_cast<const T*>(a.h), static_cast<const T*>(a.Y),                     \
+      static_cast<const T*>(a.R), static_cast<const T*>(a.G), static_cast<T*>(a.dR),           \
+      static_cast<T*>(a.dY), static_cast<T*>(a.dh_edge));
+#define TPC_X(T, A, B, D)                                                                  \
+  if (dtype == tp_detail::dtype_id<T>() && L1 == A && L2 == B && L3 == D) {                \
+    switch (nw) { case 0: TPC_LAUNCH_BE(T, A, B, D, 0) break; case 1: TPC_LAUNCH_BE(T, A, B, D, 1) break; \
+                  case 2: TPC_LAUNCH_BE(T, A, B, D, 2) break; default: return hipErrorInvalidValue; } \
+    return hipGetLastError();                                                              \
   }
   TPC_TP_CONFIGS(TPC_X)
 #undef TPC_X
+#undef TPC_LAUNCH_BE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_dh_gather(int dtype, int64_t n, int din_c, const int32_t* row_ptr, double scale,
+                            const void* dh_edge, void* dh, hipStream_t s) {
+  const int64_t total = n * din_c;
+  if (total <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (dtype == 1)
+    k_dh_gather<double><<<blocks, 256, 0, s>>>(n, din_c, row_ptr, scale,
+                                               static_cast<const double*>(dh_edge), static_cast<double*>(dh));
+  else
+    k_dh_gather<float><<<blocks, 256, 0, s>>>(n, din_c, row_ptr, (float)scale,
+                                              static_cast<const float*>(dh_edge), static_cast<float*>(dh));
+  return hipGetLastError();
 }
 
 }  // namespace tpc

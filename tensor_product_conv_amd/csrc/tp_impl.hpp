@@ -2,30 +2,38 @@
 //
 // Forward (FlashCart paper, section 2 "Equivariant convolution and many-body
 // correlations"; section 4 receiver-sorted kernel):
-//   out[i,(p,m3),u] = s * sum_{e in row i} R[e,p,u] * sum_{m1} M^p_e[m1,m3] h[src_e,(l1,m1),u]
-//   M^p_e[m1,m3]   = sum_{m2} C^p[m1,m2,m3] Y[e,(l2,m2)]
-// One wave owns one receiver row; lanes own channels (CPL consecutive channels
-// per lane).  The edge loop runs in CSR order, so every output is a sum in a
-// fixed order, accumulated in registers and stored once: no atomics and no
+//   out[i,(p,m3),u] = s * sum_{e in row i} R[e,p,u] * sum_{m1} M_e^p[m1,m3] h[src_e,(l1,m1),u]
+//   M_e^p[m1,m3]   = sum_{m2} C^p[m1,m2,m3] Y[e,(l2,m2)]
+// The per-edge coupling matrices M_e are built once per edge by the geometry
+// kernel and read here through scalar loads: they are the same for every
+// channel.  A wave owns one receiver row and 64 channels (one per lane); C > 64
+// uses C/64 waves per row.  The edge loop runs in CSR order, so every output
+// is a fixed-order sum held in registers and stored once: no atomics and no
 // per-edge message tensor (the receiver-streaming design of FastMACE's
-// "streaming_conv" and FlashCart's receiver-sorted kernel, on a 64-wide wave).
-// M^p_e is wave-uniform; its sparsity and the coupling coefficients are
-// compile-time constants, so the unrolled code only touches non-zeros.
+// "streaming_conv" and FlashCart's receiver-sorted kernel, on a 64-wide
+// wave).  The next edge's radial weights and sender features are loaded while
+// the current edge is computed (two register buffers).
 //
 // Backward of L = sum(G * out) (FlashCart section 3 "Symbolic derivatives":
 // the weight gradient is the inner product of the incoming gradient with the
-// unweighted product; input gradients are the other factors times the weight):
-//   edge kernel (wave per receiver i, G[i] loaded once):
-//     dR[e,p,u]   = s * sum_m3 G[i,(p,m3),u] * sum_m1 M^p_e[m1,m3] h[j,m1,u]
-//     dY[e,l2m2]  = s * sum_p sum_{m1,m3} C^p[m1,m2,m3] sum_u h[j,m1,u] R[e,p,u] G[i,(p,m3),u]
-//   node kernel (wave per atom j, over j's own row):
-//     dh[j,m1,u]  = s * sum_{e' in row j} sum_p (-1)^{l2} R[e',p,u]
-//                       sum_{m3} M^p_{e'}[m1,m3] G[src_e',(p,m3),u]
-// The node kernel uses the symmetry of the list: an edge e = (k <- j, S) has
-// the reverse e' = (j <- k, -S) in row j with the same length (so the same R)
-// and the opposite direction (so Y(e) = (-1)^l2 Y(e')).  Sender gradients are
-// therefore gathered per row instead of scattered with atomics (FlashCart's
-// VJP uses atomics there) or through a sender permutation.
+// unweighted product; the input gradients are the other factors times the
+// weight).  With the per-channel projection
+//     Q_e^p[m2,u] = sum_{m1,m3} C^p[m1,m2,m3] h[src_e,m1,u] G[i,(p,m3),u]
+// both edge gradients follow from one contraction:
+//     dR[e,p,u]  = s * sum_{m2} Y[e,(l2,m2)] Q_e^p[m2,u]
+//     dY[e,l2m2] = s * sum_p sum_u R[e,p,u] Q_e^p[m2,u]      (channel reduction)
+// computed by the edge kernel (one wave per receiver row and 64 channels, G[i]
+// loaded once per row).  The channel reduction of dY is a wave reduce-scatter;
+// with several waves per row each writes its partial sum and the geometry
+// backward adds them in a fixed order.
+// Node kernel (one wave per atom j and 64 channels, over j's own row):
+//     dh[j,m1,u] = s * sum_{e' in row j} sum_p (-1)^{l2} R[e',p,u]
+//                      sum_{m3} M_{e'}^p[m1,m3] G[src_e',(p,m3),u]
+// It uses the symmetry of the list: the edge e = (k <- j, S) has its reverse
+// e' = (j <- k, -S) in row j, with the same length (same R) and the opposite
+// direction (Y(e) = (-1)^l2 Y(e')).  Sender gradients are therefore gathered
+// per row instead of scattered with atomics (FlashCart's VJP uses atomics
+// there) or through a sender permutation.
 #pragma once
 
 #include "common.hpp"
@@ -37,284 +45,443 @@ namespace tpc {
 constexpr int kTPWave = 64;
 constexpr int kTPWavesPerBlock = 4;
 
-template <typename T, int N>
-struct VecN {
-  typedef T type __attribute__((ext_vector_type(N)));
+// NW = waves per row: C = 64 * NW channels, one per lane; NW = 0 stands for
+// C < 64 (lanes beyond C masked).  Loads take a wave-uniform base pointer and
+// a 32-bit lane offset so they use the scalar-base addressing form.
+template <int NW, typename T>
+__device__ __forceinline__ T ldc(const T* __restrict__ base, uint32_t off, bool on) {
+  if constexpr (NW > 0) {
+    return base[off];
+  } else {
+    return on ? base[off] : T(0);
+  }
+}
+
+template <int NW, typename T>
+__device__ __forceinline__ void stc(T* __restrict__ base, uint32_t off, bool on, T v) {
+  if constexpr (NW > 0) {
+    base[off] = v;
+  } else {
+    if (on) base[off] = v;
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ int channels(int C) {
+  if constexpr (NW > 0) {
+    return 64 * NW;
+  } else {
+    return C;
+  }
+}
+
+// Coupling-matrix row of one edge from its harmonics (compile-time sparsity).
+template <typename T, int L1, int L2, int L3>
+__device__ __forceinline__ void coupling_row(const T* y, T* out) {
+  static_for<kTable<L1, L2, L3>.np>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    constexpr Path P = kTable<L1, L2, L3>.path[p];
+    static_for<2 * P.l3 + 1>([&](auto m3c) {
+      constexpr int m3 = decltype(m3c)::value;
+      static_for<2 * P.l1 + 1>([&](auto m1c) {
+        constexpr int m1 = decltype(m1c)::value;
+        constexpr int k = kTable<L1, L2, L3>.midx[p][m1][m3];
+        if constexpr (k >= 0) {
+          T M = T(0);
+          static_for<2 * P.l2 + 1>([&](auto m2c) {
+            constexpr int m2 = decltype(m2c)::value;
+            constexpr double cv = kTable<L1, L2, L3>.cg[p][m1][m2][m3];
+            if constexpr (cv != 0.0) M += T(cv) * y[P.l2 * P.l2 + m2];
+          });
+          out[k] = M;
+        }
+      });
+    });
+  });
+}
+
+struct RowWave {
+  int row;   // receiver (or atom) index
+  int c0;    // this lane's channel
+  bool on;   // c0 < C
+  bool ok;   // the wave has a row to process
 };
 
+template <int NW>
+__device__ __forceinline__ RowWave row_wave(int64_t row_begin, int64_t row_end, int C) {
+  const int lane = threadIdx.x % kTPWave;
+  const int wpr = NW > 0 ? NW : 1;  // waves per row
+  const int64_t w = blockIdx.x * (int64_t)kTPWavesPerBlock + threadIdx.x / kTPWave;
+  RowWave r;
+  const int64_t row = row_begin + w / wpr;
+  r.ok = row < row_end;
+  r.row = uniform((int)(r.ok ? row : row_begin));
+  r.c0 = (int)(w % wpr) * kTPWave + lane;
+  r.on = r.c0 < C;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Forward.  NG waves share a receiver row, each owning a compile-time subset of
+// the paths (kGroups): the per-edge coupling matrices of a path are computed
+// by exactly one wave, from the edge's harmonics held in scalar registers.
+// Lanes own CPL consecutive channels (CPL = 2 for C = 128); MASKED kernels
+// serve C < 64 with one channel per lane.
 template <typename T, int CPL>
-__device__ __forceinline__ void load_ch(const T* __restrict__ p, bool on, T (&v)[CPL]) {
+__device__ __forceinline__ void ld_vec(const T* __restrict__ base, uint32_t off, bool on, T (&v)[CPL],
+                                       bool masked) {
   if constexpr (CPL == 1) {
-    v[0] = on ? p[0] : T(0);
+    v[0] = (!masked || on) ? base[off] : T(0);
   } else {
-    using V = typename VecN<T, CPL>::type;
-    V x = on ? *reinterpret_cast<const V*>(p) : V{};
+    using V = T __attribute__((ext_vector_type(CPL)));
+    const V x = *reinterpret_cast<const V*>(base + off);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) v[c] = x[c];
   }
 }
 
 template <typename T, int CPL>
-__device__ __forceinline__ void store_ch(T* __restrict__ p, bool on, const T (&v)[CPL]) {
-  if (!on) return;
+__device__ __forceinline__ void st_vec(T* __restrict__ base, uint32_t off, bool on, const T (&v)[CPL],
+                                       bool masked) {
   if constexpr (CPL == 1) {
-    p[0] = v[0];
+    if (!masked || on) base[off] = v[0];
   } else {
-    using V = typename VecN<T, CPL>::type;
+    using V = T __attribute__((ext_vector_type(CPL)));
     V x;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) x[c] = v[c];
-    *reinterpret_cast<V*>(p) = x;
+    *reinterpret_cast<V*>(base + off) = x;
   }
 }
 
-// M^p[m1][m3] for an edge from its uniform harmonics (compile-time sparsity).
-template <typename T, int L1, int L2, int L3, int p, int m1, int m3>
-__device__ __forceinline__ T coupling_matrix_entry(const T* y) {
-  constexpr Path P = kTable<L1, L2, L3>.path[p];
-  T M = T(0);
-  static_for<2 * P.l2 + 1>([&](auto m2c) {
-    constexpr int m2 = decltype(m2c)::value;
-    constexpr double cv = kTable<L1, L2, L3>.cg[p][m1][m2][m3];
-    if constexpr (cv != 0.0) M += T(cv) * y[P.l2 * P.l2 + m2];
+template <typename T, int L1, int L2, int L3, int CPL, int NG, bool MASKED, int G>
+__device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, int e_lo, int e_hi,
+                                             int64_t edge_begin, int C, uint32_t c0, bool on,
+                                             const T* __restrict__ h, const T* __restrict__ Y,
+                                             const T* __restrict__ R, T* __restrict__ oi, T scale) {
+  constexpr int NP = kTable<L1, L2, L3>.np, DIN = kTable<L1, L2, L3>.din;
+  constexpr int DSH = kTable<L1, L2, L3>.dsh, DOUT = kTable<L1, L2, L3>.dout;
+  const int PC = NP * C;
+  T acc[DOUT][CPL];
+  static_for<NP>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) {
+      constexpr Path P = kTable<L1, L2, L3>.path[p];
+      static_for<2 * P.l3 + 1>([&](auto m3c) {
+        constexpr int row = kTable<L1, L2, L3>.out_row(p, decltype(m3c)::value);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[row][c] = T(0);
+      });
+    }
   });
-  return M;
+  struct Buf {
+    T h[DIN][CPL];
+    T r[NP][CPL];
+  };
+  auto load = [&](int e, Buf& b) {
+    const int j = uniform(src[e]);
+    const T* __restrict__ hj = h + (int64_t)j * DIN * C;
+    const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
+#pragma unroll
+    for (int m = 0; m < DIN; ++m) ld_vec<T, CPL>(hj, m * C + c0, on, b.h[m], MASKED);
+    static_for<NP>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) ld_vec<T, CPL>(re, p * C + c0, on, b.r[p], MASKED);
+    });
+  };
+  auto compute = [&](int e, const Buf& b) {
+    const T* __restrict__ ye = Y + ((int64_t)e - edge_begin) * DSH;
+    static_for<NP>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) {
+        constexpr Path P = kTable<L1, L2, L3>.path[p];
+        T hr[2 * P.l1 + 1][CPL];
+#pragma unroll
+        for (int m1 = 0; m1 < 2 * P.l1 + 1; ++m1)
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) hr[m1][c] = b.r[p][c] * b.h[P.l1 * P.l1 + m1][c];
+        static_for<2 * P.l3 + 1>([&](auto m3c) {
+          constexpr int m3 = decltype(m3c)::value;
+          constexpr int row = kTable<L1, L2, L3>.out_row(p, m3);
+          static_for<2 * P.l1 + 1>([&](auto m1c) {
+            constexpr int m1 = decltype(m1c)::value;
+            if constexpr (kTable<L1, L2, L3>.midx[p][m1][m3] >= 0) {
+              T M = T(0);
+              static_for<2 * P.l2 + 1>([&](auto m2c) {
+                constexpr int m2 = decltype(m2c)::value;
+                constexpr double cv = kTable<L1, L2, L3>.cg[p][m1][m2][m3];
+                if constexpr (cv != 0.0) M += T(cv) * ye[P.l2 * P.l2 + m2];
+              });
+#pragma unroll
+              for (int c = 0; c < CPL; ++c) acc[row][c] += M * hr[m1][c];
+            }
+          });
+        });
+      }
+    });
+  };
+  Buf A, B;
+  int e = e_lo;
+  if (e < e_hi) load(e, A);
+  while (e < e_hi) {
+    if (e + 1 < e_hi) load(e + 1, B);
+    compute(e, A);
+    if (++e >= e_hi) break;
+    if (e + 1 < e_hi) load(e + 1, A);
+    compute(e, B);
+    ++e;
+  }
+  static_for<NP>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) {
+      constexpr Path P = kTable<L1, L2, L3>.path[p];
+      static_for<2 * P.l3 + 1>([&](auto m3c) {
+        constexpr int row = kTable<L1, L2, L3>.out_row(p, decltype(m3c)::value);
+        T v[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[c] = scale * acc[row][c];
+        st_vec<T, CPL>(oi, row * C + c0, on, v, MASKED);
+      });
+    }
+  });
 }
 
-// ---------------------------------------------------------------------------
-template <typename T, int L1, int L2, int L3, int CPL>
+template <typename T, int L1, int L2, int L3, int CPL, int NG, bool MASKED>
 __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
 k_tp_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, int64_t row_begin,
          int64_t row_end, int64_t edge_begin, int C, T scale, const T* __restrict__ h,
          const T* __restrict__ Y, const T* __restrict__ R, T* __restrict__ out) {
-  constexpr int NP = kTable<L1, L2, L3>.np, DIN = kTable<L1, L2, L3>.din, DSH = kTable<L1, L2, L3>.dsh, DOUT = kTable<L1, L2, L3>.dout;
+  constexpr int DOUT = kTable<L1, L2, L3>.dout;
   const int lane = threadIdx.x % kTPWave;
   const int64_t w = blockIdx.x * (int64_t)kTPWavesPerBlock + threadIdx.x / kTPWave;
-  if (row_begin + w >= row_end) return;
-  const int i = uniform((int)(row_begin + w));
-  const int c0 = lane * CPL;
-  const bool on = c0 < C;
-  const int PC = NP * C;
+  const int64_t row = row_begin + w / NG;
+  if (row >= row_end) return;
+  const int i = uniform((int)row);
+  const int g = uniform((int)(w % NG));
+  const int CC = MASKED ? C : 64 * CPL;
+  const uint32_t c0 = (uint32_t)(lane * CPL);
+  const bool on = (int)c0 < C;
   const int e_lo = uniform(row_ptr[i]), e_hi = uniform(row_ptr[i + 1]);
-
-  T acc[DOUT][CPL];
-#pragma unroll
-  for (int o = 0; o < DOUT; ++o)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[o][c] = T(0);
-
-  for (int e = e_lo; e < e_hi; ++e) {
-    const int j = uniform(src[e]);
-    const int64_t el = (int64_t)e - edge_begin;
-    T y[DSH];
-#pragma unroll
-    for (int k = 0; k < DSH; ++k) y[k] = Y[el * DSH + k];
-    T hv[DIN][CPL];
-#pragma unroll
-    for (int m = 0; m < DIN; ++m) load_ch<T, CPL>(h + ((int64_t)j * DIN + m) * C + c0, on, hv[m]);
-    static_for<NP>([&](auto pc) {
-      constexpr int p = decltype(pc)::value;
-      constexpr Path P = kTable<L1, L2, L3>.path[p];
-      T rp[CPL];
-      load_ch<T, CPL>(R + el * PC + p * C + c0, on, rp);
-      T hr[2 * P.l1 + 1][CPL];
-#pragma unroll
-      for (int m1 = 0; m1 < 2 * P.l1 + 1; ++m1)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) hr[m1][c] = rp[c] * hv[P.l1 * P.l1 + m1][c];
-      static_for<2 * P.l3 + 1>([&](auto m3c) {
-        constexpr int m3 = decltype(m3c)::value;
-        constexpr int row = kTable<L1, L2, L3>.out_row(p, m3);
-        static_for<2 * P.l1 + 1>([&](auto m1c) {
-          constexpr int m1 = decltype(m1c)::value;
-          if constexpr (m13_nonzero(kTable<L1, L2, L3>, p, m1, m3)) {
-            const T M = coupling_matrix_entry<T, L1, L2, L3, p, m1, m3>(y);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[row][c] += M * hr[m1][c];
-          }
-        });
-      });
-    });
-  }
-#pragma unroll
-  for (int o = 0; o < DOUT; ++o) {
-    T v[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) v[c] = scale * acc[o][c];
-    store_ch<T, CPL>(out + ((int64_t)i * DOUT + o) * C + c0, on, v);
-  }
+  T* __restrict__ oi = out + (int64_t)i * DOUT * CC;
+  static_for<NG>([&](auto gc) {
+    constexpr int G = decltype(gc)::value;
+    if (g == G)
+      tp_fwd_group<T, L1, L2, L3, CPL, NG, MASKED, G>(src, e_lo, e_hi, edge_begin, CC, c0, on, h, Y,
+                                                     R, oi, scale);
+  });
 }
 
 // ---------------------------------------------------------------------------
+// Sum of v[0..15] over the 64 lanes of a wave, reduce-scatter style: lane l
+// with l % 4 == 0 ends with the total of entry l / 4 (17 cross-lane moves).
 template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kTPWave);
-  return v;
-}
-
-template <typename T, int L1, int L2, int L3, int CPL>
-__global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
-k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src,
-              int64_t row_begin, int64_t row_end, int64_t edge_begin, int C, T scale,
-              const T* __restrict__ h, const T* __restrict__ Y, const T* __restrict__ R,
-              const T* __restrict__ G, T* __restrict__ dR, T* __restrict__ dY) {
-  constexpr int NP = kTable<L1, L2, L3>.np, DIN = kTable<L1, L2, L3>.din, DSH = kTable<L1, L2, L3>.dsh, DOUT = kTable<L1, L2, L3>.dout;
+__device__ __forceinline__ T wave_reduce_scatter16(const T (&v)[16]) {
   const int lane = threadIdx.x % kTPWave;
-  const int64_t w = blockIdx.x * (int64_t)kTPWavesPerBlock + threadIdx.x / kTPWave;
-  if (row_begin + w >= row_end) return;
-  const int i = uniform((int)(row_begin + w));
-  const int c0 = lane * CPL;
-  const bool on = c0 < C;
-  const int PC = NP * C;
-  const int e_lo = uniform(row_ptr[i]), e_hi = uniform(row_ptr[i + 1]);
-  if (e_lo == e_hi) return;
-
-  T gi[DOUT][CPL];
+  T a[8];
+  {
+    const bool hi = lane & 32;
 #pragma unroll
-  for (int o = 0; o < DOUT; ++o) load_ch<T, CPL>(G + ((int64_t)i * DOUT + o) * C + c0, on, gi[o]);
-
-  for (int e = e_lo; e < e_hi; ++e) {
-    const int j = uniform(src[e]);
-    const int64_t el = (int64_t)e - edge_begin;
-    T y[DSH];
-#pragma unroll
-    for (int k = 0; k < DSH; ++k) y[k] = Y[el * DSH + k];
-    T hv[DIN][CPL];
-#pragma unroll
-    for (int m = 0; m < DIN; ++m) load_ch<T, CPL>(h + ((int64_t)j * DIN + m) * C + c0, on, hv[m]);
-    T dy[DSH];
-#pragma unroll
-    for (int k = 0; k < DSH; ++k) dy[k] = T(0);
-    static_for<NP>([&](auto pc) {
-      constexpr int p = decltype(pc)::value;
-      constexpr Path P = kTable<L1, L2, L3>.path[p];
-      T rp[CPL];
-      load_ch<T, CPL>(R + el * PC + p * C + c0, on, rp);
-      T drp[CPL];
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) drp[c] = T(0);
-      static_for<2 * P.l3 + 1>([&](auto m3c) {
-        constexpr int m3 = decltype(m3c)::value;
-        constexpr int row = kTable<L1, L2, L3>.out_row(p, m3);
-        T tm[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) tm[c] = T(0);
-        T rg[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) rg[c] = rp[c] * gi[row][c];
-        static_for<2 * P.l1 + 1>([&](auto m1c) {
-          constexpr int m1 = decltype(m1c)::value;
-          if constexpr (m13_nonzero(kTable<L1, L2, L3>, p, m1, m3)) {
-            const T M = coupling_matrix_entry<T, L1, L2, L3, p, m1, m3>(y);
-            T hg = T(0);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-              tm[c] += M * hv[P.l1 * P.l1 + m1][c];
-              hg += hv[P.l1 * P.l1 + m1][c] * rg[c];
-            }
-            static_for<2 * P.l2 + 1>([&](auto m2c) {
-              constexpr int m2 = decltype(m2c)::value;
-              constexpr double cv = kTable<L1, L2, L3>.cg[p][m1][m2][m3];
-              if constexpr (cv != 0.0) dy[P.l2 * P.l2 + m2] += T(cv) * hg;
-            });
-          }
-        });
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) drp[c] += gi[row][c] * tm[c];
-      });
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) drp[c] *= scale;
-      store_ch<T, CPL>(dR + el * PC + p * C + c0, on, drp);
-    });
-#pragma unroll
-    for (int k = 0; k < DSH; ++k) {
-      const T v = wave_sum(dy[k]);
-      if (lane == k) dY[el * DSH + k] = scale * v;
+    for (int k = 0; k < 8; ++k) {
+      const T send = hi ? v[k] : v[k + 8];
+      const T keep = hi ? v[k + 8] : v[k];
+      a[k] = keep + __shfl_xor(send, 32, kTPWave);
     }
   }
+  T b[4];
+  {
+    const bool hi = lane & 16;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const T send = hi ? a[k] : a[k + 4];
+      const T keep = hi ? a[k + 4] : a[k];
+      b[k] = keep + __shfl_xor(send, 16, kTPWave);
+    }
+  }
+  T c[2];
+  {
+    const bool hi = lane & 8;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const T send = hi ? b[k] : b[k + 2];
+      const T keep = hi ? b[k + 2] : b[k];
+      c[k] = keep + __shfl_xor(send, 8, kTPWave);
+    }
+  }
+  T d;
+  {
+    const bool hi = lane & 4;
+    const T send = hi ? c[0] : c[1];
+    const T keep = hi ? c[1] : c[0];
+    d = keep + __shfl_xor(send, 4, kTPWave);
+  }
+  d += __shfl_xor(d, 2, kTPWave);
+  d += __shfl_xor(d, 1, kTPWave);
+  return d;
 }
 
-// ---------------------------------------------------------------------------
-template <typename T, int L1, int L2, int L3, int CPL>
+// Backward, edge side.  One wave per receiver row and 64 channels (NW waves
+// per row, one channel per lane), G[i] held in registers for the whole row.
+// Per edge and path, with K[m1][m2] = sum_m3 C^p[m1,m2,m3] G[i,(p,m3)]:
+//   W[m1] = sum_m2 Y[m2] K[m1][m2]    Q[m2] = sum_m1 h[j,m1] K[m1][m2]
+//   dR    = s * sum_m1 h[j,m1] W[m1]  dY[m2] += R Q[m2]   (channel reduction)
+//   t[m1] += R W[m1]                  (the edge's contribution to dh of its
+//                                      sender j, stored at the reverse edge's
+//                                      slot so dh of j is a contiguous row sum)
+template <typename T, int L1, int L2, int L3, int NW>
 __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
-k_tp_bwd_node(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src,
-              int64_t row_begin, int64_t row_end, int64_t edge_begin, int C, T scale,
+k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src,
+              const int32_t* __restrict__ rev, int64_t row_begin, int64_t row_end,
+              int64_t edge_begin, int64_t n_chunk_edges, int C, T scale, const T* __restrict__ h,
               const T* __restrict__ Y, const T* __restrict__ R, const T* __restrict__ G,
-              T* __restrict__ dh) {
-  constexpr int NP = kTable<L1, L2, L3>.np, DIN = kTable<L1, L2, L3>.din, DSH = kTable<L1, L2, L3>.dsh, DOUT = kTable<L1, L2, L3>.dout;
+              T* __restrict__ dR, T* __restrict__ dYp, T* __restrict__ dh_edge) {
+  constexpr int NP = kTable<L1, L2, L3>.np, DIN = kTable<L1, L2, L3>.din;
+  constexpr int DSH = kTable<L1, L2, L3>.dsh, DOUT = kTable<L1, L2, L3>.dout;
+  static_assert(DSH <= 16, "harmonics beyond l = 3");
+  const RowWave rw = row_wave<NW>(row_begin, row_end, C);
+  if (!rw.ok) return;
+  const int i = rw.row;
+  const int CC = channels<NW>(C);
+  const int PC = NP * CC;
+  const uint32_t c0 = (uint32_t)rw.c0;
+  const int e_lo = uniform(row_ptr[i]), e_hi = uniform(row_ptr[i + 1]);
+  if (e_lo == e_hi) return;
   const int lane = threadIdx.x % kTPWave;
-  const int64_t w = blockIdx.x * (int64_t)kTPWavesPerBlock + threadIdx.x / kTPWave;
-  if (row_begin + w >= row_end) return;
-  const int jn = uniform((int)(row_begin + w));
-  const int c0 = lane * CPL;
-  const bool on = c0 < C;
-  const int PC = NP * C;
-  const int e_lo = uniform(row_ptr[jn]), e_hi = uniform(row_ptr[jn + 1]);
+  const int part = rw.c0 / kTPWave;   // which 64-channel slice (partial dY buffer)
 
-  T acc[DIN][CPL];
+  T gi[DOUT];
+  {
+    const T* __restrict__ gr = G + (int64_t)i * DOUT * CC;
 #pragma unroll
-  for (int m = 0; m < DIN; ++m)
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[m][c] = T(0);
+    for (int o = 0; o < DOUT; ++o) gi[o] = ldc<NW>(gr, o * CC + c0, rw.on);
+  }
 
-  for (int e = e_lo; e < e_hi; ++e) {
-    const int k = uniform(src[e]);  // the reverse edge (k <- jn) has jn as sender
+  struct Buf {
+    T h[DIN];
+    T r[NP];
+  };
+  auto load = [&](int e, Buf& b) {
+    const int j = uniform(src[e]);
+    const T* __restrict__ hj = h + (int64_t)j * DIN * CC;
+    const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
+#pragma unroll
+    for (int m = 0; m < DIN; ++m) b.h[m] = ldc<NW>(hj, m * CC + c0, rw.on);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) b.r[p] = ldc<NW>(re, p * CC + c0, rw.on);
+  };
+  auto compute = [&](int e, const Buf& b) {
     const int64_t el = (int64_t)e - edge_begin;
-    T y[DSH];
+    const T* __restrict__ ye = Y + el * DSH;
+    T* __restrict__ dre = dR + el * PC;
+    T dy[16];
 #pragma unroll
-    for (int q = 0; q < DSH; ++q) y[q] = Y[el * DSH + q];
+    for (int k = 0; k < 16; ++k) dy[k] = T(0);
+    T t[DIN];
+#pragma unroll
+    for (int m = 0; m < DIN; ++m) t[m] = T(0);
     static_for<NP>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
       constexpr Path P = kTable<L1, L2, L3>.path[p];
-      constexpr T sgn = (P.l2 % 2) ? T(-1) : T(1);
-      T rp[CPL];
-      load_ch<T, CPL>(R + el * PC + p * C + c0, on, rp);
+      constexpr int n1 = 2 * P.l1 + 1, n2 = 2 * P.l2 + 1;
+      T K[n1][n2];
+#pragma unroll
+      for (int a = 0; a < n1; ++a)
+#pragma unroll
+        for (int c = 0; c < n2; ++c) K[a][c] = T(0);
       static_for<2 * P.l3 + 1>([&](auto m3c) {
         constexpr int m3 = decltype(m3c)::value;
         constexpr int row = kTable<L1, L2, L3>.out_row(p, m3);
-        T gk[CPL];
-        load_ch<T, CPL>(G + ((int64_t)k * DOUT + row) * C + c0, on, gk);
-        T rg[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) rg[c] = sgn * rp[c] * gk[c];
-        static_for<2 * P.l1 + 1>([&](auto m1c) {
+        static_for<n1>([&](auto m1c) {
           constexpr int m1 = decltype(m1c)::value;
-          if constexpr (m13_nonzero(kTable<L1, L2, L3>, p, m1, m3)) {
-            const T M = coupling_matrix_entry<T, L1, L2, L3, p, m1, m3>(y);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[P.l1 * P.l1 + m1][c] += M * rg[c];
-          }
+          static_for<n2>([&](auto m2c) {
+            constexpr int m2 = decltype(m2c)::value;
+            constexpr double cv = kTable<L1, L2, L3>.cg[p][m1][m2][m3];
+            if constexpr (cv != 0.0) K[m1][m2] += T(cv) * gi[row];
+          });
         });
       });
+      T dr = T(0);
+      static_for<n1>([&](auto m1c) {
+        constexpr int m1 = decltype(m1c)::value;
+        T w = T(0);
+        static_for<n2>([&](auto m2c) {
+          constexpr int m2 = decltype(m2c)::value;
+          if constexpr (kTable<L1, L2, L3>.m12nz(p, m1, m2)) w += ye[P.l2 * P.l2 + m2] * K[m1][m2];
+        });
+        dr += b.h[P.l1 * P.l1 + m1] * w;
+        t[P.l1 * P.l1 + m1] += b.r[p] * w;
+      });
+      static_for<n2>([&](auto m2c) {
+        constexpr int m2 = decltype(m2c)::value;
+        T q = T(0);
+        static_for<n1>([&](auto m1c) {
+          constexpr int m1 = decltype(m1c)::value;
+          if constexpr (kTable<L1, L2, L3>.m12nz(p, m1, m2)) q += b.h[P.l1 * P.l1 + m1] * K[m1][m2];
+        });
+        dy[P.l2 * P.l2 + m2] += b.r[p] * q;
+      });
+      stc<NW>(dre, p * CC + c0, rw.on, scale * dr);
     });
-  }
+    const int er = uniform(rev[e]);
+    T* __restrict__ te = dh_edge + (int64_t)er * DIN * CC;
 #pragma unroll
-  for (int m = 0; m < DIN; ++m) {
-    T v[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) v[c] = scale * acc[m][c];
-    store_ch<T, CPL>(dh + ((int64_t)jn * DIN + m) * C + c0, on, v);
+    for (int m = 0; m < DIN; ++m) stc<NW>(te, m * CC + c0, rw.on, t[m]);
+    const T tot = wave_reduce_scatter16<T>(dy);
+    if ((lane & 3) == 0 && (lane >> 2) < DSH)
+      dYp[((int64_t)part * n_chunk_edges + el) * DSH + (lane >> 2)] = scale * tot;
+  };
+  Buf A, B;
+  int e = e_lo;
+  load(e, A);
+  while (e < e_hi) {
+    if (e + 1 < e_hi) load(e + 1, B);
+    compute(e, A);
+    if (++e >= e_hi) break;
+    if (e + 1 < e_hi) load(e + 1, A);
+    compute(e, B);
+    ++e;
   }
 }
 
 // ---------------------------------------------------------------------------
-inline unsigned tp_blocks(int64_t rows) {
-  return (unsigned)((rows + kTPWavesPerBlock - 1) / kTPWavesPerBlock);
+// dh[j] = s * sum over the edges e of row j of dh_edge[e]: each slot holds the
+// contribution of the reverse edge (whose sender is j), so the sum runs over a
+// contiguous range in CSR order (deterministic, no atomics).  One thread per
+// (atom, feature row, channel).
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_dh_gather(int64_t n, int din_c, const int32_t* __restrict__ row_ptr, T scale,
+            const T* __restrict__ dh_edge, T* __restrict__ dh) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= n * din_c) return;
+  const int64_t j = t / din_c;
+  const int q = (int)(t - j * din_c);
+  T acc = T(0);
+  const int lo = row_ptr[j], hi = row_ptr[j + 1];
+  for (int e = lo; e < hi; ++e) acc += dh_edge[(int64_t)e * din_c + q];
+  dh[t] = scale * acc;
 }
 
-}  // namespace tpc
+// ---------------------------------------------------------------------------
+inline int tp_waves_per_row(int C) { return C <= kTPWave ? 1 : C / kTPWave; }
 
-// Instantiated (dtype, node_lmax, sh_lmax, out_lmax, channels-per-lane) sets.
-// Channels per lane is 1 for C <= 64 and 2 for C = 128.
-#define TPC_TP_CONFIGS(X)                                                          \
-  X(float, 1, 2, 1, 1) X(float, 1, 2, 1, 2) X(float, 1, 3, 3, 1) X(float, 1, 3, 3, 2) \
-  X(float, 2, 3, 3, 1) X(float, 2, 3, 3, 2) X(float, 3, 3, 3, 1)                   \
-  X(double, 1, 2, 1, 1) X(double, 1, 3, 3, 1) X(double, 2, 3, 3, 1) X(double, 3, 3, 3, 1)
+inline unsigned tp_blocks(int64_t rows, int C) {
+  const int64_t waves = rows * tp_waves_per_row(C);
+  return (unsigned)((waves + kTPWavesPerBlock - 1) / kTPWavesPerBlock);
+}
 
-inline int tp_cpl(int C) { return C >= 1 && C <= 64 ? 1 : (C == 128 ? 2 : 0); }
+inline bool tp_channels_ok(int C) { return (C >= 1 && C <= 64) || C == 128; }
+
+// Compile-time waves per row for a channel count (0: fewer than 64 channels).
+inline int tp_nw(int C) { return C < 64 ? 0 : C / 64; }
 
 namespace tp_detail {
 template <typename T>
 constexpr int dtype_id() { return std::is_same<T, double>::value ? 1 : 0; }
 }  // namespace tp_detail
+
+}  // namespace tpc
+
+// Built (dtype, node_lmax, sh_lmax, out_lmax) sets.  Channels: 1..64 or 128.
+#define TPC_TP_CONFIGS(X)                                                    \
+  X(float, 1, 2, 1) X(float, 1, 3, 3) X(float, 2, 3, 3) X(float, 3, 3, 3)   \
+  X(double, 1, 2, 1) X(double, 1, 3, 3) X(double, 2, 3, 3) X(double, 3, 3, 3)

@@ -93,6 +93,7 @@ def run_chunked(case, nl, chunks=1, keep_edges=None, want_forces=True):
     out = t.empty((N, ctx.d_out, case.cfg["C"]), dtype=ctx.dtype, device="cuda")
     dh = t.empty_like(case.h)
     g_edge = t.empty((nl.n_edges, 3), dtype=ctx.dtype, device="cuda")
+    dh_edge = t.empty((nl.n_edges, ctx.d_in, case.cfg["C"]), dtype=ctx.dtype, device="cuda")
     forces = t.empty((N, 3), dtype=ctx.dtype, device="cuda") if want_forces else None
     bounds = row_bounds(rp, chunks)
     max_e = max(int(rp[b] - rp[a]) for a, b in bounds)
@@ -106,7 +107,8 @@ def run_chunked(case, nl, chunks=1, keep_edges=None, want_forces=True):
         ctx.conv_fwd(case.pos, case.cell, nl, case.h, case.W, s, out=out, eb=eb, rows=(a, b),
                      edges=(e0, e1))
         last = n == len(bounds) - 1
-        ctx.conv_bwd(nl, case.h, case.W, s, case.G, eb, dh=dh, dR=dR, g_edge=g_edge,
+        ctx.conv_bwd(nl, case.h, case.W, s, case.G, eb, dh=dh if last else None, dR=dR,
+                     g_edge=g_edge, dh_edge=dh_edge, want_dh=last,
                      want_forces=want_forces and last, forces=forces if last else None)
         sel = keep_edges[(keep_edges >= e0) & (keep_edges < e1)]
         if len(sel):

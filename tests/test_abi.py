@@ -132,10 +132,10 @@ def test_conv_argument_checks_run_before_device_work():
     for needle in ("row_begin <= row_end <= n_atoms", "row_ptr", "eb.Y", "weights"):
         assert needle in m
     st = lib.tpc_conv_bwd(h, 10, 3, None, None, None, 0, 5, 0, 5, None, None, float("nan"), None,
-                          ctypes.byref(eb), None, None, None, None, None, 0, None)
+                          ctypes.byref(eb), None, None, None, None, None, None, 0, None)
     assert st == 1
     m = lib.tpc_last_error().decode()
-    for needle in ("n_edges must be >= edge_end", "scale", "g_edge", "workspace"):
+    for needle in ("n_edges must be >= edge_end", "scale", "g_edge", "dh_edge", "rev", "workspace"):
         assert needle in m
 
 
