@@ -38,7 +38,8 @@ KERNEL_SOURCES = {
     "tp_bwd_edge": ["tp_impl.hpp", "tp_bwd_edge.hip", "tables.hpp"],
     "dh_gather": ["tp_impl.hpp", "tp_bwd_edge.hip"],
     "radial_fwd": ["radial.hip"],
-    "radial_bwd": ["radial.hip"],
+    "radial_bwd_dA": ["radial.hip"],
+    "radial_bwd_mlp": ["radial.hip"],
     "geom_fwd": ["geom.hip"],
     "geom_bwd": ["geom.hip"],
 }
@@ -76,8 +77,12 @@ def algorithmic(kernel, N, E, cfg, ctx):
     hidden = 2 * (8 * H + (NH - 1) * H * H)
     if kernel == "radial_fwd":
         return E * (8 * T + T * PC), E * (hidden + 2 * H * PC)
-    if kernel == "radial_bwd":
-        return E * (8 * T + T * PC + 8 * T), E * (2 * hidden + 2 * H * PC)
+    if kernel == "radial_bwd_dA":
+        # reads dR, writes dA (H per edge)
+        return E * (T * PC + T * H), E * 2 * H * PC
+    if kernel == "radial_bwd_mlp":
+        # reads ef and dA, writes d(ef); recomputes the hidden layers
+        return E * (8 * T + T * H + 8 * T), E * 2 * hidden
     return None, None
 
 
@@ -219,9 +224,12 @@ def main(argv=None):
 
     per_kernel = {n: dict(avg_ms=tot / cnt, launches_per_step=cnt / a.steps, ms_per_step=tot / a.steps)
                   for n, (tot, cnt) in kt.items()}
-    fwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0) for n in ("geom_fwd", "radial_fwd", "tp_fwd"))
-    bwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0)
-                 for n in ("tp_bwd_edge", "radial_bwd", "geom_bwd", "dh_gather", "forces"))
+    # one launch of each per pass (the weight packing runs once in each pass)
+    fwd_ms = sum(per_kernel.get(n, {}).get("avg_ms", 0.0)
+                 for n in ("geom_fwd", "radial_pack", "radial_fwd", "tp_fwd"))
+    bwd_ms = sum(per_kernel.get(n, {}).get("avg_ms", 0.0)
+                 for n in ("tp_bwd_edge", "radial_pack", "radial_bwd_dA", "radial_bwd_mlp", "geom_bwd",
+                           "dh_gather", "forces"))
     nbr_ms = sum(v["ms_per_step"] for n, v in per_kernel.items() if n.startswith("nbr"))
     dominant = max((n for n in per_kernel if n in KERNEL_SOURCES), key=lambda n: per_kernel[n]["ms_per_step"])
     roof = roofline_for(dominant, per_kernel[dominant]["avg_ms"] * 1e-3, N, E, cfg, ctx)

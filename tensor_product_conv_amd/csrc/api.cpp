@@ -198,8 +198,27 @@ NbrWs nbr_layout(int64_t n, int64_t nbin) {
 }
 
 struct BwdWs {
-  size_t dR, dY, d_ef, status, total, total_without_dR;
+  size_t dR, dY, d_ef, status, pack, dA, total, total_without_dR;
 };
+
+tpc::RadialPack pack_layout(const tpc_ctx* c) {
+  return tpc::radial_pack_layout(c->hidden, c->n_hidden, c->tab.np * c->spec.channels);
+}
+
+struct FwdWs {
+  size_t status, pack, total;
+};
+
+FwdWs fwd_layout(const tpc_ctx* c) {
+  FwdWs w{};
+  size_t off = 0;
+  w.status = off;
+  off += align_up(sizeof(int32_t) * 8);
+  w.pack = off;
+  off += align_up(c->tsize * (size_t)pack_layout(c).total);
+  w.total = off;
+  return w;
+}
 
 int waves_per_row(int C) { return C <= 64 ? 1 : C / 64; }
 
@@ -213,6 +232,10 @@ BwdWs bwd_layout(const tpc_ctx* c, int64_t ne) {
   off += align_up(T * (size_t)ne * 8);
   w.status = off;
   off += align_up(sizeof(int32_t) * 8);
+  w.pack = off;
+  off += align_up(T * (size_t)pack_layout(c).total);
+  w.dA = off;
+  off += align_up(T * (size_t)tpc::radial_dA_elems(c->hidden, ne));
   w.total_without_dR = off;
   w.dR = off;
   off += align_up(T * (size_t)ne * c->tab.np * c->spec.channels);
@@ -411,7 +434,7 @@ tpc_status tpc_workspace_query(const tpc_ctx* c, int op, int64_t n_atoms, int64_
     if (E.status != TPC_OK) return E.finish();
     *bytes = nbr_layout(n_atoms, (int64_t)g.nb[0] * g.nb[1] * g.nb[2]).total;
   } else if (op == TPC_OP_FWD) {
-    *bytes = align_up(sizeof(int32_t) * 8);
+    *bytes = fwd_layout(c).total;
   } else if (op == TPC_OP_BWD) {
     *bytes = bwd_layout(c, n_edges).total;
   } else {
@@ -598,9 +621,12 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
     for (int k = 0; k < c->spec.n_layers; ++k)
       if (!weights[k]) E.add(TPC_ERR_INVALID, "weights[%d] must be non-null", k);
   }
-  const size_t need = align_up(sizeof(int32_t) * 8);
-  if (c->spec.validate && (!ws || ws_bytes < need))
-    E.add(TPC_ERR_WORKSPACE, "validation needs a workspace of %zu bytes", need);
+  const FwdWs FL = fwd_layout(c);
+  if (edge_end > edge_begin || c->spec.validate) {
+    if (!ws) E.add(TPC_ERR_INVALID, "workspace must be non-null");
+    else if (ws_bytes < FL.total)
+      E.add(TPC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, FL.total);
+  }
   if (ws && !aligned(ws, 256)) E.add(TPC_ERR_INVALID, "workspace must be 256-byte aligned");
   tpc_status st = E.finish();
   if (st != TPC_OK) return st;
@@ -608,7 +634,7 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (c->spec.validate) {
     st = run_csr_check(n, edge_end, row_ptr, src, shift, row_begin, row_end, edge_begin, edge_end,
-                       static_cast<int32_t*>(ws), s);
+                       reinterpret_cast<int32_t*>(static_cast<char*>(ws) + FL.status), s);
     if (st != TPC_OK) return st;
   }
   const int dt = c->spec.dtype;
@@ -628,9 +654,11 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
   if (ne > 0) {
     TPC_LAUNCH("geom_fwd", s, tpc::launch_geom_fwd(dt, c->spec.sh_lmax, ga, eb->Y, eb->ef, eb->rv, s),
                "conv_fwd: geometry");
-    TPC_LAUNCH("radial_fwd", s,
-               tpc::launch_radial_fwd(dt, c->hidden, c->n_hidden, ne, c->tab.np * c->spec.channels,
-                                      eb->ef, weights, eb->R, s),
+    const tpc::RadialPack PL = pack_layout(c);
+    void* pk = static_cast<char*>(ws) + FL.pack;
+    TPC_LAUNCH("radial_pack", s, tpc::launch_radial_pack(dt, PL, weights, pk, s),
+               "conv_fwd: radial weight packing");
+    TPC_LAUNCH("radial_fwd", s, tpc::launch_radial_fwd(dt, PL, ne, eb->ef, pk, eb->R, s),
                "conv_fwd: radial MLP");
   }
   tpc::TPArgs ta{};
@@ -741,10 +769,15 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
   ta.dh_edge = dh_edge;
   if (ne > 0) {
     TPC_LAUNCH("tp_bwd_edge", s, tpc::launch_tp_bwd_edge(dt, L1, L2, L3, ta, s), "conv_bwd: tensor product (edges)");
-    TPC_LAUNCH("radial_bwd", s,
-               tpc::launch_radial_bwd(dt, c->hidden, c->n_hidden, ne, c->tab.np * c->spec.channels,
-                                      eb->ef, dRp, weights, d_ef, s),
-               "conv_bwd: radial MLP");
+    const tpc::RadialPack PL = pack_layout(c);
+    void* pk = w + L.pack;
+    void* dA = w + L.dA;
+    TPC_LAUNCH("radial_pack", s, tpc::launch_radial_pack(dt, PL, weights, pk, s),
+               "conv_bwd: radial weight packing");
+    TPC_LAUNCH("radial_bwd_dA", s, tpc::launch_radial_bwd_dA(dt, PL, ne, dRp, pk, dA, s),
+               "conv_bwd: radial last layer");
+    TPC_LAUNCH("radial_bwd_mlp", s, tpc::launch_radial_bwd_mlp(dt, PL, ne, eb->ef, dA, pk, d_ef, s),
+               "conv_bwd: radial hidden layers");
     TPC_LAUNCH("geom_bwd", s,
                tpc::launch_geom_bwd(dt, L2, ne, edge_begin, c->spec.r_cut, eb->rv, dY,
                                     waves_per_row(c->spec.channels), d_ef, g_edge, s),

@@ -49,11 +49,57 @@ hipError_t launch_geom_bwd(int dtype, int L2, int64_t ne, int64_t edge_begin, do
                            const void* rv, const void* dY, int n_parts, const void* d_ef, void* g,
                            hipStream_t s);
 
+// The radial MLP's weights rewritten in MFMA operand order (element offsets
+// of each section in one buffer; every section starts on a 64-element
+// boundary).  NB = H/16 output blocks per hidden layer, S4 = 4*NB reduction
+// steps per block, nblk = ceil(pc/16) blocks of the last layer.
+//   f0  forward layer 1        [NB][64 lanes][2]
+//   fh  forward layers 2..NH   [NH-1][NB][64][S4]
+//   fl  forward last layer     [nblk][64][S4]
+//   bl  backward last layer    [nblk][64][S4]   (W_L^T as the A operand)
+//   bh  backward layers 2..NH  [NH-1][NB][64][S4]
+//   b0  backward layer 1       [64][S4]          (rows 8..15 zero)
+struct RadialPack {
+  int H, NH, pc, nblk;
+  int64_t f0, fh, fl, bl, bh, b0, total;
+};
+inline RadialPack radial_pack_layout(int H, int NH, int pc) {
+  auto up = [](int64_t v) { return (v + 63) / 64 * 64; };
+  RadialPack L{};
+  L.H = H;
+  L.NH = NH;
+  L.pc = pc;
+  L.nblk = (pc + 15) / 16;
+  const int64_t NB = H / 16, S4 = 4 * NB, hid = (int64_t)(NH - 1) * NB * 64 * S4;
+  int64_t off = 0;
+  L.f0 = off;
+  off += up(NB * 64 * 2);
+  L.fh = off;
+  off += up(hid);
+  L.fl = off;
+  off += up((int64_t)L.nblk * 64 * S4);
+  L.bl = off;
+  off += up((int64_t)L.nblk * 64 * S4);
+  L.bh = off;
+  off += up(hid);
+  L.b0 = off;
+  off += up(64 * S4);
+  L.total = off;
+  return L;
+}
+// Per-edge buffer of the backward's first stage: dA for every 16-edge strip
+// in register order, H values per edge.
+inline int64_t radial_dA_elems(int H, int64_t ne) { return (ne + 15) / 16 * 16 * H; }
+
 bool radial_supported(int H, int NH);
-hipError_t launch_radial_fwd(int dtype, int H, int NH, int64_t ne, int pc, const void* ef,
-                             const void* const* w, void* R, hipStream_t s);
-hipError_t launch_radial_bwd(int dtype, int H, int NH, int64_t ne, int pc, const void* ef,
-                             const void* dR, const void* const* w, void* d_ef, hipStream_t s);
+hipError_t launch_radial_pack(int dtype, const RadialPack& L, const void* const* w, void* pk,
+                              hipStream_t s);
+hipError_t launch_radial_fwd(int dtype, const RadialPack& L, int64_t ne, const void* ef,
+                             const void* pk, void* R, hipStream_t s);
+hipError_t launch_radial_bwd_dA(int dtype, const RadialPack& L, int64_t ne, const void* dR,
+                                const void* pk, void* dA3, hipStream_t s);
+hipError_t launch_radial_bwd_mlp(int dtype, const RadialPack& L, int64_t ne, const void* ef,
+                                 const void* dA3, const void* pk, void* d_ef, hipStream_t s);
 
 // Which (node_lmax, sh_lmax, out_lmax, channels) the fused kernels are built for.
 bool tp_supported(int dtype, int L1, int L2, int L3, int C);

@@ -5,7 +5,7 @@
 // and precision options", section "Radial network"; FlashCart section 2 calls
 // them the distance-dependent weights).  Bias-free: a_k = SiLU(a_{k-1} W_k) for
 // the hidden layers, R = a_{L-1} W_L.  This is the only dense contraction of
-// the convolution.
+// the convolution, and its last layer (H x P*C) holds nearly all of its flops.
 //
 // Mapping.  Each MFMA computes D'[n][e] = sum_k W[k][n] * A[e][k] for 16 output
 // features n and 16 edges e: the weight matrix is the A operand (lane l gives
@@ -20,10 +20,20 @@
 // leave registers between layers.  A wave owns S strips of 16 edges and
 // reuses every weight load S times.
 //
+// Weights.  k_radial_pack rewrites the caller's weight matrices once per call
+// into "operand order": for every 16-wide output block, the values each lane
+// feeds to the MFMA steps of that block lie next to each other, so a lane
+// fetches a block's weights with 16-byte vector loads and the hot loops carry
+// no index arithmetic, bounds tests or scattered loads.  The last layer is
+// streamed block by block with the next block's weights in flight while the
+// current block's MFMAs run.
+//
 // Backward (input gradient only; FastMACE's "fused_folded_backward" idea of
-// one kernel for the radial input gradient): the hidden layers are recomputed
-// in registers, dA = dR W_L^T runs on MFMA with dR streamed as the B operand,
-// then dz = dA * SiLU'(z) and dA_prev = dz W_k^T down to d(ef).
+// one pass for the radial input gradient): k_radial_bwd_dA forms the big
+// product dA = dR W_L^T on MFMA, streaming dR as the B operand and keeping
+// only the accumulators live, and writes dA per wave strip in register order;
+// k_radial_bwd_mlp recomputes the hidden layers in registers and carries dA
+// down through dz = dA * SiLU'(z), dA_prev = dz W_k^T to d(ef).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,6 +43,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 template <typename T>
 struct Vec4;
@@ -54,9 +65,22 @@ __device__ __forceinline__ f64x4 mfma(double a, double b, f64x4 c) {
   return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 
+// Four consecutive values from a 16-byte aligned address.
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f64x4 ld4(const double* p) {
+  const f64x2 a = *reinterpret_cast<const f64x2*>(p);
+  const f64x2 b = *reinterpret_cast<const f64x2*>(p + 2);
+  return f64x4{a[0], a[1], b[0], b[1]};
+}
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void st4(double* p, f64x4 v) {
+  *reinterpret_cast<f64x2*>(p) = f64x2{v[0], v[1]};
+  *reinterpret_cast<f64x2*>(p + 2) = f64x2{v[2], v[3]};
+}
+
 // Row of the 16x16 MFMA result held in register r of a lane in group g.
 template <typename T>
-__device__ constexpr int drow(int g, int r) {
+__host__ __device__ constexpr int drow(int g, int r) {
   return std::is_same<T, double>::value ? 4 * r + g : 4 * g + r;
 }
 
@@ -75,197 +99,314 @@ __device__ __forceinline__ T silu_dz(T z) {
 
 constexpr int kWave = 64;
 
+template <typename T>
+__device__ __forceinline__ vec4<T> zero4() {
+  return vec4<T>{T(0), T(0), T(0), T(0)};
+}
+
+// ---------------------------------------------------------------------------
+// weight packing (see RadialPack for the sections)
+template <typename T>
+__global__ void __launch_bounds__(256) k_radial_pack(RadialPack L, RadialWeights<T> W, T* __restrict__ pk) {
+  const int H = L.H, NB = L.H / 16, S4 = 4 * L.H / 16, pc = L.pc;
+  const int64_t per_hidden = (int64_t)NB * kWave * S4;
+  const T* __restrict__ WL = W.w[L.NH];
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < L.total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    T v = T(0);
+    if (i < L.fh) {
+      const int64_t q = i - L.f0;
+      if (q < (int64_t)NB * kWave * 2) {
+        const int s = (int)(q % 2), lane = (int)((q / 2) % kWave), nb = (int)(q / (2 * kWave));
+        v = W.w[0][(4 * s + lane / 16) * H + nb * 16 + lane % 16];
+      }
+    } else if (i < L.fl) {
+      int64_t q = i - L.fh;
+      if (q < (L.NH - 1) * per_hidden) {
+        const int k = 1 + (int)(q / per_hidden);
+        q %= per_hidden;
+        const int j = (int)(q % S4), lane = (int)((q / S4) % kWave), no = (int)(q / (S4 * kWave));
+        const int g = lane / 16, el = lane % 16;
+        v = W.w[k][(16 * (j / 4) + drow<T>(g, j % 4)) * H + no * 16 + el];
+      }
+    } else if (i < L.bl) {
+      const int64_t q = i - L.fl;
+      if (q < (int64_t)L.nblk * kWave * S4) {
+        const int j = (int)(q % S4), lane = (int)((q / S4) % kWave);
+        const int64_t cb = q / (S4 * kWave);
+        const int g = lane / 16, el = lane % 16;
+        const int64_t col = cb * 16 + el;
+        if (col < pc) v = WL[(int64_t)(16 * (j / 4) + drow<T>(g, j % 4)) * pc + col];
+      }
+    } else if (i < L.bh) {
+      const int64_t q = i - L.bl;
+      if (q < (int64_t)L.nblk * kWave * S4) {
+        const int j = (int)(q % S4), lane = (int)((q / S4) % kWave);
+        const int64_t t = q / (S4 * kWave);
+        const int g = lane / 16, el = lane % 16;
+        const int64_t col = 16 * t + 4 * g + j % 4;
+        if (col < pc) v = WL[(int64_t)((j / 4) * 16 + el) * pc + col];
+      }
+    } else if (i < L.b0) {
+      int64_t q = i - L.bh;
+      if (q < (L.NH - 1) * per_hidden) {
+        const int k = 1 + (int)(q / per_hidden);
+        q %= per_hidden;
+        const int j = (int)(q % S4), lane = (int)((q / S4) % kWave), ko = (int)(q / (S4 * kWave));
+        const int g = lane / 16, el = lane % 16;
+        v = W.w[k][(ko * 16 + el) * H + 16 * (j / 4) + drow<T>(g, j % 4)];
+      }
+    } else {
+      const int64_t q = i - L.b0;
+      if (q < (int64_t)kWave * S4) {
+        const int j = (int)(q % S4), lane = (int)(q / S4);
+        const int g = lane / 16, el = lane % 16;
+        if (el < 8) v = W.w[0][el * H + 16 * (j / 4) + drow<T>(g, j % 4)];
+      }
+    }
+    pk[i] = v;
+  }
+}
+
+// First layer (K = 8, two reduction steps with k = 4*s + g) for S strips;
+// pre-activations into z.
+template <typename T, int H, int S>
+__device__ __forceinline__ void layer0(int64_t e0, int64_t ne, int lane, const T* __restrict__ ef,
+                                       const T* __restrict__ w0, T (&z)[S][H / 16][4]) {
+  constexpr int NB = H / 16;
+  const int g = lane / 16, el = lane % 16;
+  T b[S][2];
+#pragma unroll
+  for (int st = 0; st < S; ++st) {
+    int64_t e = e0 + st * 16 + el;
+    e = e < ne ? e : ne - 1;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) b[st][s] = ef[e * 8 + 4 * s + g];
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const T a0 = w0[(nb * kWave + lane) * 2], a1 = w0[(nb * kWave + lane) * 2 + 1];
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+      vec4<T> acc = mfma(a0, b[st][0], zero4<T>());
+      acc = mfma(a1, b[st][1], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z[st][nb][r] = acc[r];
+    }
+  }
+}
+
+// One H -> H layer: out = act W_k (pre-activation), weights in operand order.
+template <typename T, int H, int S>
+__device__ __forceinline__ void hidden(int lane, const T* __restrict__ wk, const T (&act)[S][H / 16][4],
+                                       T (&out)[S][H / 16][4]) {
+  constexpr int NB = H / 16, S4 = 4 * NB;
+#pragma unroll
+  for (int no = 0; no < NB; ++no) {
+    vec4<T> w[NB];
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni) w[ni] = ld4(wk + (no * kWave + lane) * S4 + 4 * ni);
+    vec4<T> acc[S];
+#pragma unroll
+    for (int st = 0; st < S; ++st) acc[st] = zero4<T>();
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int st = 0; st < S; ++st) acc[st] = mfma(w[ni][r], act[st][ni][r], acc[st]);
+#pragma unroll
+    for (int st = 0; st < S; ++st)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[st][no][r] = acc[st][r];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // forward
-template <typename T, int H, int NH, int S>
+template <typename T, int H, int NH, int S, bool VEC>
 __global__ void __launch_bounds__(256)
-k_radial_fwd(int64_t ne, int pc, const T* __restrict__ ef, RadialWeights<T> W, T* __restrict__ R) {
-  constexpr int NB = H / 16;
+k_radial_fwd(int64_t ne, int pc, const T* __restrict__ ef, const T* __restrict__ pk, RadialPack L,
+             T* __restrict__ R) {
+  constexpr int NB = H / 16, S4 = 4 * NB;
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, el = lane % 16;
   const int64_t e0 = (blockIdx.x * (int64_t)(blockDim.x / kWave) + threadIdx.x / kWave) * (16 * S);
   if (e0 >= ne) return;
 
   T act[S][NB][4];
-  // layer 1: K = 8 (two reduction steps, k = 4*s + g)
-  {
-    T b[S][2];
+  layer0<T, H, S>(e0, ne, lane, ef, pk + L.f0, act);
 #pragma unroll
-    for (int st = 0; st < S; ++st) {
-      const int64_t e = e0 + st * 16 + el;
+  for (int st = 0; st < S; ++st)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) b[st][s] = e < ne ? ef[e * 8 + 4 * s + g] : T(0);
-    }
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      T a[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) a[s] = W.w[0][(4 * s + g) * H + nb * 16 + el];
-#pragma unroll
-      for (int st = 0; st < S; ++st) {
-        vec4<T> acc = {T(0), T(0), T(0), T(0)};
-#pragma unroll
-        for (int s = 0; s < 2; ++s) acc = mfma(a[s], b[st][s], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) act[st][nb][r] = silu<T>(acc[r]);
-      }
-    }
-  }
-  // hidden layers 2..NH: K = H, step (nb, r) uses k = 16*nb + row(g, r)
+      for (int r = 0; r < 4; ++r) act[st][nb][r] = silu<T>(act[st][nb][r]);
 #pragma unroll
   for (int layer = 1; layer < NH; ++layer) {
-    const T* __restrict__ Wk = W.w[layer];
-    T nxt[S][NB][4];
-#pragma unroll
-    for (int no = 0; no < NB; ++no) {
-      vec4<T> acc[S];
-#pragma unroll
-      for (int st = 0; st < S; ++st) acc[st] = vec4<T>{T(0), T(0), T(0), T(0)};
-#pragma unroll
-      for (int ni = 0; ni < NB; ++ni)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const T a = Wk[(16 * ni + drow<T>(g, r)) * H + no * 16 + el];
-#pragma unroll
-          for (int st = 0; st < S; ++st) acc[st] = mfma(a, act[st][ni][r], acc[st]);
-        }
-#pragma unroll
-      for (int st = 0; st < S; ++st)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) nxt[st][no][r] = silu<T>(acc[st][r]);
-    }
+    T z[S][NB][4];
+    hidden<T, H, S>(lane, pk + L.fh + (int64_t)(layer - 1) * NB * kWave * S4, act, z);
 #pragma unroll
     for (int st = 0; st < S; ++st)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) act[st][nb][r] = nxt[st][nb][r];
+        for (int r = 0; r < 4; ++r) act[st][nb][r] = silu<T>(z[st][nb][r]);
   }
-  // last layer: R[e][c] for 16 columns per block
-  const T* __restrict__ WL = W.w[NH];
-  const int nblk = (pc + 15) / 16;
-  for (int cb = 0; cb < nblk; ++cb) {
-    const int col = cb * 16 + el;
-    const bool col_ok = col < pc;
+
+  // last layer, one 16-column block at a time; lane holds
+  // R[e0 + st*16 + el][cb*16 + row(g, r)]
+  const T* __restrict__ wl = pk + L.fl + lane * S4;
+  const int nblk = L.nblk;
+  auto load = [&](int cb, vec4<T>(&w)[NB]) {
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni) w[ni] = ld4(wl + (int64_t)cb * kWave * S4 + 4 * ni);
+  };
+  auto block = [&](int cb, const vec4<T>(&w)[NB]) {
     vec4<T> acc[S];
 #pragma unroll
-    for (int st = 0; st < S; ++st) acc[st] = vec4<T>{T(0), T(0), T(0), T(0)};
+    for (int st = 0; st < S; ++st) acc[st] = zero4<T>();
 #pragma unroll
     for (int ni = 0; ni < NB; ++ni)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const T a = col_ok ? WL[(int64_t)(16 * ni + drow<T>(g, r)) * pc + col] : T(0);
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int st = 0; st < S; ++st) acc[st] = mfma(a, act[st][ni][r], acc[st]);
-      }
-    // lane holds R[e0 + st*16 + el][cb*16 + row(g, r)]
+        for (int st = 0; st < S; ++st) acc[st] = mfma(w[ni][r], act[st][ni][r], acc[st]);
 #pragma unroll
     for (int st = 0; st < S; ++st) {
       const int64_t e = e0 + st * 16 + el;
       if (e >= ne) continue;
       T* dst = R + e * (int64_t)pc + cb * 16;
-      if (std::is_same<T, float>::value && cb * 16 + 4 * g + 3 < pc && (pc % 4) == 0) {
-        *reinterpret_cast<vec4<T>*>(dst + 4 * g) = acc[st];
+      if constexpr (VEC) {
+        st4(dst + 4 * g, acc[st]);
       } else {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (cb * 16 + drow<T>(g, r) < pc) dst[drow<T>(g, r)] = acc[st][r];
       }
     }
+  };
+  // two register sets: the next block's weights load while this one runs
+  // (the last prefetch of an even count re-reads the final block, unused)
+  vec4<T> wa[NB], wb[NB];
+  load(0, wa);
+  int cb = 0;
+  for (; cb + 2 <= nblk; cb += 2) {
+    load(cb + 1, wb);
+    block(cb, wa);
+    load(cb + 2 < nblk ? cb + 2 : nblk - 1, wa);
+    block(cb + 1, wb);
   }
+  if (cb < nblk) block(cb, wa);
 }
 
 // ---------------------------------------------------------------------------
-// backward: d(ef) from dR
-template <typename T, int H, int NH, int S>
+// backward, part 1: dA[e][k] = sum_n dR[e][n] W_L[k][n].  Reduction step
+// (t, r), k-slot g covers n = 16t + 4g + r, so a lane reads four consecutive
+// dR values per strip and step block.  Output in register order per strip:
+// dA3[strip][lane][NB*4].
+template <typename T, int H, int S, bool VEC>
 __global__ void __launch_bounds__(256)
-k_radial_bwd(int64_t ne, int pc, const T* __restrict__ ef, const T* __restrict__ dR,
-             RadialWeights<T> W, T* __restrict__ d_ef) {
-  constexpr int NB = H / 16;
+k_radial_bwd_dA(int64_t ne, int pc, const T* __restrict__ dR, const T* __restrict__ pk,
+                RadialPack L, T* __restrict__ dA3) {
+  constexpr int NB = H / 16, S4 = 4 * NB;
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16, el = lane % 16;
   const int64_t e0 = (blockIdx.x * (int64_t)(blockDim.x / kWave) + threadIdx.x / kWave) * (16 * S);
   if (e0 >= ne) return;
 
-  // recompute hidden pre-activations z[layer]
-  T z[NH][S][NB][4];
-  {
-    T b[S][2];
+  // rows past the end read the last row: their columns of the product are
+  // never stored, and every other column is independent of them
+  const T* __restrict__ rowp[S];
 #pragma unroll
-    for (int st = 0; st < S; ++st) {
-      const int64_t e = e0 + st * 16 + el;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) b[st][s] = e < ne ? ef[e * 8 + 4 * s + g] : T(0);
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      T a[2];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) a[s] = W.w[0][(4 * s + g) * H + nb * 16 + el];
-#pragma unroll
-      for (int st = 0; st < S; ++st) {
-        vec4<T> acc = {T(0), T(0), T(0), T(0)};
-#pragma unroll
-        for (int s = 0; s < 2; ++s) acc = mfma(a[s], b[st][s], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) z[0][st][nb][r] = acc[r];
-      }
-    }
+  for (int st = 0; st < S; ++st) {
+    int64_t e = e0 + st * 16 + el;
+    e = e < ne ? e : ne - 1;
+    rowp[st] = dR + e * (int64_t)pc + 4 * g;
   }
-#pragma unroll
-  for (int layer = 1; layer < NH; ++layer) {
-    const T* __restrict__ Wk = W.w[layer];
-#pragma unroll
-    for (int no = 0; no < NB; ++no) {
-      vec4<T> acc[S];
-#pragma unroll
-      for (int st = 0; st < S; ++st) acc[st] = vec4<T>{T(0), T(0), T(0), T(0)};
-#pragma unroll
-      for (int ni = 0; ni < NB; ++ni)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const T a = Wk[(16 * ni + drow<T>(g, r)) * H + no * 16 + el];
-#pragma unroll
-          for (int st = 0; st < S; ++st) acc[st] = mfma(a, silu<T>(z[layer - 1][st][ni][r]), acc[st]);
-        }
-#pragma unroll
-      for (int st = 0; st < S; ++st)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) z[layer][st][no][r] = acc[st][r];
-    }
-  }
+  const T* __restrict__ wq = pk + L.bl + lane * S4;
+  const int nt = L.nblk;
 
-  // dA = dR W_L^T : D[k][e] = sum_n W_L[k][n] dR[e][n]; step (t, r) uses
-  // n = 16*t + 4*g + r so each lane reads 4 consecutive columns.
-  const T* __restrict__ WL = W.w[NH];
   vec4<T> dA[S][NB];
 #pragma unroll
   for (int st = 0; st < S; ++st)
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) dA[st][kb] = vec4<T>{T(0), T(0), T(0), T(0)};
-  const int nt = (pc + 15) / 16;
-  for (int t = 0; t < nt; ++t) {
-    const int n0 = 16 * t + 4 * g;
-    T bv[S][4];
+    for (int kb = 0; kb < NB; ++kb) dA[st][kb] = zero4<T>();
+
+  auto load = [&](int t, vec4<T>(&bv)[S], vec4<T>(&wv)[NB]) {
 #pragma unroll
     for (int st = 0; st < S; ++st) {
-      const int64_t e = e0 + st * 16 + el;
+      if constexpr (VEC) {
+        bv[st] = ld4(rowp[st] + 16 * t);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) bv[st][r] = (e < ne && n0 + r < pc) ? dR[e * (int64_t)pc + n0 + r] : T(0);
+        for (int r = 0; r < 4; ++r) bv[st][r] = (16 * t + 4 * g + r < pc) ? rowp[st][16 * t + r] : T(0);
+      }
     }
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-      T av[4];
+    for (int kb = 0; kb < NB; ++kb) wv[kb] = ld4(wq + (int64_t)t * kWave * S4 + 4 * kb);
+  };
+  auto step = [&](const vec4<T>(&bv)[S], const vec4<T>(&wv)[NB]) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        av[r] = (n0 + r < pc) ? WL[(int64_t)(kb * 16 + el) * pc + n0 + r] : T(0);
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-        for (int st = 0; st < S; ++st) dA[st][kb] = mfma(av[r], bv[st][r], dA[st][kb]);
-    }
+        for (int st = 0; st < S; ++st) dA[st][kb] = mfma(wv[kb][r], bv[st][r], dA[st][kb]);
+  };
+  vec4<T> ba[S], bb[S], wa[NB], wb[NB];
+  load(0, ba, wa);
+  int t = 0;
+  for (; t + 2 <= nt; t += 2) {
+    load(t + 1, bb, wb);
+    step(ba, wa);
+    load(t + 2 < nt ? t + 2 : nt - 1, ba, wa);
+    step(bb, wb);
   }
-  // back through the hidden layers
+  if (t < nt) step(ba, wa);
+#pragma unroll
+  for (int st = 0; st < S; ++st) {
+    const int64_t strip = e0 / 16 + st;
+    if (strip * 16 >= ne) continue;
+    T* dst = dA3 + (strip * kWave + lane) * S4;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) st4(dst + 4 * kb, dA[st][kb]);
+  }
+}
+
+// backward, part 2: recompute the hidden layers, then d(ef) from dA3.
+template <typename T, int H, int NH, int S>
+__global__ void __launch_bounds__(256)
+k_radial_bwd_mlp(int64_t ne, const T* __restrict__ ef, const T* __restrict__ dA3,
+                 const T* __restrict__ pk, RadialPack L, T* __restrict__ d_ef) {
+  constexpr int NB = H / 16, S4 = 4 * NB;
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, el = lane % 16;
+  const int64_t e0 = (blockIdx.x * (int64_t)(blockDim.x / kWave) + threadIdx.x / kWave) * (16 * S);
+  if (e0 >= ne) return;
+
+  T z[NH][S][NB][4];
+  layer0<T, H, S>(e0, ne, lane, ef, pk + L.f0, z[0]);
+#pragma unroll
+  for (int layer = 1; layer < NH; ++layer) {
+    T act[S][NB][4];
+#pragma unroll
+    for (int st = 0; st < S; ++st)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) act[st][nb][r] = silu<T>(z[layer - 1][st][nb][r]);
+    hidden<T, H, S>(lane, pk + L.fh + (int64_t)(layer - 1) * NB * kWave * S4, act, z[layer]);
+  }
+
+  vec4<T> dA[S][NB];
+#pragma unroll
+  for (int st = 0; st < S; ++st) {
+    const int64_t strip = e0 / 16 + st;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+      dA[st][kb] = strip * 16 < ne ? ld4(dA3 + (strip * kWave + lane) * S4 + 4 * kb) : zero4<T>();
+  }
 #pragma unroll
   for (int layer = NH - 1; layer >= 0; --layer) {
     T dz[S][NB][4];
@@ -275,35 +416,31 @@ k_radial_bwd(int64_t ne, int pc, const T* __restrict__ ef, const T* __restrict__
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) dz[st][kb][r] = dA[st][kb][r] * silu_dz<T>(z[layer][st][kb][r]);
-    const T* __restrict__ Wk = W.w[layer];
     if (layer > 0) {
-      // D[k'][e] = sum_k W_k[k'][k] dz[e][k], k' in H
+      // dA_prev[e][k'] = sum_k W_k[k'][k] dz[e][k]
+      T nxt[S][NB][4];
+      hidden<T, H, S>(lane, pk + L.bh + (int64_t)(layer - 1) * NB * kWave * S4, dz, nxt);
 #pragma unroll
-      for (int ko = 0; ko < NB; ++ko) {
+      for (int st = 0; st < S; ++st)
 #pragma unroll
-        for (int st = 0; st < S; ++st) dA[st][ko] = vec4<T>{T(0), T(0), T(0), T(0)};
+        for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-        for (int ni = 0; ni < NB; ++ni)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const T a = Wk[(ko * 16 + el) * H + 16 * ni + drow<T>(g, r)];
-#pragma unroll
-            for (int st = 0; st < S; ++st) dA[st][ko] = mfma(a, dz[st][ni][r], dA[st][ko]);
-          }
-      }
+          for (int r = 0; r < 4; ++r) dA[st][kb][r] = nxt[st][kb][r];
     } else {
-      // d(ef)[e][k'] for k' < 8: rows 8..15 of the MFMA tile are zero
+      // d(ef)[e][k'] for k' < 8 (rows 8..15 of the tile carry zero weights)
+      const T* __restrict__ w = pk + L.b0 + lane * S4;
+      vec4<T> wv[NB];
+#pragma unroll
+      for (int ni = 0; ni < NB; ++ni) wv[ni] = ld4(w + 4 * ni);
       vec4<T> acc[S];
 #pragma unroll
-      for (int st = 0; st < S; ++st) acc[st] = vec4<T>{T(0), T(0), T(0), T(0)};
+      for (int st = 0; st < S; ++st) acc[st] = zero4<T>();
 #pragma unroll
       for (int ni = 0; ni < NB; ++ni)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const T a = el < 8 ? Wk[el * H + 16 * ni + drow<T>(g, r)] : T(0);
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int st = 0; st < S; ++st) acc[st] = mfma(a, dz[st][ni][r], acc[st]);
-        }
+          for (int st = 0; st < S; ++st) acc[st] = mfma(wv[ni][r], dz[st][ni][r], acc[st]);
 #pragma unroll
       for (int st = 0; st < S; ++st) {
         const int64_t e = e0 + st * 16 + el;
@@ -316,46 +453,90 @@ k_radial_bwd(int64_t ne, int pc, const T* __restrict__ ef, const T* __restrict__
   }
 }
 
+constexpr int kFwdStrips = 4, kBwdStrips = 4, kMlpStrips = 2;
+
 template <typename T, int H, int NH>
-hipError_t radial_fwd_impl(int64_t ne, int pc, const void* ef, const RadialWeights<T>& W, void* R,
-                           hipStream_t s) {
-  constexpr int S = 4;
-  const int64_t per_block = 4 * 16 * S;
-  k_radial_fwd<T, H, NH, S><<<(unsigned)((ne + per_block - 1) / per_block), 256, 0, s>>>(
-      ne, pc, static_cast<const T*>(ef), W, static_cast<T*>(R));
+hipError_t fwd_impl(int64_t ne, int pc, const T* ef, const T* pk, const RadialPack& L, T* R,
+                    hipStream_t s) {
+  const int64_t per_block = 4 * 16 * kFwdStrips;
+  const unsigned blocks = (unsigned)((ne + per_block - 1) / per_block);
+  const bool vec = std::is_same<T, float>::value && pc % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(R) % 16 == 0;
+  if (vec)
+    k_radial_fwd<T, H, NH, kFwdStrips, true><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
+  else
+    k_radial_fwd<T, H, NH, kFwdStrips, false><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
+  return hipGetLastError();
+}
+
+template <typename T, int H>
+hipError_t bwd_dA_impl(int64_t ne, int pc, const T* dR, const T* pk, const RadialPack& L, T* dA3,
+                       hipStream_t s) {
+  const int64_t per_block = 4 * 16 * kBwdStrips;
+  const unsigned blocks = (unsigned)((ne + per_block - 1) / per_block);
+  // the vector path reads whole 16-column blocks of every row
+  const bool vec = pc % 16 == 0 && reinterpret_cast<uintptr_t>(dR) % 16 == 0;
+  if (vec)
+    k_radial_bwd_dA<T, H, kBwdStrips, true><<<blocks, 256, 0, s>>>(ne, pc, dR, pk, L, dA3);
+  else
+    k_radial_bwd_dA<T, H, kBwdStrips, false><<<blocks, 256, 0, s>>>(ne, pc, dR, pk, L, dA3);
   return hipGetLastError();
 }
 
 template <typename T, int H, int NH>
-hipError_t radial_bwd_impl(int64_t ne, int pc, const void* ef, const void* dR,
-                           const RadialWeights<T>& W, void* d_ef, hipStream_t s) {
-  constexpr int S = 2;
-  const int64_t per_block = 4 * 16 * S;
-  k_radial_bwd<T, H, NH, S><<<(unsigned)((ne + per_block - 1) / per_block), 256, 0, s>>>(
-      ne, pc, static_cast<const T*>(ef), static_cast<const T*>(dR), W, static_cast<T*>(d_ef));
+hipError_t bwd_mlp_impl(int64_t ne, const T* ef, const T* dA3, const T* pk, const RadialPack& L,
+                        T* d_ef, hipStream_t s) {
+  const int64_t per_block = 4 * 16 * kMlpStrips;
+  k_radial_bwd_mlp<T, H, NH, kMlpStrips><<<(unsigned)((ne + per_block - 1) / per_block), 256, 0, s>>>(
+      ne, ef, dA3, pk, L, d_ef);
   return hipGetLastError();
+}
+
+#define TPC_RADIAL_SHAPES(X) X(16, 1) X(16, 2) X(16, 3) X(32, 1) X(32, 2) X(32, 3) X(64, 1) X(64, 2) X(64, 3)
+
+template <typename T>
+hipError_t fwd_dispatch(const RadialPack& L, int64_t ne, const void* ef, const void* pk, void* R,
+                        hipStream_t s) {
+#define TPC_CASE(HH, NN)                                                                       \
+  if (L.H == HH && L.NH == NN)                                                                 \
+    return fwd_impl<T, HH, NN>(ne, L.pc, static_cast<const T*>(ef), static_cast<const T*>(pk), L, \
+                               static_cast<T*>(R), s);
+  TPC_RADIAL_SHAPES(TPC_CASE)
+#undef TPC_CASE
+  return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t radial_dispatch(bool fwd, int H, int NH, int64_t ne, int pc, const void* ef,
-                           const void* dR, const void* const* w, void* out, hipStream_t s) {
-  RadialWeights<T> W{};
-  for (int k = 0; k <= NH; ++k) W.w[k] = static_cast<const T*>(w[k]);
-#define TPC_RADIAL_CASE(HH, NN)                                             \
-  if (H == HH && NH == NN)                                                  \
-    return fwd ? radial_fwd_impl<T, HH, NN>(ne, pc, ef, W, out, s)          \
-               : radial_bwd_impl<T, HH, NN>(ne, pc, ef, dR, W, out, s);
-  TPC_RADIAL_CASE(16, 1)
-  TPC_RADIAL_CASE(16, 2)
-  TPC_RADIAL_CASE(16, 3)
-  TPC_RADIAL_CASE(32, 1)
-  TPC_RADIAL_CASE(32, 2)
-  TPC_RADIAL_CASE(32, 3)
-  TPC_RADIAL_CASE(64, 1)
-  TPC_RADIAL_CASE(64, 2)
-  TPC_RADIAL_CASE(64, 3)
-#undef TPC_RADIAL_CASE
+hipError_t bwd_dA_dispatch(const RadialPack& L, int64_t ne, const void* dR, const void* pk, void* dA3,
+                           hipStream_t s) {
+  const T* d = static_cast<const T*>(dR);
+  const T* p = static_cast<const T*>(pk);
+  T* o = static_cast<T*>(dA3);
+  if (L.H == 16) return bwd_dA_impl<T, 16>(ne, L.pc, d, p, L, o, s);
+  if (L.H == 32) return bwd_dA_impl<T, 32>(ne, L.pc, d, p, L, o, s);
+  if (L.H == 64) return bwd_dA_impl<T, 64>(ne, L.pc, d, p, L, o, s);
   return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t bwd_mlp_dispatch(const RadialPack& L, int64_t ne, const void* ef, const void* dA3,
+                            const void* pk, void* d_ef, hipStream_t s) {
+#define TPC_CASE(HH, NN)                                                                  \
+  if (L.H == HH && L.NH == NN)                                                            \
+    return bwd_mlp_impl<T, HH, NN>(ne, static_cast<const T*>(ef), static_cast<const T*>(dA3), \
+                                   static_cast<const T*>(pk), L, static_cast<T*>(d_ef), s);
+  TPC_RADIAL_SHAPES(TPC_CASE)
+#undef TPC_CASE
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t pack_impl(const RadialPack& L, const void* const* w, void* pk, hipStream_t s) {
+  RadialWeights<T> W{};
+  for (int k = 0; k <= L.NH; ++k) W.w[k] = static_cast<const T*>(w[k]);
+  const int64_t blocks = (L.total + 255) / 256;
+  k_radial_pack<T><<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, s>>>(L, W, static_cast<T*>(pk));
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -364,18 +545,29 @@ bool radial_supported(int H, int NH) {
   return (H == 16 || H == 32 || H == 64) && NH >= 1 && NH <= 3;
 }
 
-hipError_t launch_radial_fwd(int dtype, int H, int NH, int64_t ne, int pc, const void* ef,
-                             const void* const* w, void* R, hipStream_t s) {
-  if (ne <= 0) return hipSuccess;
-  return dtype == 1 ? radial_dispatch<double>(true, H, NH, ne, pc, ef, nullptr, w, R, s)
-                    : radial_dispatch<float>(true, H, NH, ne, pc, ef, nullptr, w, R, s);
+hipError_t launch_radial_pack(int dtype, const RadialPack& L, const void* const* w, void* pk,
+                              hipStream_t s) {
+  return dtype == 1 ? pack_impl<double>(L, w, pk, s) : pack_impl<float>(L, w, pk, s);
 }
 
-hipError_t launch_radial_bwd(int dtype, int H, int NH, int64_t ne, int pc, const void* ef,
-                             const void* dR, const void* const* w, void* d_ef, hipStream_t s) {
+hipError_t launch_radial_fwd(int dtype, const RadialPack& L, int64_t ne, const void* ef,
+                             const void* pk, void* R, hipStream_t s) {
   if (ne <= 0) return hipSuccess;
-  return dtype == 1 ? radial_dispatch<double>(false, H, NH, ne, pc, ef, dR, w, d_ef, s)
-                    : radial_dispatch<float>(false, H, NH, ne, pc, ef, dR, w, d_ef, s);
+  return dtype == 1 ? fwd_dispatch<double>(L, ne, ef, pk, R, s) : fwd_dispatch<float>(L, ne, ef, pk, R, s);
+}
+
+hipError_t launch_radial_bwd_dA(int dtype, const RadialPack& L, int64_t ne, const void* dR,
+                                const void* pk, void* dA3, hipStream_t s) {
+  if (ne <= 0) return hipSuccess;
+  return dtype == 1 ? bwd_dA_dispatch<double>(L, ne, dR, pk, dA3, s)
+                    : bwd_dA_dispatch<float>(L, ne, dR, pk, dA3, s);
+}
+
+hipError_t launch_radial_bwd_mlp(int dtype, const RadialPack& L, int64_t ne, const void* ef,
+                                 const void* dA3, const void* pk, void* d_ef, hipStream_t s) {
+  if (ne <= 0) return hipSuccess;
+  return dtype == 1 ? bwd_mlp_dispatch<double>(L, ne, ef, dA3, pk, d_ef, s)
+                    : bwd_mlp_dispatch<float>(L, ne, ef, dA3, pk, d_ef, s);
 }
 
 }  // namespace tpc
