@@ -45,6 +45,20 @@ KERNEL_SOURCES = {
 }
 
 
+# Symbol fragment of each timed kernel, to find its dispatches in rocprofv3 output.
+KERNEL_SYMBOLS = {
+    "tp_fwd": "k_tp_fwd<",
+    "tp_bwd_edge": "k_tp_bwd_edge<",
+    "dh_gather": "k_dh_gather<",
+    "radial_fwd": "k_radial_fwd<",
+    "radial_bwd_dA": "k_radial_bwd_dA<",
+    "radial_bwd_mlp": "k_radial_bwd_mlp<",
+    "geom_fwd": "k_geom_fwd<",
+    "geom_bwd": "k_geom_bwd<",
+}
+COPY_PROBE_BYTES = 1 << 30   # one plain device-to-device copy of this size calibrates the counters
+
+
 def source_hash(kernel):
     h = hashlib.sha256()
     for f in KERNEL_SOURCES.get(kernel, []):
@@ -116,6 +130,62 @@ def measured_traffic(kernel):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(directory):
+    """(kernel name, dispatch id, counter, value) from every rocprofv3
+    counter_collection.csv under ``directory``."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                k = {key.lower(): v for key, v in r.items()}
+                rows.append((k.get("kernel_name", ""), k.get("dispatch_id", ""), k.get("counter_name", ""),
+                             float(k.get("counter_value", "nan"))))
+    return rows
+
+
+def _per_dispatch(rows, counter):
+    acc = {}
+    for name, did, cname, v in rows:
+        if cname == counter:
+            key = (name, did)
+            acc[key] = acc.get(key, 0.0) + v
+    return acc
+
+
+def traffic_from(fetch_dir, write_dir, out_path):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, both in KiB
+    per dispatch) of ``bench.py --copy-probe`` into HBM bytes per launch of
+    each kernel, each counter scaled by what it reads for a plain copy of
+    COPY_PROBE_BYTES (read once, written once)."""
+    out = {}
+    per = {}
+    for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        disp = _per_dispatch(_counter_rows(d), counter)
+        copies = sorted((v for (name, _), v in disp.items() if "copy" in name.lower()), reverse=True)[:3]
+        if not copies:
+            raise SystemExit(f"no copy-kernel dispatch with {counter} under {d}")
+        copy_kib = sorted(copies)[len(copies) // 2]
+        factor = COPY_PROBE_BYTES / (copy_kib * 1024.0)
+        out[f"_{label}_calibration"] = {"counter": counter, "copy_bytes": COPY_PROBE_BYTES,
+                                        "copy_counter_kib": copy_kib, "factor": factor}
+        for kernel, sym in KERNEL_SYMBOLS.items():
+            vals = [v for (name, _), v in disp.items() if sym in name]
+            if vals:
+                per.setdefault(kernel, {})[label] = (sum(vals) / len(vals)) * 1024.0 * factor
+                per[kernel][label + "_dispatches"] = len(vals)
+    for kernel, v in per.items():
+        if "fetch" in v and "write" in v:
+            out[kernel] = {"hbm_bytes_per_launch": v["fetch"] + v["write"], "read_bytes": v["fetch"],
+                           "write_bytes": v["write"], "dispatches": v["fetch_dispatches"],
+                           "source_hash": source_hash(kernel)}
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out, indent=1, sort_keys=True))
+    return 0
+
+
 def cpu_baseline(case_data, nl_np, budget_s=15.0):
     """Oracle conv forward + backward on a sample of receiver rows (1 thread)."""
     import numpy as np
@@ -157,7 +227,15 @@ def main(argv=None):
     ap.add_argument("--workload", default="medium", choices=["medium", "small"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed steps, copy %d bytes device to device three times "
+                         "(counter calibration for rocprofv3 --pmc runs)" % COPY_PROBE_BYTES)
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc output folders and exit")
     a = ap.parse_args(argv)
+    if a.traffic_from:
+        return traffic_from(a.traffic_from[0], a.traffic_from[1],
+                            os.path.join(ROOT, "profiles", "traffic.json"))
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE={world}); "
@@ -238,6 +316,14 @@ def main(argv=None):
         r = roofline_for(n, v["avg_ms"] * 1e-3, N, E, cfg, ctx) if n in KERNEL_SOURCES else None
         kernels[n] = dict(avg_ms=round(v["avg_ms"], 4), launches_per_step=v["launches_per_step"],
                           **({"bound": r["bound"], "frac": round(r["frac"], 4)} if r else {}))
+
+    if a.copy_probe:
+        src_t = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        dst_t = torch.empty_like(src_t)
+        for _ in range(3):
+            dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        del src_t, dst_t
 
     cpu = None
     if not a.no_cpu_baseline:

@@ -222,15 +222,143 @@ __device__ __forceinline__ void hidden(int lane, const T* __restrict__ wk, const
   }
 }
 
+// Last layer R = act W_L for S strips, one 16-column block at a time, with
+// the next block's weights loading while the current block runs (the final
+// prefetch of an even block count re-reads the last block, unused).  Lane
+// (g, el) holds R[e0 + st*16 + el][cb*16 + row(g, r)].  Used for float64,
+// for widths that are not a multiple of 32 and for the last, partial wave.
+template <typename T, int H, int S, bool VEC, bool FULL>
+__device__ __forceinline__ void radial_last(int64_t e0, int64_t ne, int pc, int lane,
+                                            const T* __restrict__ wl, int nblk,
+                                            const T (&act)[S][H / 16][4], T* __restrict__ R) {
+  constexpr int NB = H / 16, S4 = 4 * NB;
+  const int g = lane / 16, el = lane % 16;
+  wl += lane * S4;
+  T* rowp[S];
+#pragma unroll
+  for (int st = 0; st < S; ++st) rowp[st] = R + (e0 + st * 16 + el) * (int64_t)pc;
+  auto load = [&](int cb, vec4<T>(&w)[NB]) {
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni) w[ni] = ld4(wl + (int64_t)cb * kWave * S4 + 4 * ni);
+  };
+  auto block = [&](int cb, const vec4<T>(&w)[NB]) {
+    vec4<T> acc[S];
+#pragma unroll
+    for (int st = 0; st < S; ++st) acc[st] = zero4<T>();
+#pragma unroll
+    for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int st = 0; st < S; ++st) acc[st] = mfma(w[ni][r], act[st][ni][r], acc[st]);
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+      if (!FULL && e0 + st * 16 + el >= ne) continue;
+      T* dst = rowp[st] + cb * 16;
+      if constexpr (VEC) {
+        st4(dst + 4 * g, acc[st]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (cb * 16 + drow<T>(g, r) < pc) dst[drow<T>(g, r)] = acc[st][r];
+      }
+    }
+  };
+  vec4<T> wa[NB], wb[NB];
+  load(0, wa);
+  int cb = 0;
+  for (; cb + 2 <= nblk; cb += 2) {
+    load(cb + 1, wb);
+    block(cb, wa);
+    load(cb + 2 < nblk ? cb + 2 : nblk - 1, wa);
+    block(cb + 1, wb);
+  }
+  if (cb < nblk) block(cb, wa);
+}
+
+// Rotate each 16-lane row of the wave by 8 lanes (DPP row_ror:8).
+__device__ __forceinline__ float row_swap8(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+}
+
+// Float32 last layer for full waves and widths that are a multiple of 32:
+// column blocks go in pairs (one 128-byte line per row).  Before storing, the
+// upper half of every 16-lane row of block c trades places with the lower
+// half of block c+1, so lanes el < 8 hold the whole line of row el and the
+// others the whole line of row el + 8 after the other store: every store
+// writes 8 rows x 128 bytes.  R is written once and read much later, so the
+// stores are non-temporal.
+template <int H, int S>
+__device__ __forceinline__ void radial_last_pairs(int64_t e0, int pc, int lane, const float* __restrict__ wl,
+                                                  int nblk, const float (&act)[S][H / 16][4],
+                                                  float* __restrict__ R) {
+  constexpr int NB = H / 16, S4 = 4 * NB;
+  const int g = lane / 16, el = lane % 16;
+  const bool lo = el < 8;
+  wl += lane * S4;
+  float* rowp[S];
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+    rowp[st] = R + (e0 + st * 16 + (el & 7)) * (int64_t)pc + (lo ? 0 : 16) + 4 * g;
+  auto load = [&](int cb, f32x4(&w)[2][NB]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int ni = 0; ni < NB; ++ni) w[c][ni] = ld4(wl + (int64_t)(cb + c) * kWave * S4 + 4 * ni);
+  };
+  auto pair = [&](int cb, const f32x4(&w)[2][NB]) {
+    f32x4 acc[2][S];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int st = 0; st < S; ++st) acc[c][st] = zero4<float>();
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int ni = 0; ni < NB; ++ni)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int st = 0; st < S; ++st) acc[c][st] = mfma(w[c][ni][r], act[st][ni][r], acc[c][st]);
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+      f32x4 X, Y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = acc[0][st][r], y = acc[1][st][r];
+        const float xs = row_swap8(x), ys = row_swap8(y);
+        X[r] = lo ? x : ys;
+        Y[r] = lo ? xs : y;
+      }
+      float* dst = rowp[st] + cb * 16;
+      __builtin_nontemporal_store(X, reinterpret_cast<f32x4*>(dst));
+      __builtin_nontemporal_store(Y, reinterpret_cast<f32x4*>(dst + 8 * (int64_t)pc));
+    }
+  };
+  const int np = nblk / 2;
+  f32x4 wa[2][NB], wb[2][NB];
+  load(0, wa);
+  int q = 0;
+  for (; q + 2 <= np; q += 2) {
+    load(2 * (q + 1), wb);
+    pair(2 * q, wa);
+    load(2 * (q + 2 < np ? q + 2 : np - 1), wa);
+    pair(2 * (q + 1), wb);
+  }
+  if (q < np) pair(2 * q, wa);
+}
+
 // ---------------------------------------------------------------------------
 // forward
-template <typename T, int H, int NH, int S, bool VEC>
+// VEC: 16-byte stores of whole 16-column blocks (float32, width a multiple
+// of 16); PAIRS: width also a multiple of 32, full waves use the paired
+// line-wide stores.
+template <typename T, int H, int NH, int S, bool VEC, bool PAIRS>
 __global__ void __launch_bounds__(256)
 k_radial_fwd(int64_t ne, int pc, const T* __restrict__ ef, const T* __restrict__ pk, RadialPack L,
              T* __restrict__ R) {
   constexpr int NB = H / 16, S4 = 4 * NB;
   const int lane = threadIdx.x % kWave;
-  const int g = lane / 16, el = lane % 16;
   const int64_t e0 = (blockIdx.x * (int64_t)(blockDim.x / kWave) + threadIdx.x / kWave) * (16 * S);
   if (e0 >= ne) return;
 
@@ -254,50 +382,17 @@ k_radial_fwd(int64_t ne, int pc, const T* __restrict__ ef, const T* __restrict__
         for (int r = 0; r < 4; ++r) act[st][nb][r] = silu<T>(z[st][nb][r]);
   }
 
-  // last layer, one 16-column block at a time; lane holds
-  // R[e0 + st*16 + el][cb*16 + row(g, r)]
-  const T* __restrict__ wl = pk + L.fl + lane * S4;
-  const int nblk = L.nblk;
-  auto load = [&](int cb, vec4<T>(&w)[NB]) {
-#pragma unroll
-    for (int ni = 0; ni < NB; ++ni) w[ni] = ld4(wl + (int64_t)cb * kWave * S4 + 4 * ni);
-  };
-  auto block = [&](int cb, const vec4<T>(&w)[NB]) {
-    vec4<T> acc[S];
-#pragma unroll
-    for (int st = 0; st < S; ++st) acc[st] = zero4<T>();
-#pragma unroll
-    for (int ni = 0; ni < NB; ++ni)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int st = 0; st < S; ++st) acc[st] = mfma(w[ni][r], act[st][ni][r], acc[st]);
-#pragma unroll
-    for (int st = 0; st < S; ++st) {
-      const int64_t e = e0 + st * 16 + el;
-      if (e >= ne) continue;
-      T* dst = R + e * (int64_t)pc + cb * 16;
-      if constexpr (VEC) {
-        st4(dst + 4 * g, acc[st]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (cb * 16 + drow<T>(g, r) < pc) dst[drow<T>(g, r)] = acc[st][r];
-      }
-    }
-  };
-  // two register sets: the next block's weights load while this one runs
-  // (the last prefetch of an even count re-reads the final block, unused)
-  vec4<T> wa[NB], wb[NB];
-  load(0, wa);
-  int cb = 0;
-  for (; cb + 2 <= nblk; cb += 2) {
-    load(cb + 1, wb);
-    block(cb, wa);
-    load(cb + 2 < nblk ? cb + 2 : nblk - 1, wa);
-    block(cb + 1, wb);
+  // Full waves store without tests, so the wait before each block covers only
+  // that block's weight loads and never stores still in flight; the last,
+  // partial wave checks each row.
+  if (e0 + 16 * S <= ne) {
+    if constexpr (PAIRS)
+      radial_last_pairs<H, S>(e0, pc, lane, pk + L.fl, L.nblk, act, R);
+    else
+      radial_last<T, H, S, VEC, true>(e0, ne, pc, lane, pk + L.fl, L.nblk, act, R);
+  } else {
+    radial_last<T, H, S, VEC, false>(e0, ne, pc, lane, pk + L.fl, L.nblk, act, R);
   }
-  if (cb < nblk) block(cb, wa);
 }
 
 // ---------------------------------------------------------------------------
@@ -333,37 +428,65 @@ k_radial_bwd_dA(int64_t ne, int pc, const T* __restrict__ dR, const T* __restric
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb) dA[st][kb] = zero4<T>();
 
-  auto load = [&](int t, vec4<T>(&bv)[S], vec4<T>(&wv)[NB]) {
+  // CB step blocks per stage: with two, a row's 128-byte line is read by two
+  // back-to-back loads
+  constexpr int CB = VEC ? 2 : 1;
+  auto load = [&](int t, vec4<T>(&bv)[CB][S], vec4<T>(&wv)[CB][NB]) {
 #pragma unroll
-    for (int st = 0; st < S; ++st) {
-      if constexpr (VEC) {
-        bv[st] = ld4(rowp[st] + 16 * t);
-      } else {
+    for (int st = 0; st < S; ++st)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bv[st][r] = (16 * t + 4 * g + r < pc) ? rowp[st][16 * t + r] : T(0);
+      for (int c = 0; c < CB; ++c) {
+        if constexpr (VEC) {
+          bv[c][st] = ld4(rowp[st] + 16 * (t + c));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            bv[c][st][r] = (16 * (t + c) + 4 * g + r < pc) ? rowp[st][16 * (t + c) + r] : T(0);
+        }
       }
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) wv[c][kb] = ld4(wq + (int64_t)(t + c) * kWave * S4 + 4 * kb);
+  };
+  auto step = [&](const vec4<T>(&bv)[CB][S], const vec4<T>(&wv)[CB][NB]) {
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+          for (int st = 0; st < S; ++st) dA[st][kb] = mfma(wv[c][kb][r], bv[c][st][r], dA[st][kb]);
+  };
+  const int nst = nt / CB;
+  vec4<T> ba[CB][S], bb[CB][S], wa[CB][NB], wb[CB][NB];
+  int q = 0;
+  if (nst > 0) {
+    load(0, ba, wa);
+    for (; q + 2 <= nst; q += 2) {
+      load((q + 1) * CB, bb, wb);
+      step(ba, wa);
+      load((q + 2 < nst ? q + 2 : nst - 1) * CB, ba, wa);
+      step(bb, wb);
     }
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb) wv[kb] = ld4(wq + (int64_t)t * kWave * S4 + 4 * kb);
-  };
-  auto step = [&](const vec4<T>(&bv)[S], const vec4<T>(&wv)[NB]) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int st = 0; st < S; ++st) dA[st][kb] = mfma(wv[kb][r], bv[st][r], dA[st][kb]);
-  };
-  vec4<T> ba[S], bb[S], wa[NB], wb[NB];
-  load(0, ba, wa);
-  int t = 0;
-  for (; t + 2 <= nt; t += 2) {
-    load(t + 1, bb, wb);
-    step(ba, wa);
-    load(t + 2 < nt ? t + 2 : nt - 1, ba, wa);
-    step(bb, wb);
+    if (q < nst) step(ba, wa);
   }
-  if (t < nt) step(ba, wa);
+  if constexpr (CB > 1) {
+    if (nst * CB < nt) {  // odd block count: the last block alone
+      vec4<T> b1[1][S], w1[1][NB];
+#pragma unroll
+      for (int st = 0; st < S; ++st) b1[0][st] = ld4(rowp[st] + 16 * (nt - 1));
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) w1[0][kb] = ld4(wq + (int64_t)(nt - 1) * kWave * S4 + 4 * kb);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+          for (int st = 0; st < S; ++st) dA[st][kb] = mfma(w1[0][kb][r], b1[0][st][r], dA[st][kb]);
+    }
+  }
 #pragma unroll
   for (int st = 0; st < S; ++st) {
     const int64_t strip = e0 / 16 + st;
@@ -453,7 +576,11 @@ k_radial_bwd_mlp(int64_t ne, const T* __restrict__ ef, const T* __restrict__ dA3
   }
 }
 
-constexpr int kFwdStrips = 4, kBwdStrips = 4, kMlpStrips = 2;
+constexpr int kFwdStrips = 4, kMlpStrips = 2;
+// the backward product keeps only its accumulators live: 8 strips of 16
+// edges in float32 (128 accumulator registers), 2 in float64
+template <typename T>
+constexpr int kBwdStrips = std::is_same<T, float>::value ? 8 : 2;
 
 template <typename T, int H, int NH>
 hipError_t fwd_impl(int64_t ne, int pc, const T* ef, const T* pk, const RadialPack& L, T* R,
@@ -462,24 +589,30 @@ hipError_t fwd_impl(int64_t ne, int pc, const T* ef, const T* pk, const RadialPa
   const unsigned blocks = (unsigned)((ne + per_block - 1) / per_block);
   const bool vec = std::is_same<T, float>::value && pc % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(R) % 16 == 0;
+  if constexpr (std::is_same<T, float>::value) {
+    if (vec && pc % 32 == 0) {
+      k_radial_fwd<T, H, NH, kFwdStrips, true, true><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
+      return hipGetLastError();
+    }
+  }
   if (vec)
-    k_radial_fwd<T, H, NH, kFwdStrips, true><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
+    k_radial_fwd<T, H, NH, kFwdStrips, true, false><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
   else
-    k_radial_fwd<T, H, NH, kFwdStrips, false><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
+    k_radial_fwd<T, H, NH, kFwdStrips, false, false><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
   return hipGetLastError();
 }
 
 template <typename T, int H>
 hipError_t bwd_dA_impl(int64_t ne, int pc, const T* dR, const T* pk, const RadialPack& L, T* dA3,
                        hipStream_t s) {
-  const int64_t per_block = 4 * 16 * kBwdStrips;
+  const int64_t per_block = 4 * 16 * kBwdStrips<T>;
   const unsigned blocks = (unsigned)((ne + per_block - 1) / per_block);
   // the vector path reads whole 16-column blocks of every row
   const bool vec = pc % 16 == 0 && reinterpret_cast<uintptr_t>(dR) % 16 == 0;
   if (vec)
-    k_radial_bwd_dA<T, H, kBwdStrips, true><<<blocks, 256, 0, s>>>(ne, pc, dR, pk, L, dA3);
+    k_radial_bwd_dA<T, H, kBwdStrips<T>, true><<<blocks, 256, 0, s>>>(ne, pc, dR, pk, L, dA3);
   else
-    k_radial_bwd_dA<T, H, kBwdStrips, false><<<blocks, 256, 0, s>>>(ne, pc, dR, pk, L, dA3);
+    k_radial_bwd_dA<T, H, kBwdStrips<T>, false><<<blocks, 256, 0, s>>>(ne, pc, dR, pk, L, dA3);
   return hipGetLastError();
 }
 
