@@ -82,12 +82,14 @@ def algorithmic(kernel, N, E, cfg, ctx):
         return (E * (T * PC + T * dsh) + N * T * C * (din + dout) + csr,
                 E * (2 * nnz + C * (2 * m13 + 2 * dout)))
     if kernel == "tp_bwd_edge":
-        # reads R, Y, h (once per atom), G (once per atom); writes dR, dY and
-        # the per-edge dh contributions
-        return (E * (2 * T * PC + 2 * T * dsh + T * C * din) + N * T * C * (din + dout) + csr,
+        # reads R, Y, h and G (once per atom); writes dR and dY.  The per-edge
+        # dh contributions it also writes are an intermediate of the two-kernel
+        # split, not algorithmic traffic.
+        return (E * (2 * T * PC + 2 * T * dsh) + N * T * C * (din + dout) + csr,
                 E * C * (2 * nnz + 4 * m13 + 2 * din + 2 * dout))
     if kernel == "dh_gather":
-        return (E * T * C * din + N * T * C * din + 4 * (N + 1), E * C * din)
+        # writes dh; its reads are the split's intermediate
+        return (N * T * C * din + 4 * (N + 1), E * C * din)
     hidden = 2 * (8 * H + (NH - 1) * H * H)
     if kernel == "radial_fwd":
         return E * (8 * T + T * PC), E * (hidden + 2 * H * PC)
@@ -98,6 +100,28 @@ def algorithmic(kernel, N, E, cfg, ctx):
         # reads ef and dA, writes d(ef); recomputes the hidden layers
         return E * (8 * T + T * H + 8 * T), E * 2 * hidden
     return None, None
+
+
+def group_rooflines(per_kernel, N, E, cfg, ctx):
+    """HBM fraction of the fused tensor-product passes, each taken as the
+    kernels that make it up: K8 = tp_fwd; K9 = tp_bwd_edge + dh_gather, whose
+    algorithmic bytes are R, Y, h, G and the CSR in, dR, dY and dh out."""
+    T = 4
+    C, PC, din, dsh, dout = cfg["C"], ctx.r_width, ctx.d_in, ctx.d_sh, ctx.d_out
+    csr = 4 * (N + 1) + 4 * E
+    groups = {
+        "K8_tp_forward": (["tp_fwd"], E * (T * PC + T * dsh) + N * T * C * (din + dout) + csr),
+        "K9_tp_backward": (["tp_bwd_edge", "dh_gather"],
+                           E * (2 * T * PC + 2 * T * dsh) + N * T * C * (2 * din + dout) + csr),
+    }
+    out = {}
+    for name, (ks, nbytes) in groups.items():
+        if not all(k in per_kernel for k in ks):
+            continue
+        sec = sum(per_kernel[k]["avg_ms"] for k in ks) * 1e-3
+        out[name] = dict(kernels=ks, algorithmic_bytes=nbytes, ms=sec * 1e3,
+                         achieved_GBps=nbytes / sec / 1e9, frac=nbytes / sec / HBM_PEAK)
+    return out
 
 
 def roofline_for(kernel, per_launch_s, N, E, cfg, ctx):
@@ -356,6 +380,7 @@ def main(argv=None):
         "fwd_bwd_edges_per_s": E / ((fwd_ms + bwd_ms) * 1e-3) if fwd_ms else None,
         "nbr_build_ms": nbr_ms,
         "kernels": kernels,
+        "tp_groups_hbm": group_rooflines(per_kernel, N, E, cfg, ctx),
         "wall_s": wall,
     }
     print(json.dumps(line), flush=True)

@@ -22,6 +22,18 @@ __host__ __device__ __forceinline__ void static_for(F&& f) {
 // Value that is the same in every lane of the wave, kept in a scalar register.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Block index for row-streaming kernels on the 8 XCDs of the chip.  Blocks
+// go to the XCDs round-robin (block b to XCD b % 8), and each XCD has its own
+// L2.  This bijection on [0, gridDim.x) gives XCD x one contiguous range of
+// logical blocks, so the rows it works on at any moment are neighbours and
+// their shared sender data stays in that XCD's L2.
+__device__ __forceinline__ int64_t xcd_block() {
+  constexpr int64_t kXcds = 8;
+  const int64_t nb = gridDim.x, b = blockIdx.x;
+  const int64_t q = nb / kXcds, r = nb % kXcds, x = b % kXcds, k = b / kXcds;
+  return x * q + (x < r ? x : r) + k;
+}
+
 // Launch status from the HIP runtime after a kernel launch.
 inline hipError_t launch_status() { return hipGetLastError(); }
 

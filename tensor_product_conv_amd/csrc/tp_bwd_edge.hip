@@ -26,18 +26,28 @@ hipError_t launch_tp_bwd_edge(int dtype, int L1, int L2, int L3, const TPArgs& a
   return hipErrorInvalidValue;
 }
 
+template <typename T, int V>
+hipError_t dh_gather_impl(int64_t n, int din_c, const int32_t* row_ptr, double scale,
+                          const void* dh_edge, void* dh, hipStream_t s) {
+  const int64_t total = n * (din_c / V);
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  k_dh_gather<T, V><<<blocks, 256, 0, s>>>(n, din_c, row_ptr, (T)scale, static_cast<const T*>(dh_edge),
+                                           static_cast<T*>(dh));
+  return hipGetLastError();
+}
+
 hipError_t launch_dh_gather(int dtype, int64_t n, int din_c, const int32_t* row_ptr, double scale,
                             const void* dh_edge, void* dh, hipStream_t s) {
-  const int64_t total = n * din_c;
-  if (total <= 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (n * din_c <= 0) return hipSuccess;
+  // 16-byte vectors when every row of din_c values starts 16-byte aligned
+  const size_t tsz = dtype == 1 ? 8 : 4;
+  const bool vec = (din_c * tsz) % 16 == 0 && reinterpret_cast<uintptr_t>(dh_edge) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(dh) % 16 == 0;
   if (dtype == 1)
-    k_dh_gather<double><<<blocks, 256, 0, s>>>(n, din_c, row_ptr, scale,
-                                               static_cast<const double*>(dh_edge), static_cast<double*>(dh));
-  else
-    k_dh_gather<float><<<blocks, 256, 0, s>>>(n, din_c, row_ptr, (float)scale,
-                                              static_cast<const float*>(dh_edge), static_cast<float*>(dh));
-  return hipGetLastError();
+    return vec ? dh_gather_impl<double, 2>(n, din_c, row_ptr, scale, dh_edge, dh, s)
+               : dh_gather_impl<double, 1>(n, din_c, row_ptr, scale, dh_edge, dh, s);
+  return vec ? dh_gather_impl<float, 4>(n, din_c, row_ptr, scale, dh_edge, dh, s)
+             : dh_gather_impl<float, 1>(n, din_c, row_ptr, scale, dh_edge, dh, s);
 }
 
 }  // namespace tpc

@@ -111,7 +111,7 @@ template <int NW>
 __device__ __forceinline__ RowWave row_wave(int64_t row_begin, int64_t row_end, int C) {
   const int lane = threadIdx.x % kTPWave;
   const int wpr = NW > 0 ? NW : 1;  // waves per row
-  const int64_t w = blockIdx.x * (int64_t)kTPWavesPerBlock + threadIdx.x / kTPWave;
+  const int64_t w = xcd_block() * kTPWavesPerBlock + threadIdx.x / kTPWave;
   RowWave r;
   const int64_t row = row_begin + w / wpr;
   r.ok = row < row_end;
@@ -253,7 +253,7 @@ k_tp_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, i
          const T* __restrict__ Y, const T* __restrict__ R, T* __restrict__ out) {
   constexpr int DOUT = kTable<L1, L2, L3>.dout;
   const int lane = threadIdx.x % kTPWave;
-  const int64_t w = blockIdx.x * (int64_t)kTPWavesPerBlock + threadIdx.x / kTPWave;
+  const int64_t w = xcd_block() * kTPWavesPerBlock + threadIdx.x / kTPWave;
   const int64_t row = row_begin + w / NG;
   if (row >= row_end) return;
   const int i = uniform((int)row);
@@ -446,19 +446,34 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
 // dh[j] = s * sum over the edges e of row j of dh_edge[e]: each slot holds the
 // contribution of the reverse edge (whose sender is j), so the sum runs over a
 // contiguous range in CSR order (deterministic, no atomics).  One thread per
-// (atom, feature row, channel).
-template <typename T>
+// (atom, group of V consecutive feature values); every value is summed over
+// the row's edges in CSR order, V at a time, with four edges' loads in flight.
+template <typename T, int V>
 __global__ void __launch_bounds__(256)
 k_dh_gather(int64_t n, int din_c, const int32_t* __restrict__ row_ptr, T scale,
             const T* __restrict__ dh_edge, T* __restrict__ dh) {
+  typedef T vec __attribute__((ext_vector_type(V)));
+  const int groups = din_c / V;
   const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (t >= n * din_c) return;
-  const int64_t j = t / din_c;
-  const int q = (int)(t - j * din_c);
-  T acc = T(0);
+  if (t >= n * groups) return;
+  const int64_t j = t / groups;
+  const int q = (int)(t - j * groups) * V;
+  vec acc = vec(T(0));
   const int lo = row_ptr[j], hi = row_ptr[j + 1];
-  for (int e = lo; e < hi; ++e) acc += dh_edge[(int64_t)e * din_c + q];
-  dh[t] = scale * acc;
+  const T* __restrict__ p = dh_edge + q;
+  int e = lo;
+  for (; e + 4 <= hi; e += 4) {
+    const vec a = *reinterpret_cast<const vec*>(p + (int64_t)e * din_c);
+    const vec b = *reinterpret_cast<const vec*>(p + (int64_t)(e + 1) * din_c);
+    const vec c = *reinterpret_cast<const vec*>(p + (int64_t)(e + 2) * din_c);
+    const vec d = *reinterpret_cast<const vec*>(p + (int64_t)(e + 3) * din_c);
+    acc += a;
+    acc += b;
+    acc += c;
+    acc += d;
+  }
+  for (; e < hi; ++e) acc += *reinterpret_cast<const vec*>(p + (int64_t)e * din_c);
+  *reinterpret_cast<vec*>(dh + j * din_c + q) = scale * acc;
 }
 
 // ---------------------------------------------------------------------------
