@@ -4,36 +4,36 @@
 // correlations"; section 4 receiver-sorted kernel):
 //   out[i,(p,m3),u] = s * sum_{e in row i} R[e,p,u] * sum_{m1} M_e^p[m1,m3] h[src_e,(l1,m1),u]
 //   M_e^p[m1,m3]   = sum_{m2} C^p[m1,m2,m3] Y[e,(l2,m2)]
-// The per-edge coupling matrices M_e are built once per edge by the geometry
-// kernel and read here through scalar loads: they are the same for every
-// channel.  A wave owns one receiver row and 64 channels (one per lane); C > 64
-// uses C/64 waves per row.  The edge loop runs in CSR order, so every output
-// is a fixed-order sum held in registers and stored once: no atomics and no
-// per-edge message tensor (the receiver-streaming design of FastMACE's
-// "streaming_conv" and FlashCart's receiver-sorted kernel, on a 64-wide
-// wave).  The next edge's radial weights and sender features are loaded while
-// the current edge is computed (two register buffers).
+// The coupling coefficients are compile-time constants (tables.hpp), so the
+// sparse contraction is straight-line code; an edge's harmonics sit in scalar
+// registers and M is formed per edge from them.  A receiver row is owned by
+// NG waves, each holding the accumulators of a fixed subset of paths for 64
+// lanes x CPL channels.  The edge loop runs in CSR order with the next edge's
+// radial weights and sender features loading while the current edge is
+// computed, so every output is a fixed-order sum held in registers and stored
+// once: no atomics and no per-edge message tensor (the receiver-streaming
+// design of FastMACE's "streaming_conv" and FlashCart's receiver-sorted
+// kernel, on a 64-wide wave).
 //
 // Backward of L = sum(G * out) (FlashCart section 3 "Symbolic derivatives":
 // the weight gradient is the inner product of the incoming gradient with the
 // unweighted product; the input gradients are the other factors times the
-// weight).  With the per-channel projection
-//     Q_e^p[m2,u] = sum_{m1,m3} C^p[m1,m2,m3] h[src_e,m1,u] G[i,(p,m3),u]
-// both edge gradients follow from one contraction:
-//     dR[e,p,u]  = s * sum_{m2} Y[e,(l2,m2)] Q_e^p[m2,u]
-//     dY[e,l2m2] = s * sum_p sum_u R[e,p,u] Q_e^p[m2,u]      (channel reduction)
-// computed by the edge kernel (one wave per receiver row and 64 channels, G[i]
-// loaded once per row).  The channel reduction of dY is a wave reduce-scatter;
-// with several waves per row each writes its partial sum and the geometry
-// backward adds them in a fixed order.
-// Node kernel (one wave per atom j and 64 channels, over j's own row):
-//     dh[j,m1,u] = s * sum_{e' in row j} sum_p (-1)^{l2} R[e',p,u]
-//                      sum_{m3} M_{e'}^p[m1,m3] G[src_e',(p,m3),u]
-// It uses the symmetry of the list: the edge e = (k <- j, S) has its reverse
-// e' = (j <- k, -S) in row j, with the same length (same R) and the opposite
-// direction (Y(e) = (-1)^l2 Y(e')).  Sender gradients are therefore gathered
-// per row instead of scattered with atomics (FlashCart's VJP uses atomics
-// there) or through a sender permutation.
+// weight).  One wave per receiver row and 64 channels loads G[i] once per row;
+// per edge and path it forms K[m1][m2] = sum_m3 C^p[m1,m2,m3] G[i,(p,m3),u] and
+// from it
+//     W[m1]  = sum_m2 Y[e,(l2,m2)] K[m1][m2]
+//     dR[e,p,u] = s * sum_m1 h[src_e,m1,u] W[m1]
+//     t[m1]  += R[e,p,u] W[m1]                 (contribution to dh of the sender)
+//     Q[m2]  = sum_m1 h[src_e,m1,u] K[m1][m2]
+//     dY[e,(l2,m2)] = s * sum_u R[e,p,u] Q[m2]  (channel reduction)
+// The channel reduction of dY is a wave reduce-scatter; with several waves per
+// row each writes its partial sum and the geometry backward adds them in a
+// fixed order.  The sender contribution t is stored at the reverse edge's
+// slot: the list is symmetric, and the reverse of e = (i <- j, S) is
+// (j <- i, -S) in row j.  k_dh_gather then sums row j in CSR order,
+//     dh[j] = s * sum_{e in row j} t_stored[e],
+// so sender gradients are gathered per row instead of scattered with atomics
+// (FlashCart's VJP uses atomics there) or through a sender permutation.
 #pragma once
 
 #include "common.hpp"
