@@ -13,7 +13,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/tpconv.h"
+#include "tpconv.h"
 #include "common.hpp"
 #include "kernels.hpp"
 #include "nbr.hpp"

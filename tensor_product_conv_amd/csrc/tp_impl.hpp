@@ -66,6 +66,61 @@ __device__ __forceinline__ void stc(T* __restrict__ base, uint32_t off, bool on,
   }
 }
 
+// Value held by lane k of v, for every lane (v_readlane; k is uniform).
+__device__ __forceinline__ float lane_value(float v, int k) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), k));
+}
+__device__ __forceinline__ double lane_value(double v, int k) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, k);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), k);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Rows of at most 64 * kIdxWindows edges keep their sender (and reverse-edge)
+// indices in registers: lane k of window q holds a[e_lo + 64 q + k], and an
+// edge's index is a v_readlane away instead of a dependent memory load.
+// Longer rows take a separate loop that loads each index.
+constexpr int kIdxWindows = 2;
+
+template <int NWIN>
+struct RowIdx {
+  int v[NWIN];
+  __device__ __forceinline__ void init(const int32_t* __restrict__ a, int e_lo, int e_hi, int lane) {
+#pragma unroll
+    for (int q = 0; q < NWIN; ++q) v[q] = a[min(e_lo + 64 * q + lane, e_hi - 1)];
+  }
+  // entry of edge e_lo + k (k uniform, 0 <= k < 64 * NWIN)
+  __device__ __forceinline__ int get(int k) const {
+    int r = __builtin_amdgcn_readlane(v[0], k & 63);
+#pragma unroll
+    for (int q = 1; q < NWIN; ++q) {
+      const int t = __builtin_amdgcn_readlane(v[q], k & 63);
+      r = (k >> 6) == q ? t : r;
+    }
+    return r;
+  }
+};
+
+// compute(e, buf) over the edges [e_lo, e_hi) (non-empty) in order, with the
+// next edge's loads in flight in a second buffer.  Every prefetch is
+// unconditional (the index is clamped; the final one re-reads the last edge,
+// unused) and the loop has a single exit, so the wait before each edge covers
+// exactly that edge's loads and never the stores issued since.
+template <typename Buf, typename Load, typename Compute>
+__device__ __forceinline__ void edge_loop(int e_lo, int e_hi, Load&& load, Compute&& compute) {
+  Buf A, B;
+  load(e_lo, A);
+  int e = e_lo;
+  for (; e + 2 <= e_hi; e += 2) {
+    load(e + 1, B);
+    compute(e, A);
+    load(min(e + 2, e_hi - 1), A);
+    compute(e + 1, B);
+  }
+  if (e < e_hi) compute(e, A);
+}
+
 template <int NW>
 __device__ __forceinline__ int channels(int C) {
   if constexpr (NW > 0) {
@@ -174,12 +229,16 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
       });
     }
   });
+  // An edge's harmonics travel with its prefetch as one vector load (lane k
+  // holds Y[k]) and are broadcast with v_readlane.
   struct Buf {
     T h[DIN][CPL];
     T r[NP][CPL];
+    T y;
   };
-  auto load = [&](int e, Buf& b) {
-    const int j = uniform(src[e]);
+  const int lane = threadIdx.x % kTPWave;
+  const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
+  auto load_j = [&](int e, int j, Buf& b) {
     const T* __restrict__ hj = h + (int64_t)j * DIN * C;
     const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
 #pragma unroll
@@ -188,9 +247,12 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
       constexpr int p = decltype(pc)::value;
       if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) ld_vec<T, CPL>(re, p * C + c0, on, b.r[p], MASKED);
     });
+    b.y = Y[((int64_t)e - edge_begin) * DSH + ylane];
   };
-  auto compute = [&](int e, const Buf& b) {
-    const T* __restrict__ ye = Y + ((int64_t)e - edge_begin) * DSH;
+  auto compute = [&](int, const Buf& b) {
+    T ye[16];
+#pragma unroll
+    for (int k = 0; k < DSH; ++k) ye[k] = lane_value(b.y, k);
     static_for<NP>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
       if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) {
@@ -220,16 +282,12 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
       }
     });
   };
-  Buf A, B;
-  int e = e_lo;
-  if (e < e_hi) load(e, A);
-  while (e < e_hi) {
-    if (e + 1 < e_hi) load(e + 1, B);
-    compute(e, A);
-    if (++e >= e_hi) break;
-    if (e + 1 < e_hi) load(e + 1, A);
-    compute(e, B);
-    ++e;
+  if (e_hi - e_lo > 64 * kIdxWindows) {
+    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) { load_j(e, uniform(src[e]), b); }, compute);
+  } else if (e_hi > e_lo) {
+    RowIdx<kIdxWindows> si;
+    si.init(src, e_lo, e_hi, lane);
+    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) { load_j(e, si.get(e - e_lo), b); }, compute);
   }
   static_for<NP>([&](auto pc) {
     constexpr int p = decltype(pc)::value;
@@ -272,31 +330,68 @@ k_tp_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, i
 }
 
 // ---------------------------------------------------------------------------
-// Sum of v[0..15] over the 64 lanes of a wave, reduce-scatter style: lane l
-// with l % 4 == 0 ends with the total of entry l / 4 (17 cross-lane moves).
+// Sum of v[0..15] over the 64 lanes of a wave, reduce-scatter style: every
+// lane l ends with the total of entry l / 4 (all four lanes of a quad hold
+// it).  Each halving step pairs every lane with one in the other half of its
+// group, keeps the half of the entries that its own lane bit selects and adds
+// the partner's copy of them, so every step moves half the data.  The moves
+// stay in the vector ALU (no LDS): v_permlane32_swap across the two 32-lane
+// halves, v_permlane16_swap across 16-lane rows, then DPP within rows
+// (row_ror:8, row_half_mirror, and quad permutations for the last two steps,
+// which leave the total in all four lanes of the quad).
+__device__ __forceinline__ uint32_t u32(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)u32(x), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// (a, b) -> (a + partner's a, b + partner's b) for lanes keeping a (low half
+// of the group) / b (high half), with the two swap instructions.
+__device__ __forceinline__ float swap32_add(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(u32(a), u32(b), false, false);
+  return f32(r[0]) + f32(r[1]);
+}
+__device__ __forceinline__ float swap16_add(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(u32(a), u32(b), false, false);
+  return f32(r[0]) + f32(r[1]);
+}
+__device__ __forceinline__ double swap32_add(double a, double b) {
+  const uint64_t ua = __builtin_bit_cast(uint64_t, a), ub = __builtin_bit_cast(uint64_t, b);
+  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)ua, (uint32_t)ub, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(ua >> 32), (uint32_t)(ub >> 32), false, false);
+  const double x = __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]);
+  const double y = __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
+  return x + y;
+}
+__device__ __forceinline__ double swap16_add(double a, double b) {
+  const uint64_t ua = __builtin_bit_cast(uint64_t, a), ub = __builtin_bit_cast(uint64_t, b);
+  const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)ua, (uint32_t)ub, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(ua >> 32), (uint32_t)(ub >> 32), false, false);
+  const double x = __builtin_bit_cast(double, ((uint64_t)hi[0] << 32) | lo[0]);
+  const double y = __builtin_bit_cast(double, ((uint64_t)hi[1] << 32) | lo[1]);
+  return x + y;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_reduce_scatter16(const T (&v)[16]) {
   const int lane = threadIdx.x % kTPWave;
+  // lanes 0-31 keep entries 0-7, lanes 32-63 entries 8-15: the swap moves
+  // the upper half of a[k]'s lanes and the lower half of a[k+8]'s lanes across
   T a[8];
-  {
-    const bool hi = lane & 32;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const T send = hi ? v[k] : v[k + 8];
-      const T keep = hi ? v[k + 8] : v[k];
-      a[k] = keep + __shfl_xor(send, 32, kTPWave);
-    }
-  }
+  for (int k = 0; k < 8; ++k) a[k] = swap32_add(v[k], v[k + 8]);
+  // rows 0 and 2 keep entries (k), rows 1 and 3 entries (k + 4) of the half
   T b[4];
-  {
-    const bool hi = lane & 16;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const T send = hi ? a[k] : a[k + 4];
-      const T keep = hi ? a[k + 4] : a[k];
-      b[k] = keep + __shfl_xor(send, 16, kTPWave);
-    }
-  }
+  for (int k = 0; k < 4; ++k) b[k] = swap16_add(a[k], a[k + 4]);
+  // within a row: lanes 0-7 keep (k), lanes 8-15 keep (k + 2); partner l ^ 8
   T c[2];
   {
     const bool hi = lane & 8;
@@ -304,18 +399,19 @@ __device__ __forceinline__ T wave_reduce_scatter16(const T (&v)[16]) {
     for (int k = 0; k < 2; ++k) {
       const T send = hi ? b[k] : b[k + 2];
       const T keep = hi ? b[k + 2] : b[k];
-      c[k] = keep + __shfl_xor(send, 8, kTPWave);
+      c[k] = keep + dpp<0x128>(send);  // row_ror:8
     }
   }
+  // within 8 lanes: lanes 0-3 keep (k), lanes 4-7 keep (k + 1); partner 7 - l
   T d;
   {
     const bool hi = lane & 4;
     const T send = hi ? c[0] : c[1];
     const T keep = hi ? c[1] : c[0];
-    d = keep + __shfl_xor(send, 4, kTPWave);
+    d = keep + dpp<0x141>(send);  // row_half_mirror
   }
-  d += __shfl_xor(d, 2, kTPWave);
-  d += __shfl_xor(d, 1, kTPWave);
+  d += dpp<0x4E>(d);  // quad_perm [2,3,0,1]
+  d += dpp<0xB1>(d);  // quad_perm [1,0,3,2]
   return d;
 }
 
@@ -355,22 +451,32 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
     for (int o = 0; o < DOUT; ++o) gi[o] = ldc<NW>(gr, o * CC + c0, rw.on);
   }
 
+  // The edge's harmonics travel with the prefetch as one vector load (lane k
+  // holds Y[k]) and are broadcast with v_readlane: held in scalar registers
+  // through the whole path loop they would be re-read from memory, each
+  // re-read waiting on the scalar cache.
   struct Buf {
     T h[DIN];
     T r[NP];
+    T y;
+    int er;  // reverse edge
   };
-  auto load = [&](int e, Buf& b) {
-    const int j = uniform(src[e]);
+  const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
+  auto load_j = [&](int e, int j, int er, Buf& b) {
     const T* __restrict__ hj = h + (int64_t)j * DIN * CC;
     const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
 #pragma unroll
     for (int m = 0; m < DIN; ++m) b.h[m] = ldc<NW>(hj, m * CC + c0, rw.on);
 #pragma unroll
     for (int p = 0; p < NP; ++p) b.r[p] = ldc<NW>(re, p * CC + c0, rw.on);
+    b.y = Y[((int64_t)e - edge_begin) * DSH + ylane];
+    b.er = er;
   };
   auto compute = [&](int e, const Buf& b) {
     const int64_t el = (int64_t)e - edge_begin;
-    const T* __restrict__ ye = Y + el * DSH;
+    T ye[16];
+#pragma unroll
+    for (int k = 0; k < DSH; ++k) ye[k] = lane_value(b.y, k);
     T* __restrict__ dre = dR + el * PC;
     T dy[16];
 #pragma unroll
@@ -421,24 +527,25 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
       });
       stc<NW>(dre, p * CC + c0, rw.on, scale * dr);
     });
-    const int er = uniform(rev[e]);
-    T* __restrict__ te = dh_edge + (int64_t)er * DIN * CC;
+    T* __restrict__ te = dh_edge + (int64_t)b.er * DIN * CC;
 #pragma unroll
     for (int m = 0; m < DIN; ++m) stc<NW>(te, m * CC + c0, rw.on, t[m]);
+    // every lane of a quad holds the same total, so with 16 harmonics all
+    // lanes store (identical values per address) and the store needs no
+    // branch, which keeps the wait for the next edge's loads exact
     const T tot = wave_reduce_scatter16<T>(dy);
-    if ((lane & 3) == 0 && (lane >> 2) < DSH)
+    if (DSH == 16 || (lane >> 2) < DSH)
       dYp[((int64_t)part * n_chunk_edges + el) * DSH + (lane >> 2)] = scale * tot;
   };
-  Buf A, B;
-  int e = e_lo;
-  load(e, A);
-  while (e < e_hi) {
-    if (e + 1 < e_hi) load(e + 1, B);
-    compute(e, A);
-    if (++e >= e_hi) break;
-    if (e + 1 < e_hi) load(e + 1, A);
-    compute(e, B);
-    ++e;
+  if (e_hi - e_lo > 64 * kIdxWindows) {
+    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) { load_j(e, uniform(src[e]), uniform(rev[e]), b); },
+                   compute);
+  } else {
+    RowIdx<kIdxWindows> si, ri;
+    si.init(src, e_lo, e_hi, lane);
+    ri.init(rev, e_lo, e_hi, lane);
+    edge_loop<Buf>(e_lo, e_hi,
+                   [&](int e, Buf& b) { load_j(e, si.get(e - e_lo), ri.get(e - e_lo), b); }, compute);
   }
 }
 
