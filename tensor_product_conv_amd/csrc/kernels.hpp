@@ -59,9 +59,12 @@ hipError_t launch_geom_bwd(int dtype, int L2, int64_t ne, int64_t edge_begin, do
 //   bl  backward last layer    [nblk][64][S4]   (W_L^T as the A operand)
 //   bh  backward layers 2..NH  [NH-1][NB][64][S4]
 //   b0  backward layer 1       [64][S4]          (rows 8..15 zero)
+// and, for the float32 last layer on bf16 matrix cores (three-part split of
+// every weight), a bf16 section counted in float slots (two values per slot):
+//   fs  forward last layer     [nblk][64][H/32][3 parts][8]
 struct RadialPack {
   int H, NH, pc, nblk;
-  int64_t f0, fh, fl, bl, bh, b0, total;
+  int64_t f0, fh, fl, bl, bh, b0, fs, total;
 };
 inline RadialPack radial_pack_layout(int H, int NH, int pc) {
   auto up = [](int64_t v) { return (v + 63) / 64 * 64; };
@@ -84,6 +87,8 @@ inline RadialPack radial_pack_layout(int H, int NH, int pc) {
   off += up(hid);
   L.b0 = off;
   off += up(64 * S4);
+  L.fs = off;
+  off += up((int64_t)L.nblk * 64 * (H / 32) * 12);
   L.total = off;
   return L;
 }

@@ -105,6 +105,48 @@ __device__ __forceinline__ vec4<T> zero4() {
 }
 
 // ---------------------------------------------------------------------------
+// float32 products on the bf16 matrix cores.  Every operand x is split into
+// three bf16 parts, x = x1 + x2 + x3 + O(2^-24 |x|) (x1 = bf16(x), x2 =
+// bf16(x - x1), x3 = bf16(x - x1 - x2); the differences are exact in
+// float32), and a product keeps the six cross terms x_i y_j with i + j <= 4,
+// which carry everything above about 2^-24 |xy|, accumulated in float32 from
+// the smallest up.  FastMACE's "tf32x3_gemms" precision option splits matrix
+// products into reduced-precision tensor-core products the same way; with
+// bf16 parts three terms would leave about 2^-17 relative error, six reach
+// float32 rounding.  One v_mfma_f32_16x16x32_bf16 covers 32 reduction steps
+// in half the cycles of the float32 instruction's 4, so the six terms cost
+// 3/8 of the float32 product.
+// Lane layout (measured): lane l supplies A[l%16][8(l/16)+j] and
+// B[8(l/16)+j][l%16] for j = 0..7, and receives D[4(l/16)+r][l%16].
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void split3(float x, __bf16& p1, __bf16& p2, __bf16& p3) {
+  p1 = (__bf16)x;
+  const float r1 = x - (float)p1;
+  p2 = (__bf16)r1;
+  const float r2 = r1 - (float)p2;
+  p3 = (__bf16)r2;
+}
+
+__device__ __forceinline__ f32x4 mfma_bf(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// c += A B with A, B given as their three bf16 parts (six terms, small first).
+__device__ __forceinline__ f32x4 mfma_x6(const bf16x8 (&a)[3], const bf16x8 (&b)[3], f32x4 c) {
+  c = mfma_bf(a[2], b[0], c);
+  c = mfma_bf(a[0], b[2], c);
+  c = mfma_bf(a[1], b[1], c);
+  c = mfma_bf(a[1], b[0], c);
+  c = mfma_bf(a[0], b[1], c);
+  c = mfma_bf(a[0], b[0], c);
+  return c;
+}
+
+// Whether the float32 last layer takes the split-bf16 kernels.
+__host__ __device__ constexpr bool x6_shape(int H, int pc) { return H % 32 == 0 && pc % 32 == 0; }
+
+// ---------------------------------------------------------------------------
 // weight packing (see RadialPack for the sections)
 template <typename T>
 __global__ void __launch_bounds__(256) k_radial_pack(RadialPack L, RadialWeights<T> W, T* __restrict__ pk) {
@@ -165,6 +207,29 @@ __global__ void __launch_bounds__(256) k_radial_pack(RadialPack L, RadialWeights
       }
     }
     pk[i] = v;
+  }
+}
+
+// The split-bf16 section fs (float32 weights only): A operand of R = a W_L
+// for column block blk, lane (g, el), reduction block kb, part, step j =
+// hidden feature 32 kb + 16 (j / 4) + 4 g + j % 4.
+__global__ void __launch_bounds__(256) k_radial_pack_x6(RadialPack L, const float* __restrict__ WL,
+                                                      __bf16* __restrict__ fs) {
+  const int KB = L.H / 32, pc = L.pc;
+  const int64_t nfs = (int64_t)L.nblk * kWave * KB * 24;
+  for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < nfs;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(q % 8), part = (int)((q / 8) % 3);
+    const int kb = (int)((q / 24) % KB);
+    const int lane = (int)((q / (24 * KB)) % kWave);
+    const int64_t blk = q / (24 * (int64_t)KB * kWave);
+    const int g = lane / 16, el = lane % 16;
+    const int64_t col = blk * 16 + el;
+    const int k = 32 * kb + 16 * (j / 4) + 4 * g + j % 4;
+    const float w = col < pc ? WL[(int64_t)k * pc + col] : 0.f;
+    __bf16 p[3];
+    split3(w, p[0], p[1], p[2]);
+    fs[q] = p[part];
   }
 }
 
@@ -350,6 +415,91 @@ __device__ __forceinline__ void radial_last_pairs(int64_t e0, int pc, int lane, 
 
 // ---------------------------------------------------------------------------
 // forward
+// As radial_last_pairs, with the products on the bf16 matrix cores (three-
+// part split, six terms).  The activations a lane holds (features 16 nb +
+// 4g + r of its edge) are exactly the B-operand values of the two 32-step
+// reductions, taking step (kb, j) as feature 16 (2 kb + j / 4) + 4 g + j % 4;
+// the packed weights (section fs) follow the same order.  They are split
+// once per wave; a block's weights are six 16-byte loads per lane.
+// FULL = false serves the last, partial wave (rows at or past ne are not
+// stored), so every edge's weights come from the same arithmetic wherever
+// the wave boundaries fall.
+template <int H, int S, bool FULL>
+__device__ __forceinline__ void radial_last_pairs_x6(int64_t e0, int64_t ne, int pc, int lane,
+                                                     const __bf16* __restrict__ fs, int nblk,
+                                                     const float (&act)[S][H / 16][4],
+                                                     float* __restrict__ R) {
+  constexpr int KB = H / 32;
+  const int g = lane / 16, el = lane % 16;
+  const bool lo = el < 8;
+  bf16x8 bx[S][KB][3];
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        __bf16 p1, p2, p3;
+        split3(act[st][2 * kb + j / 4][j % 4], p1, p2, p3);
+        bx[st][kb][0][j] = p1;
+        bx[st][kb][1][j] = p2;
+        bx[st][kb][2][j] = p3;
+      }
+  const __bf16* __restrict__ wl = fs + (int64_t)lane * KB * 24;
+  float* rowp[S];
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+    rowp[st] = R + (e0 + st * 16 + (el & 7)) * (int64_t)pc + (lo ? 0 : 16) + 4 * g;
+  auto load = [&](int cb, bf16x8(&w)[2][KB][3]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int pp = 0; pp < 3; ++pp)
+          w[c][kb][pp] = *reinterpret_cast<const bf16x8*>(wl + (int64_t)(cb + c) * kWave * KB * 24 + kb * 24 + pp * 8);
+  };
+  auto pair = [&](int cb, const bf16x8(&w)[2][KB][3]) __attribute__((always_inline)) {
+    f32x4 acc[2][S];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int st = 0; st < S; ++st) acc[c][st] = zero4<float>();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int st = 0; st < S; ++st) acc[c][st] = mfma_x6(w[c][kb], bx[st][kb], acc[c][st]);
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+      f32x4 X, Y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = acc[0][st][r], y = acc[1][st][r];
+        const float xs = row_swap8(x), ys = row_swap8(y);
+        X[r] = lo ? x : ys;
+        Y[r] = lo ? xs : y;
+      }
+      float* dst = rowp[st] + cb * 16;
+      const int64_t row = e0 + st * 16 + (el & 7);
+      if (FULL || row < ne) __builtin_nontemporal_store(X, reinterpret_cast<f32x4*>(dst));
+      if (FULL || row + 8 < ne) __builtin_nontemporal_store(Y, reinterpret_cast<f32x4*>(dst + 8 * (int64_t)pc));
+    }
+  };
+  const int np = nblk / 2;
+  bf16x8 wa[2][KB][3], wb[2][KB][3];
+  load(0, wa);
+  int q = 0;
+  for (; q + 2 <= np; q += 2) {
+    load(2 * (q + 1), wb);
+    pair(2 * q, wa);
+    load(2 * (q + 2 < np ? q + 2 : np - 1), wa);
+    pair(2 * (q + 1), wb);
+  }
+  if (q < np) pair(2 * q, wa);
+}
+
 // VEC: 16-byte stores of whole 16-column blocks (float32, width a multiple
 // of 16); PAIRS: width also a multiple of 32, full waves use the paired
 // line-wide stores.
@@ -385,7 +535,13 @@ k_radial_fwd(int64_t ne, int pc, const T* __restrict__ ef, const T* __restrict__
   // Full waves store without tests, so the wait before each block covers only
   // that block's weight loads and never stores still in flight; the last,
   // partial wave checks each row.
-  if (e0 + 16 * S <= ne) {
+  if constexpr (PAIRS && x6_shape(H, 32)) {
+    const __bf16* fs = reinterpret_cast<const __bf16*>(pk + L.fs);
+    if (e0 + 16 * S <= ne)
+      radial_last_pairs_x6<H, S, true>(e0, ne, pc, lane, fs, L.nblk, act, R);
+    else
+      radial_last_pairs_x6<H, S, false>(e0, ne, pc, lane, fs, L.nblk, act, R);
+  } else if (e0 + 16 * S <= ne) {
     if constexpr (PAIRS)
       radial_last_pairs<H, S>(e0, pc, lane, pk + L.fl, L.nblk, act, R);
     else
@@ -669,6 +825,12 @@ hipError_t pack_impl(const RadialPack& L, const void* const* w, void* pk, hipStr
   for (int k = 0; k <= L.NH; ++k) W.w[k] = static_cast<const T*>(w[k]);
   const int64_t blocks = (L.total + 255) / 256;
   k_radial_pack<T><<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, s>>>(L, W, static_cast<T*>(pk));
+  if constexpr (std::is_same<T, float>::value) {
+    if (x6_shape(L.H, L.pc)) {
+      float* base = static_cast<float*>(pk);
+      k_radial_pack_x6<<<1024, 256, 0, s>>>(L, W.w[L.NH], reinterpret_cast<__bf16*>(base + L.fs));
+    }
+  }
   return hipGetLastError();
 }
 

@@ -209,6 +209,46 @@ __device__ __forceinline__ void st_vec(T* __restrict__ base, uint32_t off, bool 
   }
 }
 
+// One edge's contribution to the accumulators of the paths in group G (of
+// NG): for every such path p and output component m3,
+//   acc[(p,m3)] += sum_m1 M^p[m1][m3] * R[p] * h[(l1,m1)],  M^p = C^p . Y,
+// with the sparsity of C^p unrolled at compile time.  h and R hold CPL
+// channels per lane; ye is the edge's harmonics (uniform across lanes).
+template <typename T, int L1, int L2, int L3, int CPL, int NG, int G>
+__device__ __forceinline__ void tp_fwd_edge(const T (&hh)[kTable<L1, L2, L3>.din][CPL],
+                                            const T (&rr)[kTable<L1, L2, L3>.np][CPL], const T (&ye)[16],
+                                            T (&acc)[kTable<L1, L2, L3>.dout][CPL]) {
+  constexpr int NP = kTable<L1, L2, L3>.np;
+  static_for<NP>([&](auto pc) {
+    constexpr int p = decltype(pc)::value;
+    if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) {
+      constexpr Path P = kTable<L1, L2, L3>.path[p];
+      T hr[2 * P.l1 + 1][CPL];
+#pragma unroll
+      for (int m1 = 0; m1 < 2 * P.l1 + 1; ++m1)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) hr[m1][c] = rr[p][c] * hh[P.l1 * P.l1 + m1][c];
+      static_for<2 * P.l3 + 1>([&](auto m3c) {
+        constexpr int m3 = decltype(m3c)::value;
+        constexpr int row = kTable<L1, L2, L3>.out_row(p, m3);
+        static_for<2 * P.l1 + 1>([&](auto m1c) {
+          constexpr int m1 = decltype(m1c)::value;
+          if constexpr (kTable<L1, L2, L3>.midx[p][m1][m3] >= 0) {
+            T M = T(0);
+            static_for<2 * P.l2 + 1>([&](auto m2c) {
+              constexpr int m2 = decltype(m2c)::value;
+              constexpr double cv = kTable<L1, L2, L3>.cg[p][m1][m2][m3];
+              if constexpr (cv != 0.0) M += T(cv) * ye[P.l2 * P.l2 + m2];
+            });
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[row][c] += M * hr[m1][c];
+          }
+        });
+      });
+    }
+  });
+}
+
 template <typename T, int L1, int L2, int L3, int CPL, int NG, bool MASKED, int G>
 __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, int e_lo, int e_hi,
                                              int64_t edge_begin, int C, uint32_t c0, bool on,
@@ -238,7 +278,7 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
   };
   const int lane = threadIdx.x % kTPWave;
   const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
-  auto load_j = [&](int e, int j, Buf& b) {
+  auto load_j = [&](int e, int j, Buf& b) __attribute__((always_inline)) {
     const T* __restrict__ hj = h + (int64_t)j * DIN * C;
     const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
 #pragma unroll
@@ -249,45 +289,18 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
     });
     b.y = Y[((int64_t)e - edge_begin) * DSH + ylane];
   };
-  auto compute = [&](int, const Buf& b) {
+  auto compute = [&](int, const Buf& b) __attribute__((always_inline)) {
     T ye[16];
 #pragma unroll
     for (int k = 0; k < DSH; ++k) ye[k] = lane_value(b.y, k);
-    static_for<NP>([&](auto pc) {
-      constexpr int p = decltype(pc)::value;
-      if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) {
-        constexpr Path P = kTable<L1, L2, L3>.path[p];
-        T hr[2 * P.l1 + 1][CPL];
-#pragma unroll
-        for (int m1 = 0; m1 < 2 * P.l1 + 1; ++m1)
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) hr[m1][c] = b.r[p][c] * b.h[P.l1 * P.l1 + m1][c];
-        static_for<2 * P.l3 + 1>([&](auto m3c) {
-          constexpr int m3 = decltype(m3c)::value;
-          constexpr int row = kTable<L1, L2, L3>.out_row(p, m3);
-          static_for<2 * P.l1 + 1>([&](auto m1c) {
-            constexpr int m1 = decltype(m1c)::value;
-            if constexpr (kTable<L1, L2, L3>.midx[p][m1][m3] >= 0) {
-              T M = T(0);
-              static_for<2 * P.l2 + 1>([&](auto m2c) {
-                constexpr int m2 = decltype(m2c)::value;
-                constexpr double cv = kTable<L1, L2, L3>.cg[p][m1][m2][m3];
-                if constexpr (cv != 0.0) M += T(cv) * ye[P.l2 * P.l2 + m2];
-              });
-#pragma unroll
-              for (int c = 0; c < CPL; ++c) acc[row][c] += M * hr[m1][c];
-            }
-          });
-        });
-      }
-    });
+    tp_fwd_edge<T, L1, L2, L3, CPL, NG, G>(b.h, b.r, ye, acc);
   };
   if (e_hi - e_lo > 64 * kIdxWindows) {
-    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) { load_j(e, uniform(src[e]), b); }, compute);
+    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, uniform(src[e]), b); }, compute);
   } else if (e_hi > e_lo) {
     RowIdx<kIdxWindows> si;
     si.init(src, e_lo, e_hi, lane);
-    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) { load_j(e, si.get(e - e_lo), b); }, compute);
+    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, si.get(e - e_lo), b); }, compute);
   }
   static_for<NP>([&](auto pc) {
     constexpr int p = decltype(pc)::value;
@@ -462,7 +475,7 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
     int er;  // reverse edge
   };
   const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
-  auto load_j = [&](int e, int j, int er, Buf& b) {
+  auto load_j = [&](int e, int j, int er, Buf& b) __attribute__((always_inline)) {
     const T* __restrict__ hj = h + (int64_t)j * DIN * CC;
     const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
 #pragma unroll
@@ -472,7 +485,7 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
     b.y = Y[((int64_t)e - edge_begin) * DSH + ylane];
     b.er = er;
   };
-  auto compute = [&](int e, const Buf& b) {
+  auto compute = [&](int e, const Buf& b) __attribute__((always_inline)) {
     const int64_t el = (int64_t)e - edge_begin;
     T ye[16];
 #pragma unroll
@@ -538,14 +551,14 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
       dYp[((int64_t)part * n_chunk_edges + el) * DSH + (lane >> 2)] = scale * tot;
   };
   if (e_hi - e_lo > 64 * kIdxWindows) {
-    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) { load_j(e, uniform(src[e]), uniform(rev[e]), b); },
+    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, uniform(src[e]), uniform(rev[e]), b); },
                    compute);
   } else {
     RowIdx<kIdxWindows> si, ri;
     si.init(src, e_lo, e_hi, lane);
     ri.init(rev, e_lo, e_hi, lane);
     edge_loop<Buf>(e_lo, e_hi,
-                   [&](int e, Buf& b) { load_j(e, si.get(e - e_lo), ri.get(e - e_lo), b); }, compute);
+                   [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, si.get(e - e_lo), ri.get(e - e_lo), b); }, compute);
   }
 }
 
