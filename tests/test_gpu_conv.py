@@ -16,7 +16,10 @@ def _prob(case, nl):
     return case.oracle((rp, src, shift))
 
 
-@pytest.mark.parametrize("k", [0, 1])
+# 0 tiny (float64), 1 small; 5 and 6 are the small system at other channel
+# and hidden widths (the narrower-channel tensor-product kernels, and the
+# float32 radial kernels that the wider networks do not take)
+@pytest.mark.parametrize("k", [0, 1, 5, 6])
 def test_full_parity(k):
     case = Case(k)
     nl = case.nbr()

@@ -60,6 +60,14 @@ CONFIGS = {
     4: dict(name="large", N=262144, dtype="float32", C=64, l1max=3,
             sh_lmax=3, out_lmax=3, r_cut=6.0, hidden=[64, 64], n_paths=23,
             d_in=16, d_sh=16, d_out=99, scale="one", seed=4, geometry="fcc"),
+    # Kernel-path cases: the small system with other widths, so that the
+    # narrower-channel and narrower-network kernels are checked too.
+    5: dict(name="small_c32_h16", N=4096, dtype="float32", C=32, l1max=1,
+            sh_lmax=3, out_lmax=3, r_cut=5.0, hidden=[16, 16], n_paths=10,
+            d_in=4, d_sh=16, d_out=40, scale="one", seed=5, geometry="sc"),
+    6: dict(name="small_c64_h32", N=4096, dtype="float32", C=64, l1max=2,
+            sh_lmax=3, out_lmax=3, r_cut=5.0, hidden=[32], n_paths=17,
+            d_in=9, d_sh=16, d_out=71, scale="one", seed=6, geometry="sc"),
 }
 
 N_BESSEL = 8
