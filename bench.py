@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_F32_PEAK = 157.3e12   # flop/s, dense fp32 matrix
 VALU_F32_PEAK = 78.6e12    # flop/s, fp32 FMA without packed math: 256 CU x 4 SIMD x 16 lanes x 2 x 2.4 GHz
+MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16 matrix
 
 KERNEL_SOURCES = {
     "tp_fwd": ["tp_impl.hpp", "tp_fwd.hip", "tables.hpp"],
@@ -88,8 +89,9 @@ def algorithmic(kernel, N, E, cfg, ctx):
         return (E * (2 * T * PC + 2 * T * dsh) + N * T * C * (din + dout) + csr,
                 E * C * (2 * nnz + 4 * m13 + 2 * din + 2 * dout))
     if kernel == "dh_gather":
-        # writes dh; its reads are the split's intermediate
-        return (N * T * C * din + 4 * (N + 1), E * C * din)
+        # as a kernel of its own: reads the per-edge contributions, writes dh
+        # (the K9 group below counts only dh, the pass's algorithmic output)
+        return (E * T * C * din + N * T * C * din + 4 * (N + 1), E * C * din)
     hidden = 2 * (8 * H + (NH - 1) * H * H)
     if kernel == "radial_fwd":
         return E * (8 * T + T * PC), E * (hidden + 2 * H * PC)
@@ -128,7 +130,17 @@ def roofline_for(kernel, per_launch_s, N, E, cfg, ctx):
     nbytes, flops = algorithmic(kernel, N, E, cfg, ctx)
     if nbytes is None:
         return None
-    if kernel.startswith("radial"):
+    if kernel == "radial_fwd":
+        # float32 last layer runs as six bf16 products (three-part operand
+        # split), the hidden layers on fp32 matrix cores; at those rates the
+        # matrix work takes well under the time to write R, so HBM bounds it
+        H, PC = cfg["hidden"][0], ctx.r_width
+        last = E * 2 * H * PC
+        ach = nbytes / per_launch_s
+        r = dict(bound="hbm", achieved=ach / 1e9, peak=HBM_PEAK / 1e9, unit="GB/s",
+                 frac=ach / HBM_PEAK, algorithmic_bytes_per_launch=nbytes,
+                 matrix_frac=((flops - last) / MFMA_F32_PEAK + 6 * last / MFMA_BF16_PEAK) / per_launch_s)
+    elif kernel.startswith("radial"):
         ach = flops / per_launch_s
         r = dict(bound="mfma", achieved=ach / 1e12, peak=MFMA_F32_PEAK / 1e12, unit="TFLOP/s",
                  frac=ach / MFMA_F32_PEAK, algorithmic_flops_per_launch=flops)

@@ -62,9 +62,10 @@ hipError_t launch_geom_bwd(int dtype, int L2, int64_t ne, int64_t edge_begin, do
 // and, for the float32 last layer on bf16 matrix cores (three-part split of
 // every weight), a bf16 section counted in float slots (two values per slot):
 //   fs  forward last layer     [nblk][64][H/32][3 parts][8]
+//   bs  backward last layer    [pc/32][64][H/16][3 parts][8]
 struct RadialPack {
   int H, NH, pc, nblk;
-  int64_t f0, fh, fl, bl, bh, b0, fs, total;
+  int64_t f0, fh, fl, bl, bh, b0, fs, bs, total;
 };
 inline RadialPack radial_pack_layout(int H, int NH, int pc) {
   auto up = [](int64_t v) { return (v + 63) / 64 * 64; };
@@ -89,6 +90,8 @@ inline RadialPack radial_pack_layout(int H, int NH, int pc) {
   off += up(64 * S4);
   L.fs = off;
   off += up((int64_t)L.nblk * 64 * (H / 32) * 12);
+  L.bs = off;
+  off += up((int64_t)(pc / 32) * 64 * NB * 12);
   L.total = off;
   return L;
 }

@@ -214,22 +214,34 @@ __global__ void __launch_bounds__(256) k_radial_pack(RadialPack L, RadialWeights
 // for column block blk, lane (g, el), reduction block kb, part, step j =
 // hidden feature 32 kb + 16 (j / 4) + 4 g + j % 4.
 __global__ void __launch_bounds__(256) k_radial_pack_x6(RadialPack L, const float* __restrict__ WL,
-                                                      __bf16* __restrict__ fs) {
-  const int KB = L.H / 32, pc = L.pc;
+                                                      __bf16* __restrict__ fs, __bf16* __restrict__ bs) {
+  const int KB = L.H / 32, NB = L.H / 16, pc = L.pc;
   const int64_t nfs = (int64_t)L.nblk * kWave * KB * 24;
-  for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < nfs;
-       q += (int64_t)gridDim.x * blockDim.x) {
+  const int64_t nbs = (int64_t)(pc / 32) * kWave * NB * 24;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nfs + nbs;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const bool fwd = i < nfs;
+    const int64_t q = fwd ? i : i - nfs;
+    const int sub_n = fwd ? KB : NB;
     const int j = (int)(q % 8), part = (int)((q / 8) % 3);
-    const int kb = (int)((q / 24) % KB);
-    const int lane = (int)((q / (24 * KB)) % kWave);
-    const int64_t blk = q / (24 * (int64_t)KB * kWave);
+    const int sub = (int)((q / 24) % sub_n);
+    const int lane = (int)((q / (24 * sub_n)) % kWave);
+    const int64_t blk = q / (24 * (int64_t)sub_n * kWave);
     const int g = lane / 16, el = lane % 16;
-    const int64_t col = blk * 16 + el;
-    const int k = 32 * kb + 16 * (j / 4) + 4 * g + j % 4;
-    const float w = col < pc ? WL[(int64_t)k * pc + col] : 0.f;
+    float w;
+    if (fwd) {
+      // A operand of R = a W_L: column 16 blk + el, reduction step (sub, j)
+      const int64_t col = blk * 16 + el;
+      const int k = 32 * sub + 16 * (j / 4) + 4 * g + j % 4;
+      w = col < pc ? WL[(int64_t)k * pc + col] : 0.f;
+    } else {
+      // A operand of dA = dR W_L^T: hidden feature 16 sub + el, reduction
+      // step (g, j) of block blk = column 32 blk + 8 g + j
+      w = WL[(int64_t)(16 * sub + el) * pc + 32 * blk + 8 * g + j];
+    }
     __bf16 p[3];
     split3(w, p[0], p[1], p[2]);
-    fs[q] = p[part];
+    (fwd ? fs : bs)[q] = p[part];
   }
 }
 
@@ -419,17 +431,33 @@ __device__ __forceinline__ void radial_last_pairs(int64_t e0, int pc, int lane, 
 // part split, six terms).  The activations a lane holds (features 16 nb +
 // 4g + r of its edge) are exactly the B-operand values of the two 32-step
 // reductions, taking step (kb, j) as feature 16 (2 kb + j / 4) + 4 g + j % 4;
-// the packed weights (section fs) follow the same order.  They are split
-// once per wave; a block's weights are six 16-byte loads per lane.
-// FULL = false serves the last, partial wave (rows at or past ne are not
-// stored), so every edge's weights come from the same arithmetic wherever
-// the wave boundaries fall.
+// the packed weights (section fs) follow the same order and are split once
+// per wave.
+// The four waves of a block share the weights: each pair of column blocks
+// (2 * 64 * KB * 24 bf16, contiguous in fs) is copied once into one of two
+// LDS buffers while the previous pair is multiplied, with one barrier per
+// pair.  The barrier waits for LDS traffic only, so the R stores stay in
+// flight across it.  Every wave of the block runs every pair (barrier
+// count); FULL = false serves the block holding the last edges (rows at or
+// past ne are not stored), so every edge's weights come from the same
+// arithmetic wherever the block boundaries fall.
+template <int H>
+constexpr int kX6Pair = 2 * kWave * (H / 32) * 24;  // bf16 per pair of column blocks
+constexpr int kX6PairsPerTile = 2;
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int H, int S, bool FULL>
 __device__ __forceinline__ void radial_last_pairs_x6(int64_t e0, int64_t ne, int pc, int lane,
                                                      const __bf16* __restrict__ fs, int nblk,
                                                      const float (&act)[S][H / 16][4],
-                                                     float* __restrict__ R) {
-  constexpr int KB = H / 32;
+                                                     float* __restrict__ R, __bf16* wt) {
+  constexpr int KB = H / 32, PAIR = kX6Pair<H>, TILE = kX6PairsPerTile * PAIR;
+  constexpr int NCH = TILE / 8, CPT = (NCH + 255) / 256;  // 16-byte chunks: per tile, per thread
+  const int np = nblk / 2;
+  const int last_ch = np * (PAIR / 8) - 1;  // last chunk of fs
   const int g = lane / 16, el = lane % 16;
   const bool lo = el < 8;
   bf16x8 bx[S][KB][3];
@@ -445,21 +473,40 @@ __device__ __forceinline__ void radial_last_pairs_x6(int64_t e0, int64_t ne, int
         bx[st][kb][1][j] = p2;
         bx[st][kb][2][j] = p3;
       }
-  const __bf16* __restrict__ wl = fs + (int64_t)lane * KB * 24;
   float* rowp[S];
 #pragma unroll
   for (int st = 0; st < S; ++st)
     rowp[st] = R + (e0 + st * 16 + (el & 7)) * (int64_t)pc + (lo ? 0 : 16) + 4 * g;
-  auto load = [&](int cb, bf16x8(&w)[2][KB][3]) __attribute__((always_inline)) {
+  // chunk indices past the tile or past fs are clamped: the spare threads
+  // copy a chunk again (same value, same place), and a tile past the last
+  // pair holds values no pair reads
+  auto fetch = [&](int t, bf16x8(&pf)[CPT]) __attribute__((always_inline)) {
+    const bf16x8* __restrict__ src = reinterpret_cast<const bf16x8*>(fs);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      int ch = (int)threadIdx.x + 256 * i;
+      ch = t * (TILE / 8) + (ch < NCH ? ch : NCH - 1);
+      pf[i] = src[ch < last_ch ? ch : last_ch];
+    }
+  };
+  auto put = [&](int buf, const bf16x8(&pf)[CPT]) __attribute__((always_inline)) {
+    bf16x8* dst = reinterpret_cast<bf16x8*>(wt + buf * TILE);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = (int)threadIdx.x + 256 * i;
+      dst[ch < NCH ? ch : NCH - 1] = pf[i];
+    }
+  };
+  auto pair = [&](int q, const __bf16* tile) __attribute__((always_inline)) {
+    const __bf16* wl = tile + (q % kX6PairsPerTile) * PAIR + lane * KB * 24;
+    bf16x8 w[2][KB][3];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int pp = 0; pp < 3; ++pp)
-          w[c][kb][pp] = *reinterpret_cast<const bf16x8*>(wl + (int64_t)(cb + c) * kWave * KB * 24 + kb * 24 + pp * 8);
-  };
-  auto pair = [&](int cb, const bf16x8(&w)[2][KB][3]) __attribute__((always_inline)) {
+          w[c][kb][pp] = *reinterpret_cast<const bf16x8*>(wl + c * kWave * KB * 24 + kb * 24 + pp * 8);
     f32x4 acc[2][S];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -481,23 +528,28 @@ __device__ __forceinline__ void radial_last_pairs_x6(int64_t e0, int64_t ne, int
         X[r] = lo ? x : ys;
         Y[r] = lo ? xs : y;
       }
-      float* dst = rowp[st] + cb * 16;
+      float* dst = rowp[st] + q * 32;
       const int64_t row = e0 + st * 16 + (el & 7);
       if (FULL || row < ne) __builtin_nontemporal_store(X, reinterpret_cast<f32x4*>(dst));
       if (FULL || row + 8 < ne) __builtin_nontemporal_store(Y, reinterpret_cast<f32x4*>(dst + 8 * (int64_t)pc));
     }
   };
-  const int np = nblk / 2;
-  bf16x8 wa[2][KB][3], wb[2][KB][3];
-  load(0, wa);
-  int q = 0;
-  for (; q + 2 <= np; q += 2) {
-    load(2 * (q + 1), wb);
-    pair(2 * q, wa);
-    load(2 * (q + 2 < np ? q + 2 : np - 1), wa);
-    pair(2 * (q + 1), wb);
+  const int nt = (np + kX6PairsPerTile - 1) / kX6PairsPerTile;
+  bf16x8 pf[CPT];
+  fetch(0, pf);
+  put(0, pf);
+  lds_barrier();
+  for (int t = 0; t < nt; ++t) {
+    fetch(t + 1 < nt ? t + 1 : t, pf);  // the last round copies its own tile again, unused
+    const __bf16* tile = wt + (t & 1) * TILE;
+#pragma unroll
+    for (int h = 0; h < kX6PairsPerTile; ++h) {
+      const int q = t * kX6PairsPerTile + h;
+      if (h == 0 || q < np) pair(q, tile);
+    }
+    put((t + 1) & 1, pf);
+    lds_barrier();
   }
-  if (q < np) pair(2 * q, wa);
 }
 
 // VEC: 16-byte stores of whole 16-column blocks (float32, width a multiple
@@ -510,10 +562,12 @@ k_radial_fwd(int64_t ne, int pc, const T* __restrict__ ef, const T* __restrict__
   constexpr int NB = H / 16, S4 = 4 * NB;
   const int lane = threadIdx.x % kWave;
   const int64_t e0 = (blockIdx.x * (int64_t)(blockDim.x / kWave) + threadIdx.x / kWave) * (16 * S);
-  if (e0 >= ne) return;
+  // the shared-weight path keeps waves without edges for its barriers
+  constexpr bool kX6 = PAIRS && x6_shape(H, 32);
+  if (!kX6 && e0 >= ne) return;
 
   T act[S][NB][4];
-  layer0<T, H, S>(e0, ne, lane, ef, pk + L.f0, act);
+  layer0<T, H, S>(e0 < ne ? e0 : ne - 1, ne, lane, ef, pk + L.f0, act);
 #pragma unroll
   for (int st = 0; st < S; ++st)
 #pragma unroll
@@ -535,12 +589,14 @@ k_radial_fwd(int64_t ne, int pc, const T* __restrict__ ef, const T* __restrict__
   // Full waves store without tests, so the wait before each block covers only
   // that block's weight loads and never stores still in flight; the last,
   // partial wave checks each row.
-  if constexpr (PAIRS && x6_shape(H, 32)) {
+  if constexpr (kX6) {
+    __shared__ __attribute__((aligned(16))) __bf16 wt[2 * kX6PairsPerTile * kX6Pair<H>];
     const __bf16* fs = reinterpret_cast<const __bf16*>(pk + L.fs);
-    if (e0 + 16 * S <= ne)
-      radial_last_pairs_x6<H, S, true>(e0, ne, pc, lane, fs, L.nblk, act, R);
+    const int64_t b_end = (blockIdx.x + 1) * (int64_t)(blockDim.x / kWave) * (16 * S);
+    if (b_end <= ne)
+      radial_last_pairs_x6<H, S, true>(e0, ne, pc, lane, fs, L.nblk, act, R, wt);
     else
-      radial_last_pairs_x6<H, S, false>(e0, ne, pc, lane, fs, L.nblk, act, R);
+      radial_last_pairs_x6<H, S, false>(e0, ne, pc, lane, fs, L.nblk, act, R, wt);
   } else if (e0 + 16 * S <= ne) {
     if constexpr (PAIRS)
       radial_last_pairs<H, S>(e0, pc, lane, pk + L.fl, L.nblk, act, R);
@@ -653,6 +709,119 @@ k_radial_bwd_dA(int64_t ne, int pc, const T* __restrict__ dR, const T* __restric
   }
 }
 
+// backward, part 1 on the bf16 matrix cores (float32, width and hidden size
+// multiples of 32): dA = dR W_L^T with both operands split in three bf16
+// parts.  Reduction step (q, g, j) covers column n = 32 q + 8 g + j, so a
+// lane reads eight consecutive dR values of its row per step (two 16-byte
+// loads; the four lanes of a row cover one 128-byte line) and splits them in
+// registers, one step ahead of its products.  The weights (section bs,
+// pre-split in the same order, 64 * NB * 24 bf16 per step) are shared by the
+// block's four waves through LDS as in the forward: two steps per tile (the
+// step count pc / 32 must be even), the next tile copied while the current
+// one is used, one barrier per tile.
+// Every wave runs every step (barrier count); rows past the end read the last
+// row and their strips are not stored.  Output as the float32 kernel.
+template <int H, int S>
+__global__ void __launch_bounds__(256)
+k_radial_bwd_dA_x6(int64_t ne, int pc, const float* __restrict__ dR, const __bf16* __restrict__ bs,
+                   float* __restrict__ dA3) {
+  constexpr int NB = H / 16, S4 = 4 * NB;
+  constexpr int STEP = kWave * NB * 24, TS = 2, TILE = TS * STEP;
+  constexpr int NCH = TILE / 8, CPT = (NCH + 255) / 256;  // 16-byte chunks: per tile, per thread
+  __shared__ __attribute__((aligned(16))) __bf16 wt[2 * TILE];
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, el = lane % 16;
+  const int64_t e0 = (blockIdx.x * (int64_t)(blockDim.x / kWave) + threadIdx.x / kWave) * (16 * S);
+  const float* __restrict__ rowp[S];
+#pragma unroll
+  for (int st = 0; st < S; ++st) {
+    int64_t e = e0 + st * 16 + el;
+    e = e < ne ? e : ne - 1;
+    rowp[st] = dR + e * (int64_t)pc + 8 * g;
+  }
+  const int ns = pc / 32, ntile = ns / TS;
+  const int last_ch = ns * (STEP / 8) - 1;
+  f32x4 dA[S][NB];
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) dA[st][kb] = zero4<float>();
+  auto fetch = [&](int t, bf16x8(&pf)[CPT]) __attribute__((always_inline)) {
+    const bf16x8* __restrict__ src = reinterpret_cast<const bf16x8*>(bs);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      int ch = (int)threadIdx.x + 256 * i;
+      ch = t * (TILE / 8) + (ch < NCH ? ch : NCH - 1);
+      pf[i] = src[ch < last_ch ? ch : last_ch];
+    }
+  };
+  auto put = [&](int buf, const bf16x8(&pf)[CPT]) __attribute__((always_inline)) {
+    bf16x8* dst = reinterpret_cast<bf16x8*>(wt + buf * TILE);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int ch = (int)threadIdx.x + 256 * i;
+      dst[ch < NCH ? ch : NCH - 1] = pf[i];
+    }
+  };
+  auto load = [&](int q, f32x4(&bv)[S][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+      bv[st][0] = ld4(rowp[st] + 32 * q);
+      bv[st][1] = ld4(rowp[st] + 32 * q + 4);
+    }
+  };
+  auto step = [&](const __bf16* w, const f32x4(&bv)[S][2]) __attribute__((always_inline)) {
+    bf16x8 wv[NB][3];
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int pp = 0; pp < 3; ++pp) wv[kb][pp] = *reinterpret_cast<const bf16x8*>(w + kb * 24 + pp * 8);
+    bf16x8 bx[S][3];
+#pragma unroll
+    for (int st = 0; st < S; ++st)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        __bf16 p1, p2, p3;
+        split3(bv[st][j / 4][j % 4], p1, p2, p3);
+        bx[st][0][j] = p1;
+        bx[st][1][j] = p2;
+        bx[st][2][j] = p3;
+      }
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+      for (int st = 0; st < S; ++st) dA[st][kb] = mfma_x6(wv[kb], bx[st], dA[st][kb]);
+  };
+  bf16x8 pf[CPT];
+  f32x4 ba[S][2], bb[S][2];
+  fetch(0, pf);
+  put(0, pf);
+  load(0, ba);
+  lds_barrier();
+  for (int t = 0; t < ntile; ++t) {
+    fetch(t + 1 < ntile ? t + 1 : t, pf);  // the last round copies its own tile again, unused
+    const __bf16* tile = wt + (t & 1) * TILE + lane * NB * 24;
+    const int q = TS * t;
+    load(q + 1, bb);
+    // keep the scheduler from sinking the loads into the products
+    __builtin_amdgcn_sched_barrier(0);
+    step(tile, ba);
+    load(q + 2 < ns ? q + 2 : ns - 1, ba);  // the last step reloads its own row part, unused
+    __builtin_amdgcn_sched_barrier(0);
+    step(tile + STEP, bb);
+    put((t + 1) & 1, pf);
+    lds_barrier();
+  }
+#pragma unroll
+  for (int st = 0; st < S; ++st) {
+    const int64_t strip = e0 / 16 + st;
+    if (strip * 16 >= ne) continue;
+    float* dst = dA3 + (strip * kWave + lane) * S4;
+#pragma unroll
+    for (int kb = 0; kb < NB; ++kb) st4(dst + 4 * kb, dA[st][kb]);
+  }
+}
+
 // backward, part 2: recompute the hidden layers, then d(ef) from dA3.
 template <typename T, int H, int NH, int S>
 __global__ void __launch_bounds__(256)
@@ -732,7 +901,7 @@ k_radial_bwd_mlp(int64_t ne, const T* __restrict__ ef, const T* __restrict__ dA3
   }
 }
 
-constexpr int kFwdStrips = 4, kMlpStrips = 2;
+constexpr int kFwdStrips = 3, kMlpStrips = 2;
 // the backward product keeps only its accumulators live: 8 strips of 16
 // edges in float32 (128 accumulator registers), 2 in float64
 template <typename T>
@@ -758,9 +927,21 @@ hipError_t fwd_impl(int64_t ne, int pc, const T* ef, const T* pk, const RadialPa
   return hipGetLastError();
 }
 
+// float32 backward on bf16 matrix cores: strips of 16 edges per wave
+constexpr int kBwdStripsX6 = 4;
+
 template <typename T, int H>
 hipError_t bwd_dA_impl(int64_t ne, int pc, const T* dR, const T* pk, const RadialPack& L, T* dA3,
                        hipStream_t s) {
+  if constexpr (std::is_same<T, float>::value && x6_shape(H, 32)) {
+    if (x6_shape(H, pc) && pc % 64 == 0 && reinterpret_cast<uintptr_t>(dR) % 16 == 0) {
+      const int64_t per_block = 4 * 16 * kBwdStripsX6;
+      const __bf16* bs = reinterpret_cast<const __bf16*>(pk + L.bs);
+      k_radial_bwd_dA_x6<H, kBwdStripsX6><<<(unsigned)((ne + per_block - 1) / per_block), 256, 0, s>>>(
+          ne, pc, dR, bs, dA3);
+      return hipGetLastError();
+    }
+  }
   const int64_t per_block = 4 * 16 * kBwdStrips<T>;
   const unsigned blocks = (unsigned)((ne + per_block - 1) / per_block);
   // the vector path reads whole 16-column blocks of every row
@@ -828,7 +1009,8 @@ hipError_t pack_impl(const RadialPack& L, const void* const* w, void* pk, hipStr
   if constexpr (std::is_same<T, float>::value) {
     if (x6_shape(L.H, L.pc)) {
       float* base = static_cast<float*>(pk);
-      k_radial_pack_x6<<<1024, 256, 0, s>>>(L, W.w[L.NH], reinterpret_cast<__bf16*>(base + L.fs));
+      k_radial_pack_x6<<<1024, 256, 0, s>>>(L, W.w[L.NH], reinterpret_cast<__bf16*>(base + L.fs),
+                                            reinterpret_cast<__bf16*>(base + L.bs));
     }
   }
   return hipGetLastError();
