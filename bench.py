@@ -52,7 +52,7 @@ KERNEL_SYMBOLS = {
     "tp_bwd_edge": "k_tp_bwd_edge<",
     "dh_gather": "k_dh_gather<",
     "radial_fwd": "k_radial_fwd<",
-    "radial_bwd_dA": "k_radial_bwd_dA<",
+    "radial_bwd_dA": "k_radial_bwd_dA",   # also the bf16-split k_radial_bwd_dA_x6
     "radial_bwd_mlp": "k_radial_bwd_mlp<",
     "geom_fwd": "k_geom_fwd<",
     "geom_bwd": "k_geom_bwd<",
@@ -130,11 +130,12 @@ def roofline_for(kernel, per_launch_s, N, E, cfg, ctx):
     nbytes, flops = algorithmic(kernel, N, E, cfg, ctx)
     if nbytes is None:
         return None
-    if kernel == "radial_fwd":
-        # float32 last layer runs as six bf16 products (three-part operand
-        # split), the hidden layers on fp32 matrix cores; at those rates the
-        # matrix work takes well under the time to write R, so HBM bounds it
-        H, PC = cfg["hidden"][0], ctx.r_width
+    H, PC = cfg["hidden"][0], ctx.r_width
+    if kernel in ("radial_fwd", "radial_bwd_dA") and str(ctx.dtype) == "torch.float32" and H % 32 == 0 and PC % 64 == 0:
+        # the float32 last-layer products run as six bf16 products (three-part
+        # operand split), the hidden layers on fp32 matrix cores; at those
+        # rates the matrix work takes well under the time to stream R or dR,
+        # so HBM bounds these kernels
         last = E * 2 * H * PC
         ach = nbytes / per_launch_s
         r = dict(bound="hbm", achieved=ach / 1e9, peak=HBM_PEAK / 1e9, unit="GB/s",

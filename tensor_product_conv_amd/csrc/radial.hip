@@ -928,7 +928,7 @@ hipError_t fwd_impl(int64_t ne, int pc, const T* ef, const T* pk, const RadialPa
 }
 
 // float32 backward on bf16 matrix cores: strips of 16 edges per wave
-constexpr int kBwdStripsX6 = 4;
+constexpr int kBwdStripsX6 = 3;
 
 template <typename T, int H>
 hipError_t bwd_dA_impl(int64_t ne, int pc, const T* dR, const T* pk, const RadialPack& L, T* dA3,

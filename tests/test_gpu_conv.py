@@ -16,10 +16,12 @@ def _prob(case, nl):
     return case.oracle((rp, src, shift))
 
 
-# 0 tiny (float64), 1 small; 5 and 6 are the small system at other channel
-# and hidden widths (the narrower-channel tensor-product kernels, and the
-# float32 radial kernels that the wider networks do not take)
-@pytest.mark.parametrize("k", [0, 1, 5, 6])
+# 0 tiny (float64), 1 small; 5-7 are the small system at other channel and
+# hidden widths (the narrower-channel tensor-product kernels, the float32
+# radial kernels that the wider networks do not take, and in 7 a radial
+# width of 17 column steps of 32: a half-filled last weight tile forward and
+# the float32 fallback backward)
+@pytest.mark.parametrize("k", [0, 1, 5, 6, 7])
 def test_full_parity(k):
     case = Case(k)
     nl = case.nbr()

@@ -68,6 +68,9 @@ CONFIGS = {
     6: dict(name="small_c64_h32", N=4096, dtype="float32", C=64, l1max=2,
             sh_lmax=3, out_lmax=3, r_cut=5.0, hidden=[32], n_paths=17,
             d_in=9, d_sh=16, d_out=71, scale="one", seed=6, geometry="sc"),
+    7: dict(name="small_c32_h32", N=4096, dtype="float32", C=32, l1max=2,
+            sh_lmax=3, out_lmax=3, r_cut=5.0, hidden=[32, 32], n_paths=17,
+            d_in=9, d_sh=16, d_out=71, scale="one", seed=7, geometry="sc"),
 }
 
 N_BESSEL = 8
