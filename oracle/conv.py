@@ -177,6 +177,10 @@ class Problem:
         np.add.at(F, self.src, -g)
         return F
 
+    def virial_from(self, g):
+        """Strain derivative of L from the edge gradients (see ``virial``)."""
+        return virial(self.rvec(np.arange(len(self.src))), g)
+
     # ---- sampled pieces for large systems ---------------------------------
     def edges_with_sender(self, atoms):
         atoms = np.asarray(atoms, dtype=np.int64)
@@ -207,6 +211,21 @@ class Problem:
             g_out = self.edge_backward(e_out)["g"]
             np.add.at(F, [where[int(j)] for j in self.src[e_out]], -g_out)
         return F
+
+
+def virial(vec, g):
+    """W[a, b] = dL/d(eps_ab) for a homogeneous strain x -> (I + eps) x applied
+    to the positions and the cell rows together (the pet-jax README,
+    "Conventions": the virial is the strain derivative of the energy; the
+    FastMACE page, "Rewrites and precision options", Stress: one structure's
+    strained cell).  With the neighbour list fixed, every edge vector becomes
+    (I + eps) r_e, so by the chain rule through g_e = dL/dr_e
+
+        W[a, b] = sum_e g_e[a] * r_e[b].
+
+    ``vec`` [E, 3] are the edge vectors, ``g`` [E, 3] the edge gradients."""
+    return np.einsum("ea,eb->ab", np.asarray(g, dtype=np.float64),
+                     np.asarray(vec, dtype=np.float64))
 
 
 def scale_for(cfg, n_atoms, n_edges):

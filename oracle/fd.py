@@ -1,4 +1,4 @@
-"""Finite-difference forces of the surrogate scalar L = sum(G * out).
+"""Finite-difference forces and virial of the surrogate scalar L = sum(G * out).
 
 Forces are the negative position gradient of a scalar (FlashCart paper, §2
 "Machine-learned interatomic potentials").  With the neighbour list held
@@ -48,3 +48,25 @@ def fd_forces(prob: Problem, atoms, delta=1e-3):
             F[n, d] = -(vals[0] - 8 * vals[1] + 8 * vals[2] - vals[3]) / (12 * delta)
     prob.pos = base
     return F
+
+
+def fd_virial(prob: Problem, delta=1e-4):
+    """W[a, b] = dL/d(eps_ab) by a 5-point central stencil in each strain
+    component.  The strain x -> (I + eps) x moves the positions and the cell
+    rows together (pet-jax README, "Conventions"); the CSR is held fixed and L
+    is summed over every edge."""
+    e = np.arange(len(prob.src))
+    pos0, cell0 = prob.pos.copy(), prob.cell.copy()
+    W = np.zeros((3, 3))
+    for a in range(3):
+        for b in range(3):
+            vals = []
+            for c in (-2, -1, 1, 2):
+                F = np.eye(3)
+                F[a, b] += c * delta
+                prob.pos = pos0 @ F.T
+                prob.cell = cell0 @ F.T
+                vals.append(_local_L(prob, e, 1)[0])
+            W[a, b] = (vals[0] - 8 * vals[1] + 8 * vals[2] - vals[3]) / (12 * delta)
+    prob.pos, prob.cell = pos0, cell0
+    return W

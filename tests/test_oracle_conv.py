@@ -43,6 +43,38 @@ def test_forces_by_finite_differences(tiny):
     assert np.abs(F - b["F"]).max() / np.abs(b["F"]).max() < 1e-7
 
 
+def test_virial_by_strain_differences(tiny):
+    """Virial from the edge gradients against differences of L under a
+    homogeneous strain of positions and cell (an independent route: only the
+    forward is evaluated)."""
+    prob, d, out, b = tiny
+    W = prob.virial_from(b["g"])
+    Wfd = fd.fd_virial(prob, delta=1e-4)
+    assert np.abs(W - Wfd).max() / np.abs(W).max() < 1e-7
+    # the surrogate is not rotation invariant, so W need not be symmetric;
+    # a dropped transpose would show here
+    assert np.abs(W - W.T).max() > 1e-3 * np.abs(W).max()
+
+
+def test_virial_two_atom_closed_form():
+    """Two atoms, l = 0 only: L = s R(r) (G_0 h_1 + G_1 h_0) summed over
+    channels for the pair, so W = (dL/dr) r_hat r^T summed over both edges,
+    each edge vector seen from its own receiver."""
+    L = paths.Layout(0, 0, 0, 3)
+    h = np.random.default_rng(6).standard_normal((2, 1, 3))
+    prob, pos = _two_atoms(L, h)
+    prob.G = np.random.default_rng(7).standard_normal((2, 1, 3))
+    b = prob.backward()
+    W = prob.virial_from(b["g"])
+    # both edge vectors are +-(x1 - x0); g_e is parallel to r_e for l = 0, so
+    # W = sum_e |g_e| |r_e| rhat rhat^T: symmetric, rank one along the bond
+    rhat = (pos[1] - pos[0]) / np.linalg.norm(pos[1] - pos[0])
+    mag = sum(float(np.dot(b["g"][e], prob.rvec(np.array([e]))[0])) for e in range(2))
+    np.testing.assert_allclose(W, mag * np.outer(rhat, rhat), rtol=0, atol=1e-13 * abs(mag))
+    Wfd = fd.fd_virial(prob, delta=1e-4)
+    np.testing.assert_allclose(W, Wfd, rtol=0, atol=1e-8 * abs(mag))
+
+
 def test_linearity_identities(tiny):
     # L is linear in each of h, R and Y separately
     prob, d, out, b = tiny
