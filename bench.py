@@ -223,15 +223,16 @@ def traffic_from(fetch_dir, write_dir, out_path):
     return 0
 
 
-def cpu_baseline(case_data, nl_np, budget_s=15.0):
-    """Oracle conv forward + backward on a sample of receiver rows (1 thread)."""
+def cpu_baseline(case_data, budget_s=15.0):
+    """Oracle conv forward + backward on a sample of receiver rows (1 thread),
+    on the oracle's own neighbour list (built before the timed sample)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
-    from oracle import conv, paths
+    from oracle import conv, nbr, paths
 
     d = case_data
     c = d["cfg"]
-    rp, src, shift = nl_np
+    rp, src, shift = nbr.binned(d["pos"], d["cell"], c["r_cut"])
     L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"])
     prob = conv.Problem(L, d["pos"], d["cell"], rp, src, shift, d["h"], d["W"], c["r_cut"],
                         conv.scale_for(c, len(d["pos"]), rp[-1]), d["G"])
@@ -339,6 +340,21 @@ def main(argv=None):
 
     per_kernel = {n: dict(avg_ms=tot / cnt, launches_per_step=cnt / a.steps, ms_per_step=tot / a.steps)
                   for n, (tot, cnt) in kt.items()}
+
+    # the virial (strain derivative) from the step's edge gradients, timed on
+    # its own: it is not part of the step
+    vir = torch.empty((3, 3), dtype=ctx.dtype, device=dev)
+    ws_v = ctx._workspace(ctx.workspace_bytes(tpc.OP_VIRIAL, N), dev)
+    for _ in range(2):
+        ctx.virial(pos, cell, nl, g_edge, out=vir, workspace=ws_v)
+    torch.cuda.synchronize()
+    tpc.timing_enable(True)
+    for _ in range(a.steps):
+        ctx.virial(pos, cell, nl, g_edge, out=vir, workspace=ws_v)
+    torch.cuda.synchronize()
+    tpc.timing_enable(False)
+    vt = tpc.timing_collect()
+    virial_ms = vt["virial"][0] / vt["virial"][1] if "virial" in vt else None
     # one launch of each per pass (the weight packing runs once in each pass)
     fwd_ms = sum(per_kernel.get(n, {}).get("avg_ms", 0.0)
                  for n in ("geom_fwd", "radial_pack", "radial_fwd", "tp_fwd"))
@@ -364,8 +380,7 @@ def main(argv=None):
 
     cpu = None
     if not a.no_cpu_baseline:
-        rp, src, shift = (nl.row_ptr.cpu().numpy(), nl.src.cpu().numpy(), nl.shift.cpu().numpy())
-        cpu = cpu_baseline(d, (rp, src, shift), a.cpu_budget)
+        cpu = cpu_baseline(d, a.cpu_budget)
 
     line = {
         "metric": "edges/s fwd and fwd+bwd, 128ch sh l<=3 TP conv; % of HBM roofline",
@@ -392,6 +407,7 @@ def main(argv=None):
         "fwd_edges_per_s": E / (fwd_ms * 1e-3) if fwd_ms else None,
         "fwd_bwd_edges_per_s": E / ((fwd_ms + bwd_ms) * 1e-3) if fwd_ms else None,
         "nbr_build_ms": nbr_ms,
+        "virial_ms": virial_ms,
         "kernels": kernels,
         "tp_groups_hbm": group_rooflines(per_kernel, N, E, cfg, ctx),
         "wall_s": wall,

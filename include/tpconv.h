@@ -76,7 +76,7 @@ typedef enum tpc_status {
 } tpc_status;
 
 enum { TPC_F32 = 0, TPC_F64 = 1 };
-enum { TPC_OP_NBR = 0, TPC_OP_FWD = 1, TPC_OP_BWD = 2 };
+enum { TPC_OP_NBR = 0, TPC_OP_FWD = 1, TPC_OP_BWD = 2, TPC_OP_VIRIAL = 3 };
 
 #define TPC_MAX_LAYERS 8
 #define TPC_MAX_PATHS 32
@@ -137,7 +137,8 @@ tpc_status tpc_ctx_info(const tpc_ctx* ctx, tpc_info* info);
 tpc_status tpc_cg_table(const tpc_ctx* ctx, int path, double* out, size_t n);
 
 /* Workspace bytes for an operation: TPC_OP_NBR needs n_atoms and the host
- * cell; TPC_OP_FWD and TPC_OP_BWD need the number of edges of the chunk. */
+ * cell; TPC_OP_FWD and TPC_OP_BWD need the number of edges of the chunk;
+ * TPC_OP_VIRIAL needs n_atoms. */
 tpc_status tpc_workspace_query(const tpc_ctx* ctx, int op, int64_t n_atoms,
                                int64_t n_edges, const double* cell, size_t* bytes);
 
@@ -219,6 +220,27 @@ tpc_status tpc_conv_bwd(const tpc_ctx* ctx, int64_t n_atoms, int64_t n_edges,
                         double scale, const void* grad_out, const tpc_edge_buffers* eb,
                         void* dR, void* g_edge, void* dh_edge, void* dh, void* forces,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Virial of L: W[a][b] = dL/d(eps_ab) for a homogeneous strain
+ * x -> (I + eps) x applied to the positions and the cell rows together.  This
+ * is the strain derivative the pet-jax README ("Conventions") calls the
+ * virial, from one structure's strained cell as in the Stress option of
+ * FastMACE's "Rewrites and precision options"; the stress of a structure of
+ * volume V is W / V.  With the list fixed every edge vector becomes
+ * (I + eps) r_e, so W[a][b] = sum_e g_e[a] r_e[b], with r_e formed in float64
+ * exactly as tpc_nbr_build forms it.
+ *   pos, cell, row_ptr, src, shift   as for tpc_conv_fwd, all n_atoms rows
+ *   g_edge    [n_edges][3] device: dL/dr_e from tpc_conv_bwd (every chunk's
+ *             edges written earlier on this stream)
+ *   virial    [3][3] device, out: row-major W in the context dtype (zero for
+ *             a list without edges)
+ * The sums run in float64 in a fixed order (each row in CSR order, then fixed
+ * trees over rows and blocks): deterministic, no atomics.  With
+ * spec.validate the CSR is checked first (TPC_ERR_PRECONDITION). */
+tpc_status tpc_virial(const tpc_ctx* ctx, int64_t n_atoms, int64_t n_edges, const double* pos,
+                      const double* cell, const int32_t* row_ptr, const int32_t* src,
+                      const int32_t* shift, const void* g_edge, void* virial,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-kernel timing with HIP events, for benchmarks and profiling.  While
  * enabled on a thread, every kernel the library launches from that thread is

@@ -20,13 +20,14 @@ import os
 from dataclasses import dataclass, field
 
 __all__ = ["Spec", "Context", "NeighbourList", "EdgeBuffers", "TpcError", "library",
-           "nbr_build", "conv_fwd", "conv_bwd", "timing_enable", "timing_collect", "LIB_PATH"]
+           "nbr_build", "conv_fwd", "conv_bwd", "virial", "timing_enable", "timing_collect",
+           "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpconv.so")
 
 TPC_MAX_LAYERS = 8
 TPC_MAX_PATHS = 32
-OP_NBR, OP_FWD, OP_BWD = 0, 1, 2
+OP_NBR, OP_FWD, OP_BWD, OP_VIRIAL = 0, 1, 2, 3
 STATUS = {0: "ok", 1: "invalid", 2: "unsupported", 3: "capacity", 4: "precondition",
           5: "workspace", 6: "device"}
 
@@ -91,6 +92,8 @@ def library():
                                  ctypes.POINTER(_VP), ctypes.c_double, _VP,
                                  ctypes.POINTER(_EdgeBuffers), _VP, _VP, _VP, _VP, _VP, _VP,
                                  ctypes.c_size_t, _VP]
+    lib.tpc_virial.argtypes = [_VP, _I64, _I64, _VP, ctypes.POINTER(ctypes.c_double), _VP, _VP, _VP,
+                               _VP, _VP, _VP, ctypes.c_size_t, _VP]
     lib.tpc_timing_enable.argtypes = [ctypes.c_int]
     lib.tpc_timing_collect.argtypes = [ctypes.POINTER(_KernelTime), ctypes.c_int,
                                        ctypes.POINTER(ctypes.c_int)]
@@ -99,7 +102,7 @@ def library():
     lib.tpc_last_error.argtypes = []
     lib.tpc_last_error.restype = ctypes.c_char_p
     for name in ("tpc_ctx_create", "tpc_ctx_info", "tpc_cg_table", "tpc_workspace_query",
-                 "tpc_nbr_build", "tpc_conv_fwd", "tpc_conv_bwd", "tpc_timing_enable",
+                 "tpc_nbr_build", "tpc_conv_fwd", "tpc_conv_bwd", "tpc_virial", "tpc_timing_enable",
                  "tpc_timing_collect"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
@@ -344,6 +347,25 @@ class Context:
                                       _ptr(dR), _ptr(g_edge), _ptr(dh_edge), _ptr(dh), _ptr(forces),
                                       _ptr(ws), ws.numel(), _stream()))
         return dh, dR, forces, g_edge
+
+    # ---- virial ----------------------------------------------------------------
+    def virial(self, pos, cell, nl: NeighbourList, g_edge, out=None, workspace=None):
+        """W [3, 3] = dL/d(strain) = sum_e g_e r_e^T from the edge gradients of
+        conv_bwd (every edge written)."""
+        t = _torch()
+        N = pos.shape[0]
+        if out is None:
+            out = t.empty((3, 3), dtype=self.dtype, device=pos.device)
+        ws = workspace if workspace is not None else \
+            self._workspace(self.workspace_bytes(OP_VIRIAL, N), pos.device)
+        _check(library().tpc_virial(self._h, N, nl.n_edges, _ptr(pos), _cell_arg(cell),
+                                    _ptr(nl.row_ptr), _ptr(nl.src), _ptr(nl.shift), _ptr(g_edge),
+                                    _ptr(out), _ptr(ws), ws.numel(), _stream()))
+        return out
+
+
+def virial(ctx: Context, *a, **k):
+    return ctx.virial(*a, **k)
 
 
 def nbr_build(ctx: Context, *a, **k):

@@ -220,6 +220,21 @@ FwdWs fwd_layout(const tpc_ctx* c) {
   return w;
 }
 
+struct VirialWs {
+  size_t status, part, total;
+};
+
+VirialWs virial_layout(int64_t n) {
+  VirialWs w{};
+  size_t off = 0;
+  w.status = off;
+  off += align_up(sizeof(int32_t) * 8);
+  w.part = off;
+  off += align_up(sizeof(double) * 9 * (size_t)tpc::virial_blocks(n));
+  w.total = off;
+  return w;
+}
+
 int waves_per_row(int C) { return C <= 64 ? 1 : C / 64; }
 
 BwdWs bwd_layout(const tpc_ctx* c, int64_t ne) {
@@ -437,6 +452,8 @@ tpc_status tpc_workspace_query(const tpc_ctx* c, int op, int64_t n_atoms, int64_
     *bytes = fwd_layout(c).total;
   } else if (op == TPC_OP_BWD) {
     *bytes = bwd_layout(c, n_edges).total;
+  } else if (op == TPC_OP_VIRIAL) {
+    *bytes = virial_layout(n_atoms).total;
   } else {
     E.add(TPC_ERR_INVALID, "unknown op %d", op);
   }
@@ -789,6 +806,66 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
                "conv_bwd: dh row sums");
   if (forces)
     TPC_LAUNCH("forces", s, tpc::launch_forces(dt, n, row_ptr, rev, g_edge, forces, s), "conv_bwd: forces");
+  g_last_error.clear();
+  return TPC_OK;
+}
+
+tpc_status tpc_virial(const tpc_ctx* c, int64_t n, int64_t n_edges, const double* pos,
+                      const double* cell, const int32_t* row_ptr, const int32_t* src,
+                      const int32_t* shift, const void* g_edge, void* virial, void* ws,
+                      size_t ws_bytes, void* stream) {
+  Errors E;
+  if (!c) {
+    E.add(TPC_ERR_INVALID, "ctx must be non-null");
+    return E.finish();
+  }
+  if (n < 0) E.add(TPC_ERR_INVALID, "n_atoms must be >= 0");
+  if (n_edges < 0) E.add(TPC_ERR_INVALID, "n_edges must be >= 0");
+  if (n_edges > 0 && n == 0) E.add(TPC_ERR_INVALID, "edges need atoms");
+  if (!cell) E.add(TPC_ERR_INVALID, "cell (host double[9]) must be non-null");
+  else
+    for (int k = 0; k < 9; ++k)
+      if (!std::isfinite(cell[k])) {
+        E.add(TPC_ERR_INVALID, "cell must be finite");
+        break;
+      }
+  need_ptr(row_ptr, "row_ptr", 4, E);
+  if (n_edges > 0) {
+    need_ptr(pos, "pos", 8, E);
+    need_ptr(src, "src", 4, E);
+    need_ptr(shift, "shift", 4, E);
+    need_ptr(g_edge, "g_edge", c->tsize, E);
+  }
+  need_ptr(virial, "virial", c->tsize, E);
+  const VirialWs L = virial_layout(n > 0 ? n : 0);
+  if (!ws) E.add(TPC_ERR_INVALID, "workspace must be non-null");
+  else if (!aligned(ws, 256)) E.add(TPC_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (ws && ws_bytes < L.total) E.add(TPC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  tpc_status st = E.finish();
+  if (st != TPC_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  if (c->spec.validate && n > 0) {
+    st = run_csr_check(n, n_edges, row_ptr, src, shift, 0, n, 0, n_edges,
+                       reinterpret_cast<int32_t*>(w + L.status), s);
+    if (st != TPC_OK) return st;
+  }
+  tpc::GeomArgs ga{};
+  ga.pos = pos;
+  for (int r = 0; r < 3; ++r)
+    for (int k = 0; k < 3; ++k) ga.cell[r][k] = cell[3 * r + k];
+  ga.row_ptr = row_ptr;
+  ga.src = src;
+  ga.shift = shift;
+  ga.row_begin = 0;
+  ga.row_end = n;
+  ga.edge_begin = 0;
+  ga.edge_end = n_edges;
+  TPC_LAUNCH("virial", s,
+             tpc::launch_virial(c->spec.dtype, n, ga, g_edge, reinterpret_cast<double*>(w + L.part),
+                                virial, s),
+             "virial");
   g_last_error.clear();
   return TPC_OK;
 }

@@ -84,7 +84,96 @@ k_csr_check(int64_t n, int64_t n_edges, const int32_t* __restrict__ row_ptr,
   if (flags) atomicOr(status, flags);
 }
 
+// Virial W[a][b] = dL/d(eps_ab) for the strain x -> (I + eps) x of the
+// positions and the cell rows (the pet-jax README, "Conventions": the virial
+// is the strain derivative of the energy).  With the list fixed every edge
+// vector becomes (I + eps) r_e, so W[a][b] = sum_e g_e[a] r_e[b].  r_e is
+// formed in float64 exactly as the neighbour build forms it.  One thread per
+// row sums its edges in CSR order in float64; each block folds its rows' sums
+// with a fixed tree in LDS into one partial; one block then folds the
+// partials the same way.  Deterministic, no atomics.
+template <typename T>
+__global__ void __launch_bounds__(kVirialBlock)
+k_virial_rows(int64_t n, GeomArgs a, const T* __restrict__ g, double* __restrict__ part) {
+  __shared__ double sm[9][kVirialBlock];
+  const int t = threadIdx.x;
+  const int64_t i = blockIdx.x * (int64_t)kVirialBlock + t;
+  double w[9];
+#pragma unroll
+  for (int c = 0; c < 9; ++c) w[c] = 0.0;
+  if (i < n) {
+    for (int e = a.row_ptr[i]; e < a.row_ptr[i + 1]; ++e) {
+#pragma clang fp contract(off)
+      const int j = a.src[e];
+      const double S1 = (double)a.shift[3 * e], S2 = (double)a.shift[3 * e + 1],
+                   S3 = (double)a.shift[3 * e + 2];
+      double r[3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        r[k] = (a.pos[3 * j + k] - a.pos[3 * i + k]) +
+               ((S1 * a.cell[0][k] + S2 * a.cell[1][k]) + S3 * a.cell[2][k]);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const double gp = (double)g[3 * (int64_t)e + p];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) w[3 * p + q] += gp * r[q];
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 9; ++c) sm[c][t] = w[c];
+  __syncthreads();
+  for (int h = kVirialBlock / 2; h > 0; h >>= 1) {
+    if (t < h) {
+#pragma unroll
+      for (int c = 0; c < 9; ++c) sm[c][t] += sm[c][t + h];
+    }
+    __syncthreads();
+  }
+  if (t < 9) part[blockIdx.x * (int64_t)9 + t] = sm[t][0];
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kVirialBlock)
+k_virial_sum(int64_t nblk, const double* __restrict__ part, T* __restrict__ W) {
+  __shared__ double sm[9][kVirialBlock];
+  const int t = threadIdx.x;
+  double w[9];
+#pragma unroll
+  for (int c = 0; c < 9; ++c) w[c] = 0.0;
+  for (int64_t b = t; b < nblk; b += kVirialBlock) {
+#pragma unroll
+    for (int c = 0; c < 9; ++c) w[c] += part[b * 9 + c];
+  }
+#pragma unroll
+  for (int c = 0; c < 9; ++c) sm[c][t] = w[c];
+  __syncthreads();
+  for (int h = kVirialBlock / 2; h > 0; h >>= 1) {
+    if (t < h) {
+#pragma unroll
+      for (int c = 0; c < 9; ++c) sm[c][t] += sm[c][t + h];
+    }
+    __syncthreads();
+  }
+  if (t < 9) W[t] = (T)sm[t][0];
+}
+
 }  // namespace
+
+hipError_t launch_virial(int dtype, int64_t n, const GeomArgs& a, const void* g, double* part,
+                         void* W, hipStream_t s) {
+  const int64_t nblk = virial_blocks(n);
+  if (dtype == 1) {
+    if (nblk > 0)
+      k_virial_rows<double><<<(unsigned)nblk, kVirialBlock, 0, s>>>(n, a, static_cast<const double*>(g), part);
+    k_virial_sum<double><<<1, kVirialBlock, 0, s>>>(nblk, part, static_cast<double*>(W));
+  } else {
+    if (nblk > 0)
+      k_virial_rows<float><<<(unsigned)nblk, kVirialBlock, 0, s>>>(n, a, static_cast<const float*>(g), part);
+    k_virial_sum<float><<<1, kVirialBlock, 0, s>>>(nblk, part, static_cast<float*>(W));
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_forces(int dtype, int64_t n, const int32_t* row_ptr, const int32_t* rev,
                          const void* g, void* forces, hipStream_t s) {

@@ -119,6 +119,11 @@ hipError_t launch_dh_gather(int dtype, int64_t n, int din_c, const int32_t* row_
 
 hipError_t launch_forces(int dtype, int64_t n, const int32_t* row_ptr, const int32_t* rev,
                          const void* g, void* forces, hipStream_t s);
+// Virial: float64 partial sums per block of kVirialBlock rows, then one fold.
+constexpr int kVirialBlock = 256;
+inline int64_t virial_blocks(int64_t n) { return n > 0 ? (n + kVirialBlock - 1) / kVirialBlock : 0; }
+hipError_t launch_virial(int dtype, int64_t n, const GeomArgs& a, const void* g, double* part,
+                         void* W, hipStream_t s);
 hipError_t launch_csr_check(int64_t n, int64_t n_edges, const int32_t* row_ptr,
                             const int32_t* src, const int32_t* shift, int64_t row_begin,
                             int64_t row_end, int64_t edge_begin, int64_t edge_end,

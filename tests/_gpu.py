@@ -60,6 +60,14 @@ class Case:
     def scale(self, nl):
         return conv.scale_for(self.cfg, self.N, nl.n_edges)
 
+    def oracle_csr(self):
+        """The oracle's own neighbour list (binned build, itself pinned to
+        brute force), computed once per case."""
+        if getattr(self, "_csr", None) is None:
+            say(f"[cpu] oracle neighbour list cfg={self.k}")
+            self._csr = nbr.binned(self.d["pos"], self.cell, self.cfg["r_cut"])
+        return self._csr
+
     def oracle(self, nl_np):
         rp, src, shift = nl_np
         return conv.Problem(self.layout, self.d["pos"], self.cell, rp, src, shift, self.d["h"],

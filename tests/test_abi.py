@@ -139,6 +139,19 @@ def test_conv_argument_checks_run_before_device_work():
         assert needle in m
 
 
+def test_virial_argument_checks_run_before_device_work():
+    ctx = tpc.Context(_spec())
+    lib, h = _raw(ctx)
+    cell = (ctypes.c_double * 9)(*([float("inf")] + [0.0] * 8))
+    st = lib.tpc_virial(h, 10, 5, None, cell, None, None, None, None, None, None, 0, None)
+    assert st == 1
+    m = lib.tpc_last_error().decode()
+    for needle in ("cell must be finite", "row_ptr", "pos", "src", "shift", "g_edge", "virial",
+                   "workspace"):
+        assert needle in m
+    assert ctx.workspace_bytes(tpc.OP_VIRIAL, 1000) >= 4 * 9 * 8   # 4 blocks of float64 partials
+
+
 def test_status_strings():
     lib = tpc.library()
     assert lib.tpc_status_string(3) == b"edge capacity too small"

@@ -6,14 +6,18 @@ import pytest
 
 import tensor_product_conv_amd as tpc
 from _gpu import TOL, Case, np_csr, rel, run_chunked, say, torch
-from oracle import conv
+from oracle import conv, nbr
 
 pytestmark = pytest.mark.gpu
 
 
 def _prob(case, nl):
-    rp, src, shift, _ = np_csr(nl)
-    return case.oracle((rp, src, shift))
+    """Oracle problem on the oracle's own neighbour list.  Per-edge outputs
+    are compared edge by edge, so the GPU list must be the same arrays."""
+    ref = case.oracle_csr()
+    for a, b in zip(np_csr(nl)[:3], ref):
+        np.testing.assert_array_equal(a, b)
+    return case.oracle(ref)
 
 
 # 0 tiny (float64), 1 small; 5-7 are the small system at other channel and
@@ -58,8 +62,8 @@ def _sampled_check(case, nl, res, rows, atoms, edges):
     assert rel(res["forces"][atoms].cpu().numpy(), prob.forces_atoms(atoms)) < tol
 
 
-def _samples(nl, N, n_rows, seed):
-    rp = nl.row_ptr.cpu().numpy()
+def _samples(case, n_rows, seed):
+    rp, N = case.oracle_csr()[0], case.N
     rng = np.random.default_rng(seed)
     rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, n_rows, replace=False)]))
     edges = np.concatenate([np.arange(rp[i], rp[i + 1]) for i in rows[:16]])
@@ -69,16 +73,17 @@ def _samples(nl, N, n_rows, seed):
 def test_medium_parity_sampled():
     case = Case(3)
     nl = case.nbr()
-    rows, edges = _samples(nl, case.N, 96, 11)
+    rows, edges = _samples(case, 96, 11)
     atoms = np.unique(np.concatenate([np.arange(64), rows[:32]]))   # includes the 0-63 slice
     res = run_chunked(case, nl, chunks=1, keep_edges=edges)
     _sampled_check(case, nl, res, rows, atoms, edges)
 
 
+@pytest.mark.timeout(300)   # the oracle's own 19.6 M-edge list takes about 40 s
 def test_large_parity_sampled_chunked():
     case = Case(4)
     nl = case.nbr()
-    rows, edges = _samples(nl, case.N, 40, 12)
+    rows, edges = _samples(case, 40, 12)
     res = run_chunked(case, nl, chunks=3, keep_edges=edges)
     _sampled_check(case, nl, res, rows, rows[:24], edges)
 
@@ -137,6 +142,45 @@ def test_validation_refuses_an_unsorted_csr():
     torch().cuda.synchronize()
 
 
+@pytest.mark.parametrize("k", [0, 1])
+def test_virial_parity(k):
+    """The virial kernel on the oracle's own edge gradients (same inputs), and
+    end to end from the GPU's edge gradients."""
+    t = torch()
+    case = Case(k)
+    nl = case.nbr()
+    tol = TOL[case.cfg["dtype"]]
+    res = run_chunked(case, nl, chunks=1)
+    prob = _prob(case, nl)
+    say(f"[cpu] oracle backward cfg={k}")
+    b = prob.backward()
+    g_in = t.tensor(b["g"], dtype=case.ctx.dtype, device="cuda")
+    say(f"[gpu] virial cfg={k} on the oracle's edge gradients")
+    W1 = case.ctx.virial(case.pos, case.cell, nl, g_in)
+    ref1 = conv.virial(prob.rvec(np.arange(nl.n_edges)), g_in.cpu().double().numpy())
+    assert rel(W1.cpu().numpy(), ref1) < tol
+    say(f"[gpu] virial cfg={k} on its own edge gradients")
+    W2 = case.ctx.virial(case.pos, case.cell, nl, res["g_edge"])
+    assert rel(W2.cpu().numpy(), prob.virial_from(b["g"])) < tol
+
+
+def test_virial_medium_size():
+    """Full-size virial on seeded edge gradients (its only input besides the
+    list and positions) against the oracle's sum over its own edge vectors."""
+    t = torch()
+    case = Case(3, with_grad=False)
+    nl = case.nbr()
+    rp, src, shift = case.oracle_csr()
+    for a, b in zip(np_csr(nl)[:3], (rp, src, shift)):
+        np.testing.assert_array_equal(a, b)
+    g = t.tensor(np.random.default_rng(31).standard_normal((len(src), 3)), dtype=case.ctx.dtype,
+                 device="cuda")
+    say("[gpu] virial medium")
+    W = case.ctx.virial(case.pos, case.cell, nl, g).cpu().numpy()
+    vec = nbr.edge_vectors(case.d["pos"], case.cell, nbr.receivers_of(rp), src, shift)
+    assert rel(W, conv.virial(vec, g.cpu().double().numpy())) < TOL[case.cfg["dtype"]]
+
+
 def test_empty_rows_and_zero_edges():
     t = torch()
     case = Case(0)
@@ -152,12 +196,17 @@ def test_empty_rows_and_zero_edges():
     t.cuda.synchronize()
     assert float(out[1].abs().max()) == 0.0 and float(dh[1].abs().max()) == 0.0
     assert float(F[1].abs().max()) == 0.0
-    prob = conv.Problem(case.layout, pos.cpu().numpy(), cell, *[x.cpu().numpy() for x in
-                        (nl.row_ptr, nl.src, nl.shift)], h.cpu().numpy(), case.d["W"], 4.0, 1.0,
-                        G.cpu().numpy())
+    pos_np = np.array([[1.0, 1.0, 1.0], [7.0, 7.0, 7.0], [1.5, 1.0, 1.0]])
+    ref = nbr.brute_force(pos_np, cell, 4.0)
+    for a, b_ in zip(np_csr(nl)[:3], ref):
+        np.testing.assert_array_equal(a, b_)
+    prob = conv.Problem(case.layout, pos_np, cell, *ref, case.d["h"][:3], case.d["W"], 4.0, 1.0,
+                        case.d["G"][:3])
     assert rel(out.cpu().numpy(), prob.forward()) < 1e-10
     b = prob.backward()
     assert rel(F.cpu().numpy(), b["F"]) < 1e-10
+    W = ctx.virial(pos, cell, nl, g)
+    assert rel(W.cpu().numpy(), prob.virial_from(b["g"])) < 1e-10
     # no edges at all
     pos2 = t.tensor([[1.0, 1.0, 1.0], [9.0, 9.0, 9.0]], dtype=t.float64, device="cuda")
     nl2 = ctx.nbr_build(pos2, cell)
@@ -167,3 +216,6 @@ def test_empty_rows_and_zero_edges():
     t.cuda.synchronize()
     assert float(out2.abs().max()) == 0.0 and float(dh2.abs().max()) == 0.0
     assert float(F2.abs().max()) == 0.0
+    W2 = ctx.virial(pos2, cell, nl2, t.empty((0, 3), dtype=ctx.dtype, device="cuda"))
+    t.cuda.synchronize()
+    assert float(W2.abs().max()) == 0.0
