@@ -66,6 +66,27 @@ __device__ __forceinline__ void stc(T* __restrict__ base, uint32_t off, bool on,
   }
 }
 
+// Streams touched once (R, dR, the per-edge dh contributions) go through
+// non-temporal accesses, so they displace less of the sender features that
+// the gathers of neighbouring rows reuse from L2.
+template <int NW, typename T>
+__device__ __forceinline__ T ldc_nt(const T* __restrict__ base, uint32_t off, bool on) {
+  if constexpr (NW > 0) {
+    return __builtin_nontemporal_load(base + off);
+  } else {
+    return on ? __builtin_nontemporal_load(base + off) : T(0);
+  }
+}
+
+template <int NW, typename T>
+__device__ __forceinline__ void stc_nt(T* __restrict__ base, uint32_t off, bool on, T v) {
+  if constexpr (NW > 0) {
+    __builtin_nontemporal_store(v, base + off);
+  } else {
+    if (on) __builtin_nontemporal_store(v, base + off);
+  }
+}
+
 // Value held by lane k of v, for every lane (v_readlane; k is uniform).
 __device__ __forceinline__ float lane_value(float v, int k) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), k));
@@ -196,6 +217,19 @@ __device__ __forceinline__ void ld_vec(const T* __restrict__ base, uint32_t off,
 }
 
 template <typename T, int CPL>
+__device__ __forceinline__ void ld_vec_nt(const T* __restrict__ base, uint32_t off, bool on, T (&v)[CPL],
+                                          bool masked) {
+  if constexpr (CPL == 1) {
+    v[0] = (!masked || on) ? __builtin_nontemporal_load(base + off) : T(0);
+  } else {
+    using V = T __attribute__((ext_vector_type(CPL)));
+    const V x = __builtin_nontemporal_load(reinterpret_cast<const V*>(base + off));
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) v[c] = x[c];
+  }
+}
+
+template <typename T, int CPL>
 __device__ __forceinline__ void st_vec(T* __restrict__ base, uint32_t off, bool on, const T (&v)[CPL],
                                        bool masked) {
   if constexpr (CPL == 1) {
@@ -285,7 +319,7 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
     for (int m = 0; m < DIN; ++m) ld_vec<T, CPL>(hj, m * C + c0, on, b.h[m], MASKED);
     static_for<NP>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
-      if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) ld_vec<T, CPL>(re, p * C + c0, on, b.r[p], MASKED);
+      if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) ld_vec_nt<T, CPL>(re, p * C + c0, on, b.r[p], MASKED);
     });
     b.y = Y[((int64_t)e - edge_begin) * DSH + ylane];
   };
@@ -481,7 +515,7 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
 #pragma unroll
     for (int m = 0; m < DIN; ++m) b.h[m] = ldc<NW>(hj, m * CC + c0, rw.on);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) b.r[p] = ldc<NW>(re, p * CC + c0, rw.on);
+    for (int p = 0; p < NP; ++p) b.r[p] = ldc_nt<NW>(re, p * CC + c0, rw.on);
     b.y = Y[((int64_t)e - edge_begin) * DSH + ylane];
     b.er = er;
   };
@@ -538,11 +572,11 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
         });
         dy[P.l2 * P.l2 + m2] += b.r[p] * q;
       });
-      stc<NW>(dre, p * CC + c0, rw.on, scale * dr);
+      stc_nt<NW>(dre, p * CC + c0, rw.on, scale * dr);
     });
     T* __restrict__ te = dh_edge + (int64_t)b.er * DIN * CC;
 #pragma unroll
-    for (int m = 0; m < DIN; ++m) stc<NW>(te, m * CC + c0, rw.on, t[m]);
+    for (int m = 0; m < DIN; ++m) stc_nt<NW>(te, m * CC + c0, rw.on, t[m]);
     // every lane of a quad holds the same total, so with 16 harmonics all
     // lanes store (identical values per address) and the store needs no
     // branch, which keeps the wait for the next edge's loads exact
