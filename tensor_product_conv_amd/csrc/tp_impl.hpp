@@ -601,7 +601,8 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
 // contribution of the reverse edge (whose sender is j), so the sum runs over a
 // contiguous range in CSR order (deterministic, no atomics).  One thread per
 // (atom, group of V consecutive feature values); every value is summed over
-// the row's edges in CSR order, V at a time, with four edges' loads in flight.
+// the row's edges in CSR order, V at a time, with eight edges' loads in
+// flight (non-temporal: each value is read once).
 template <typename T, int V>
 __global__ void __launch_bounds__(256)
 k_dh_gather(int64_t n, int din_c, const int32_t* __restrict__ row_ptr, T scale,
@@ -616,15 +617,13 @@ k_dh_gather(int64_t n, int din_c, const int32_t* __restrict__ row_ptr, T scale,
   const int lo = row_ptr[j], hi = row_ptr[j + 1];
   const T* __restrict__ p = dh_edge + q;
   int e = lo;
-  for (; e + 4 <= hi; e += 4) {
-    const vec a = *reinterpret_cast<const vec*>(p + (int64_t)e * din_c);
-    const vec b = *reinterpret_cast<const vec*>(p + (int64_t)(e + 1) * din_c);
-    const vec c = *reinterpret_cast<const vec*>(p + (int64_t)(e + 2) * din_c);
-    const vec d = *reinterpret_cast<const vec*>(p + (int64_t)(e + 3) * din_c);
-    acc += a;
-    acc += b;
-    acc += c;
-    acc += d;
+  for (; e + 8 <= hi; e += 8) {
+    vec a[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      a[k] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(p + (int64_t)(e + k) * din_c));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += a[k];
   }
   for (; e < hi; ++e) acc += *reinterpret_cast<const vec*>(p + (int64_t)e * din_c);
   *reinterpret_cast<vec*>(dh + j * din_c + q) = scale * acc;
