@@ -12,6 +12,11 @@ ranks first, channels contiguous):
   h   [N][d_in][C]   l1 blocks ascending, m1 = -l1..l1 inside a block
   out [N][d_out][C]  l3 blocks ascending; inside the l3 block the order is
                      (m3, q, channel) where q ranks the paths with that l3
+
+Path-summed output (FlashCart §3 "Generating Cartesian tensor products": the
+kernels may sum the paths that share an output rank): every path with a
+given l3 adds into one row block, so d_out = sum over the l3 values that
+occur of (2 l3 + 1), with (m3, channel) order inside a block.
 """
 from __future__ import annotations
 
@@ -36,6 +41,7 @@ class Layout:
     sh_lmax: int
     out_lmax: int
     C: int
+    sum_paths: bool = False
     paths: list = field(init=False)
 
     def __post_init__(self):
@@ -53,8 +59,13 @@ class Layout:
     def d_sh(self):
         return (self.sh_lmax + 1) ** 2
 
+    def _out_l3(self):
+        return sorted({l3 for (_, _, l3) in self.paths})
+
     @property
     def d_out(self):
+        if self.sum_paths:
+            return sum(2 * l3 + 1 for l3 in self._out_l3())
         return sum(2 * l3 + 1 for (_, _, l3) in self.paths)
 
     def in_slice(self, l1):
@@ -66,6 +77,9 @@ class Layout:
     def out_rows(self, p):
         """Output row index of (path p, m3) for m3 = 0..2 l3."""
         l3 = self.paths[p][2]
+        if self.sum_paths:
+            base = sum(2 * l + 1 for l in self._out_l3() if l < l3)
+            return [base + m3 for m3 in range(2 * l3 + 1)]
         base = sum((2 * l + 1) * sum(1 for q in self.paths if q[2] == l)
                    for l in range(l3))
         same = [k for k, q in enumerate(self.paths) if q[2] == l3]

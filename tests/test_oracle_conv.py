@@ -75,6 +75,49 @@ def test_virial_two_atom_closed_form():
     np.testing.assert_allclose(W, Wfd, rtol=0, atol=1e-8 * abs(mag))
 
 
+@pytest.fixture(scope="module")
+def tiny_summed():
+    """The tiny system with path-summed outputs and its own upstream gradient."""
+    d = workloads.generate(0)
+    c = d["cfg"]
+    L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"], sum_paths=True)
+    rp, src, shift = nbr.binned(d["pos"], d["cell"], c["r_cut"])
+    G = np.random.default_rng(8).standard_normal((c["N"], L.d_out, c["C"]))
+    prob = conv.Problem(L, d["pos"], d["cell"], rp, src, shift, d["h"], d["W"], c["r_cut"], 1.0, G)
+    return prob, d
+
+
+def test_summed_layout_sums_the_paths_of_each_rank(tiny_summed):
+    """Each l3 block of the summed output is the sum of that rank's path
+    blocks of the separate output (whose layout the closed forms pin)."""
+    prob, d = tiny_summed
+    Ls = prob.L
+    assert Ls.d_out == sum(2 * l + 1 for l in sorted({p[2] for p in Ls.paths}))
+    sep = conv.Problem(paths.Layout(Ls.l1max, Ls.sh_lmax, Ls.out_lmax, Ls.C), prob.pos, prob.cell,
+                       prob.row_ptr, prob.src, prob.shift, d["h"], d["W"], prob.r_cut, 1.0)
+    out_sep, out_sum = sep.forward(), prob.forward()
+    ref = np.zeros_like(out_sum)
+    for p in range(Ls.n_paths):
+        ref[:, Ls.out_rows(p)] += out_sep[:, sep.L.out_rows(p)]
+    np.testing.assert_allclose(out_sum, ref, rtol=0, atol=1e-13 * np.abs(ref).max())
+
+
+def test_summed_layout_backward(tiny_summed):
+    """Backward with summed outputs: autograd of the independent torch
+    forward, 5-point difference forces, and <dh, h> = L."""
+    from oracle import autograd_check as ag
+    prob, d = tiny_summed
+    b = prob.backward()
+    a = ag.grads(prob.L, prob.pos, prob.cell, prob.row_ptr, prob.src, prob.shift, d["h"], d["W"],
+                 prob.G, prob.r_cut, prob.scale)
+    for k in ("dh", "dR", "dY", "F"):
+        np.testing.assert_allclose(b[k], a[k], rtol=0, atol=1e-12 * np.abs(a[k]).max())
+    F = fd.fd_forces(prob, np.arange(len(prob.pos)), delta=1e-3)
+    assert np.abs(F - b["F"]).max() / np.abs(b["F"]).max() < 1e-7
+    L = float((prob.G * prob.forward()).sum())
+    assert abs(float((b["dh"] * d["h"]).sum()) - L) < 1e-10 * abs(L)
+
+
 def test_linearity_identities(tiny):
     # L is linear in each of h, R and Y separately
     prob, d, out, b = tiny
