@@ -254,7 +254,7 @@ def cpu_baseline(case_data, budget_s=10.0):
     d = case_data
     c = d["cfg"]
     rp, src, shift = nbr.binned(d["pos"], d["cell"], c["r_cut"])
-    L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"])
+    L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"], c.get("sum_paths", False))
     _CPU_PROB = conv.Problem(L, d["pos"], d["cell"], rp, src, shift, d["h"], d["W"], c["r_cut"],
                              conv.scale_for(c, len(d["pos"]), rp[-1]), d["G"])
     order = np.random.default_rng(0).permutation(len(d["pos"]))
@@ -285,6 +285,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="medium", choices=["medium", "small"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sum-paths", action="store_true",
+                    help="path-summed outputs (one block per output rank) on the same system")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, copy %d bytes device to device three times "
@@ -310,6 +312,11 @@ def main(argv=None):
     k = {"small": 1, "medium": 3}[a.workload]
     d = workloads.generate(k)
     cfg = d["cfg"]
+    if a.sum_paths:
+        cfg = dict(cfg, sum_paths=True, name=cfg["name"] + "_summed")
+        cfg["d_out"] = tpc.Context(tpc.spec_for(cfg)).d_out   # host only, no device call
+        d = dict(d, cfg=cfg, G=np.random.default_rng(cfg["seed"] + 100).standard_normal(
+            (cfg["N"], cfg["d_out"], cfg["C"])).astype(d["G"].dtype))
     # the CPU leg forks its workers, so it runs before anything touches the GPU
     cpu = None if a.no_cpu_baseline else cpu_baseline(d, a.cpu_budget)
     dev = "cuda"
@@ -419,7 +426,8 @@ def main(argv=None):
                                f"N={N} E={E} C={cfg['C']} node_lmax={cfg['l1max']} "
                                f"sh_lmax={cfg['sh_lmax']} out_lmax={cfg['out_lmax']} "
                                f"mlp={'-'.join(map(str, cfg['layer_dims']))}: "
-                               "nbr_build + conv_fwd + conv_bwd (forces)",
+                               "nbr_build + conv_fwd + conv_bwd (forces)"
+                               + (", path-summed outputs" if cfg.get("sum_paths") else ""),
                    "n_atoms": N, "n_edges": E, "channels": cfg["C"], "paths": ctx.n_paths,
                    "parallelism": "single GPU"},
         "roofline": roof,

@@ -38,7 +38,9 @@
  *      h, dh      [N][d_in][C]   l1 blocks ascending, m1 = -l1..l1
  *      out, G     [N][d_out][C]  l3 blocks ascending; inside an l3 block the
  *                                order is (m3, q, channel), q ranking the
- *                                paths with that l3 in path order
+ *                                paths with that l3 in path order (with
+ *                                spec.sum_paths: (m3, channel), one block
+ *                                per l3)
  *      R, dR      [E][P*C]       column p*C + u, paths in lexicographic
  *                                (l1,l2,l3) order
  *      Y          [E][d_sh]      real harmonics, index l*l + (m+l)
@@ -103,6 +105,12 @@ typedef struct tpc_spec {
   int validate;              /* nonzero: conv_fwd/conv_bwd also check the CSR
                                 on the device (sorted rows, src in range) and
                                 wait for the result */
+  int sum_paths;             /* nonzero: paths with the same output rank add
+                                into one block (FlashCart section 3,
+                                "Generating Cartesian tensor products"):
+                                d_out = sum of (2 l3 + 1) over the ranks that
+                                occur, (m3, channel) order inside a block;
+                                G follows the same layout */
 } tpc_spec;
 
 typedef struct tpc_info {

@@ -44,7 +44,7 @@ class _Spec(ctypes.Structure):
                 ("sh_lmax", ctypes.c_int), ("out_lmax", ctypes.c_int), ("n_bessel", ctypes.c_int),
                 ("poly_p", ctypes.c_int), ("n_species", ctypes.c_int), ("r_cut", ctypes.c_double),
                 ("n_layers", ctypes.c_int), ("layer_dims", ctypes.c_int * (TPC_MAX_LAYERS + 1)),
-                ("validate", ctypes.c_int)]
+                ("validate", ctypes.c_int), ("sum_paths", ctypes.c_int)]
 
 
 class _Info(ctypes.Structure):
@@ -161,6 +161,7 @@ class Spec:
     n_bessel: int = 8
     poly_p: int = 5
     validate: bool = False
+    sum_paths: bool = False
 
     def to_c(self):
         s = _Spec()
@@ -173,6 +174,7 @@ class Spec:
         for k, d in enumerate(self.layer_dims[:TPC_MAX_LAYERS + 1]):
             s.layer_dims[k] = int(d)
         s.validate = int(bool(self.validate))
+        s.sum_paths = int(bool(self.sum_paths))
         return s
 
 
@@ -384,4 +386,4 @@ def spec_for(cfg, validate=False):
     """Spec of a workload configuration dict (see ``workloads.config``)."""
     return Spec(channels=cfg["C"], node_lmax=cfg["l1max"], sh_lmax=cfg["sh_lmax"],
                 out_lmax=cfg["out_lmax"], r_cut=cfg["r_cut"], layer_dims=list(cfg["layer_dims"]),
-                dtype=cfg["dtype"], validate=validate)
+                dtype=cfg["dtype"], validate=validate, sum_paths=bool(cfg.get("sum_paths", False)))

@@ -348,7 +348,7 @@ tpc_status tpc_ctx_create(const tpc_spec* spec, tpc_ctx** out) {
   if (!(s.r_cut > 0.0) || !std::isfinite(s.r_cut)) E.add(TPC_ERR_INVALID, "r_cut must be finite and > 0");
   tpc::Table tab{};
   if (lok) {
-    tab = tpc::make_table(s.node_lmax, s.sh_lmax, s.out_lmax);
+    tab = tpc::make_table(s.node_lmax, s.sh_lmax, s.out_lmax, s.sum_paths != 0);
     if (tab.np == 0) E.add(TPC_ERR_INVALID, "no admissible path for these l ranges");
   }
   int H = 0, NH = 0;
@@ -685,6 +685,7 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
   ta.row_end = row_end;
   ta.edge_begin = edge_begin;
   ta.C = c->spec.channels;
+  ta.sum_paths = c->spec.sum_paths != 0;
   ta.scale = scale;
   ta.h = h;
   ta.Y = eb ? eb->Y : nullptr;
@@ -775,6 +776,7 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
   ta.row_end = row_end;
   ta.edge_begin = edge_begin;
   ta.C = c->spec.channels;
+  ta.sum_paths = c->spec.sum_paths != 0;
   ta.scale = scale;
   ta.h = h;
   ta.Y = eb->Y;

@@ -31,6 +31,7 @@ struct TPArgs {
   int64_t row_begin, row_end, edge_begin;
   int64_t n_chunk_edges;  // edges of the chunk (stride of the partial dY slices)
   int C;           // channels
+  bool sum_paths;  // path-summed output rows (one block per l3)
   double scale;    // neighbour normalisation s
   const void* h;   // [N][d_in][C]
   const void* Y;   // [E][d_sh]

@@ -119,6 +119,7 @@ struct Path {
 
 struct Table {
   int L1, L2, L3;
+  bool summed;  // paths of one output rank share one (m3, channel) block
   int np;
   int din, dsh, dout;
   int nnz;
@@ -146,11 +147,16 @@ constexpr bool admissible(int l1, int l2, int l3) {
   return d <= l3 && l3 <= l1 + l2 && ((l1 + l2 + l3) % 2 == 0);
 }
 
-constexpr Table make_table(int L1, int L2, int L3) {
+// Output rows: l3 blocks ascending; inside a block (m3, q, channel) with q
+// the rank of the path among those with that l3, or, summed (FlashCart
+// section 3, "Generating Cartesian tensor products": paths with the same
+// output rank may be summed), one (m3, channel) block per l3 that occurs.
+constexpr Table make_table(int L1, int L2, int L3, bool summed = false) {
   Table t{};
   t.L1 = L1;
   t.L2 = L2;
   t.L3 = L3;
+  t.summed = summed;
   t.din = (L1 + 1) * (L1 + 1);
   t.dsh = (L2 + 1) * (L2 + 1);
   int np = 0;
@@ -170,11 +176,11 @@ constexpr Table make_table(int L1, int L2, int L3) {
     int q = 0;
     for (int p = 0; p < np; ++p)
       if (t.path[p].l3 == l3) {
-        t.path[p].q = q++;
-        t.path[p].nq = nq;
+        t.path[p].q = summed ? 0 : q++;
+        t.path[p].nq = summed ? 1 : nq;
         t.path[p].out_base = base;
       }
-    base += nq * (2 * l3 + 1);
+    base += (summed ? (nq > 0 ? 1 : 0) : nq) * (2 * l3 + 1);
   }
   t.dout = base;
   int nnz = 0;
@@ -219,8 +225,8 @@ constexpr Table make_table(int L1, int L2, int L3) {
   return t;
 }
 
-template <int L1, int L2, int L3>
-inline constexpr Table kTable = make_table(L1, L2, L3);
+template <int L1, int L2, int L3, bool SUM = false>
+inline constexpr Table kTable = make_table(L1, L2, L3, SUM);
 
 // Balanced split of the paths over NG waves of one receiver row: greedy by
 // descending per-wave work (coupling-matrix terms plus per-channel FMAs).
@@ -243,22 +249,40 @@ constexpr Groups make_groups(const Table& t, int ng, int cpl) {
       }
     cost[p] = cpl * (m13 + 2 * t.path[p].l1 + 1) + nnz;
   }
+  // with summed outputs a wave owns whole output blocks: the paths of one l3
+  // move together, at the cost of the class
+  if (t.summed) {
+    int cls[kMaxPaths] = {};
+    for (int p = 0; p < t.np; ++p)
+      for (int q = 0; q < t.np; ++q)
+        if (t.path[q].l3 == t.path[p].l3) cls[p] += cost[q];
+    for (int p = 0; p < t.np; ++p) cost[p] = cls[p];
+  }
   for (int it = 0; it < t.np; ++it) {
     int best = -1;
     for (int p = 0; p < t.np; ++p)
       if (!done[p] && (best < 0 || cost[p] > cost[best])) best = p;
+    if (best < 0) break;  // summed: whole classes already placed
     int gl = 0;
     for (int k = 1; k < ng; ++k)
       if (load[k] < load[gl]) gl = k;
-    g.group[best] = gl;
+    if (t.summed) {
+      for (int q = 0; q < t.np; ++q)
+        if (t.path[q].l3 == t.path[best].l3) {
+          g.group[q] = gl;
+          done[q] = true;
+        }
+    } else {
+      g.group[best] = gl;
+      done[best] = true;
+    }
     load[gl] += cost[best];
-    done[best] = true;
   }
   return g;
 }
 
-template <int L1, int L2, int L3, int NG, int CPL>
-inline constexpr Groups kGroups = make_groups(kTable<L1, L2, L3>, NG, CPL);
+template <int L1, int L2, int L3, bool SUM, int NG, int CPL>
+inline constexpr Groups kGroups = make_groups(kTable<L1, L2, L3, SUM>, NG, CPL);
 
 // Non-zero test for the pattern (m1, m3) of path p: is any C[m1][m2][m3] != 0.
 constexpr bool m13_nonzero(const Table& t, int p, int a, int c) {

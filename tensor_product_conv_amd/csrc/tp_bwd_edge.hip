@@ -9,7 +9,12 @@ hipError_t launch_tp_bwd_edge(int dtype, int L1, int L2, int L3, const TPArgs& a
   if (rows <= 0) return hipSuccess;
   const int nw = tp_nw(a.C);
 #define TPC_LAUNCH_BE(T, A, B, D, F)                                                             \
-  k_tp_bwd_edge<T, A, B, D, F><<<tp_blocks(rows, a.C), kTPWave * kTPWavesPerBlock, 0, s>>>(       \
+  if (a.sum_paths)                                                                               \
+    TPC_LAUNCH_BE2(T, A, B, D, true, F)                                                          \
+  else                                                                                           \
+    TPC_LAUNCH_BE2(T, A, B, D, false, F)
+#define TPC_LAUNCH_BE2(T, A, B, D, S, F)                                                         \
+  k_tp_bwd_edge<T, A, B, D, S, F><<<tp_blocks(rows, a.C), kTPWave * kTPWavesPerBlock, 0, s>>>(    \
       a.row_ptr, a.src, a.rev, a.row_begin, a.row_end, a.edge_begin, a.n_chunk_edges, a.C,      \
       (T)a.scale, static_cast<const T*>(a.h), static_cast<const T*>(a.Y),                     \
       static_cast<const T*>(a.R), static_cast<const T*>(a.G), static_cast<T*>(a.dR),           \
@@ -23,6 +28,7 @@ hipError_t launch_tp_bwd_edge(int dtype, int L1, int L2, int L3, const TPArgs& a
   TPC_TP_CONFIGS(TPC_X)
 #undef TPC_X
 #undef TPC_LAUNCH_BE
+#undef TPC_LAUNCH_BE2
   return hipErrorInvalidValue;
 }
 

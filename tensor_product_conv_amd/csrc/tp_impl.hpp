@@ -248,15 +248,15 @@ __device__ __forceinline__ void st_vec(T* __restrict__ base, uint32_t off, bool 
 //   acc[(p,m3)] += sum_m1 M^p[m1][m3] * R[p] * h[(l1,m1)],  M^p = C^p . Y,
 // with the sparsity of C^p unrolled at compile time.  h and R hold CPL
 // channels per lane; ye is the edge's harmonics (uniform across lanes).
-template <typename T, int L1, int L2, int L3, int CPL, int NG, int G>
-__device__ __forceinline__ void tp_fwd_edge(const T (&hh)[kTable<L1, L2, L3>.din][CPL],
-                                            const T (&rr)[kTable<L1, L2, L3>.np][CPL], const T (&ye)[16],
-                                            T (&acc)[kTable<L1, L2, L3>.dout][CPL]) {
-  constexpr int NP = kTable<L1, L2, L3>.np;
+template <typename T, int L1, int L2, int L3, bool SUM, int CPL, int NG, int G>
+__device__ __forceinline__ void tp_fwd_edge(const T (&hh)[kTable<L1, L2, L3, SUM>.din][CPL],
+                                            const T (&rr)[kTable<L1, L2, L3, SUM>.np][CPL], const T (&ye)[16],
+                                            T (&acc)[kTable<L1, L2, L3, SUM>.dout][CPL]) {
+  constexpr int NP = kTable<L1, L2, L3, SUM>.np;
   static_for<NP>([&](auto pc) {
     constexpr int p = decltype(pc)::value;
-    if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) {
-      constexpr Path P = kTable<L1, L2, L3>.path[p];
+    if constexpr (kGroups<L1, L2, L3, SUM, NG, CPL>.group[p] == G) {
+      constexpr Path P = kTable<L1, L2, L3, SUM>.path[p];
       T hr[2 * P.l1 + 1][CPL];
 #pragma unroll
       for (int m1 = 0; m1 < 2 * P.l1 + 1; ++m1)
@@ -264,14 +264,14 @@ __device__ __forceinline__ void tp_fwd_edge(const T (&hh)[kTable<L1, L2, L3>.din
         for (int c = 0; c < CPL; ++c) hr[m1][c] = rr[p][c] * hh[P.l1 * P.l1 + m1][c];
       static_for<2 * P.l3 + 1>([&](auto m3c) {
         constexpr int m3 = decltype(m3c)::value;
-        constexpr int row = kTable<L1, L2, L3>.out_row(p, m3);
+        constexpr int row = kTable<L1, L2, L3, SUM>.out_row(p, m3);
         static_for<2 * P.l1 + 1>([&](auto m1c) {
           constexpr int m1 = decltype(m1c)::value;
-          if constexpr (kTable<L1, L2, L3>.midx[p][m1][m3] >= 0) {
+          if constexpr (kTable<L1, L2, L3, SUM>.midx[p][m1][m3] >= 0) {
             T M = T(0);
             static_for<2 * P.l2 + 1>([&](auto m2c) {
               constexpr int m2 = decltype(m2c)::value;
-              constexpr double cv = kTable<L1, L2, L3>.cg[p][m1][m2][m3];
+              constexpr double cv = kTable<L1, L2, L3, SUM>.cg[p][m1][m2][m3];
               if constexpr (cv != 0.0) M += T(cv) * ye[P.l2 * P.l2 + m2];
             });
 #pragma unroll
@@ -283,21 +283,21 @@ __device__ __forceinline__ void tp_fwd_edge(const T (&hh)[kTable<L1, L2, L3>.din
   });
 }
 
-template <typename T, int L1, int L2, int L3, int CPL, int NG, bool MASKED, int G>
+template <typename T, int L1, int L2, int L3, bool SUM, int CPL, int NG, bool MASKED, int G>
 __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, int e_lo, int e_hi,
                                              int64_t edge_begin, int C, uint32_t c0, bool on,
                                              const T* __restrict__ h, const T* __restrict__ Y,
                                              const T* __restrict__ R, T* __restrict__ oi, T scale) {
-  constexpr int NP = kTable<L1, L2, L3>.np, DIN = kTable<L1, L2, L3>.din;
-  constexpr int DSH = kTable<L1, L2, L3>.dsh, DOUT = kTable<L1, L2, L3>.dout;
+  constexpr int NP = kTable<L1, L2, L3, SUM>.np, DIN = kTable<L1, L2, L3, SUM>.din;
+  constexpr int DSH = kTable<L1, L2, L3, SUM>.dsh, DOUT = kTable<L1, L2, L3, SUM>.dout;
   const int PC = NP * C;
   T acc[DOUT][CPL];
   static_for<NP>([&](auto pc) {
     constexpr int p = decltype(pc)::value;
-    if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) {
-      constexpr Path P = kTable<L1, L2, L3>.path[p];
+    if constexpr (kGroups<L1, L2, L3, SUM, NG, CPL>.group[p] == G) {
+      constexpr Path P = kTable<L1, L2, L3, SUM>.path[p];
       static_for<2 * P.l3 + 1>([&](auto m3c) {
-        constexpr int row = kTable<L1, L2, L3>.out_row(p, decltype(m3c)::value);
+        constexpr int row = kTable<L1, L2, L3, SUM>.out_row(p, decltype(m3c)::value);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) acc[row][c] = T(0);
       });
@@ -319,7 +319,7 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
     for (int m = 0; m < DIN; ++m) ld_vec<T, CPL>(hj, m * C + c0, on, b.h[m], MASKED);
     static_for<NP>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
-      if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) ld_vec_nt<T, CPL>(re, p * C + c0, on, b.r[p], MASKED);
+      if constexpr (kGroups<L1, L2, L3, SUM, NG, CPL>.group[p] == G) ld_vec_nt<T, CPL>(re, p * C + c0, on, b.r[p], MASKED);
     });
     b.y = Y[((int64_t)e - edge_begin) * DSH + ylane];
   };
@@ -327,7 +327,7 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
     T ye[16];
 #pragma unroll
     for (int k = 0; k < DSH; ++k) ye[k] = lane_value(b.y, k);
-    tp_fwd_edge<T, L1, L2, L3, CPL, NG, G>(b.h, b.r, ye, acc);
+    tp_fwd_edge<T, L1, L2, L3, SUM, CPL, NG, G>(b.h, b.r, ye, acc);
   };
   if (e_hi - e_lo > 64 * kIdxWindows) {
     edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, uniform(src[e]), b); }, compute);
@@ -338,10 +338,10 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
   }
   static_for<NP>([&](auto pc) {
     constexpr int p = decltype(pc)::value;
-    if constexpr (kGroups<L1, L2, L3, NG, CPL>.group[p] == G) {
-      constexpr Path P = kTable<L1, L2, L3>.path[p];
+    if constexpr (kGroups<L1, L2, L3, SUM, NG, CPL>.group[p] == G) {
+      constexpr Path P = kTable<L1, L2, L3, SUM>.path[p];
       static_for<2 * P.l3 + 1>([&](auto m3c) {
-        constexpr int row = kTable<L1, L2, L3>.out_row(p, decltype(m3c)::value);
+        constexpr int row = kTable<L1, L2, L3, SUM>.out_row(p, decltype(m3c)::value);
         T v[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) v[c] = scale * acc[row][c];
@@ -351,12 +351,12 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
   });
 }
 
-template <typename T, int L1, int L2, int L3, int CPL, int NG, bool MASKED>
+template <typename T, int L1, int L2, int L3, bool SUM, int CPL, int NG, bool MASKED>
 __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
 k_tp_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, int64_t row_begin,
          int64_t row_end, int64_t edge_begin, int C, T scale, const T* __restrict__ h,
          const T* __restrict__ Y, const T* __restrict__ R, T* __restrict__ out) {
-  constexpr int DOUT = kTable<L1, L2, L3>.dout;
+  constexpr int DOUT = kTable<L1, L2, L3, SUM>.dout;
   const int lane = threadIdx.x % kTPWave;
   const int64_t w = xcd_block() * kTPWavesPerBlock + threadIdx.x / kTPWave;
   const int64_t row = row_begin + w / NG;
@@ -371,7 +371,7 @@ k_tp_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, i
   static_for<NG>([&](auto gc) {
     constexpr int G = decltype(gc)::value;
     if (g == G)
-      tp_fwd_group<T, L1, L2, L3, CPL, NG, MASKED, G>(src, e_lo, e_hi, edge_begin, CC, c0, on, h, Y,
+      tp_fwd_group<T, L1, L2, L3, SUM, CPL, NG, MASKED, G>(src, e_lo, e_hi, edge_begin, CC, c0, on, h, Y,
                                                      R, oi, scale);
   });
 }
@@ -470,15 +470,15 @@ __device__ __forceinline__ T wave_reduce_scatter16(const T (&v)[16]) {
 //   t[m1] += R W[m1]                  (the edge's contribution to dh of its
 //                                      sender j, stored at the reverse edge's
 //                                      slot so dh of j is a contiguous row sum)
-template <typename T, int L1, int L2, int L3, int NW>
+template <typename T, int L1, int L2, int L3, bool SUM, int NW>
 __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
 k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src,
               const int32_t* __restrict__ rev, int64_t row_begin, int64_t row_end,
               int64_t edge_begin, int64_t n_chunk_edges, int C, T scale, const T* __restrict__ h,
               const T* __restrict__ Y, const T* __restrict__ R, const T* __restrict__ G,
               T* __restrict__ dR, T* __restrict__ dYp, T* __restrict__ dh_edge) {
-  constexpr int NP = kTable<L1, L2, L3>.np, DIN = kTable<L1, L2, L3>.din;
-  constexpr int DSH = kTable<L1, L2, L3>.dsh, DOUT = kTable<L1, L2, L3>.dout;
+  constexpr int NP = kTable<L1, L2, L3, SUM>.np, DIN = kTable<L1, L2, L3, SUM>.din;
+  constexpr int DSH = kTable<L1, L2, L3, SUM>.dsh, DOUT = kTable<L1, L2, L3, SUM>.dout;
   static_assert(DSH <= 16, "harmonics beyond l = 3");
   const RowWave rw = row_wave<NW>(row_begin, row_end, C);
   if (!rw.ok) return;
@@ -533,7 +533,7 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
     for (int m = 0; m < DIN; ++m) t[m] = T(0);
     static_for<NP>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
-      constexpr Path P = kTable<L1, L2, L3>.path[p];
+      constexpr Path P = kTable<L1, L2, L3, SUM>.path[p];
       constexpr int n1 = 2 * P.l1 + 1, n2 = 2 * P.l2 + 1;
       T K[n1][n2];
 #pragma unroll
@@ -542,12 +542,12 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
         for (int c = 0; c < n2; ++c) K[a][c] = T(0);
       static_for<2 * P.l3 + 1>([&](auto m3c) {
         constexpr int m3 = decltype(m3c)::value;
-        constexpr int row = kTable<L1, L2, L3>.out_row(p, m3);
+        constexpr int row = kTable<L1, L2, L3, SUM>.out_row(p, m3);
         static_for<n1>([&](auto m1c) {
           constexpr int m1 = decltype(m1c)::value;
           static_for<n2>([&](auto m2c) {
             constexpr int m2 = decltype(m2c)::value;
-            constexpr double cv = kTable<L1, L2, L3>.cg[p][m1][m2][m3];
+            constexpr double cv = kTable<L1, L2, L3, SUM>.cg[p][m1][m2][m3];
             if constexpr (cv != 0.0) K[m1][m2] += T(cv) * gi[row];
           });
         });
@@ -558,7 +558,7 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
         T w = T(0);
         static_for<n2>([&](auto m2c) {
           constexpr int m2 = decltype(m2c)::value;
-          if constexpr (kTable<L1, L2, L3>.m12nz(p, m1, m2)) w += ye[P.l2 * P.l2 + m2] * K[m1][m2];
+          if constexpr (kTable<L1, L2, L3, SUM>.m12nz(p, m1, m2)) w += ye[P.l2 * P.l2 + m2] * K[m1][m2];
         });
         dr += b.h[P.l1 * P.l1 + m1] * w;
         t[P.l1 * P.l1 + m1] += b.r[p] * w;
@@ -568,7 +568,7 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
         T q = T(0);
         static_for<n1>([&](auto m1c) {
           constexpr int m1 = decltype(m1c)::value;
-          if constexpr (kTable<L1, L2, L3>.m12nz(p, m1, m2)) q += b.h[P.l1 * P.l1 + m1] * K[m1][m2];
+          if constexpr (kTable<L1, L2, L3, SUM>.m12nz(p, m1, m2)) q += b.h[P.l1 * P.l1 + m1] * K[m1][m2];
         });
         dy[P.l2 * P.l2 + m2] += b.r[p] * q;
       });

@@ -41,7 +41,7 @@ class Case:
         self.cfg = self.d["cfg"]
         self.ctx = tpc.Context(tpc.spec_for(self.cfg, validate))
         self.layout = paths.Layout(self.cfg["l1max"], self.cfg["sh_lmax"], self.cfg["out_lmax"],
-                                   self.cfg["C"])
+                                   self.cfg["C"], self.cfg.get("sum_paths", False))
         dev = "cuda"
         self.pos = t.from_numpy(self.d["pos"]).to(dev)
         self.cell = self.d["cell"]

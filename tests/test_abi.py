@@ -37,11 +37,11 @@ def test_no_symbol_outside_the_header():
     assert ours == set(_declared())
 
 
-@pytest.mark.parametrize("k", [0, 1, 2, 4])
+@pytest.mark.parametrize("k", [0, 1, 2, 4, 8])
 def test_context_sizes_match_configs(k):
     c = workloads.config(k)
     ctx = tpc.Context(tpc.spec_for(c))
-    L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"])
+    L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"], c.get("sum_paths", False))
     assert ctx.paths == L.paths
     assert (ctx.n_paths, ctx.d_in, ctx.d_sh, ctx.d_out) == (c["n_paths"], c["d_in"], c["d_sh"], c["d_out"])
     assert ctx.r_width == c["n_paths"] * c["C"]

@@ -24,8 +24,9 @@ def _prob(case, nl):
 # hidden widths (the narrower-channel tensor-product kernels, the float32
 # radial kernels that the wider networks do not take, and in 7 a radial
 # width of 17 column steps of 32: a half-filled last weight tile forward and
-# the float32 fallback backward)
-@pytest.mark.parametrize("k", [0, 1, 5, 6, 7])
+# the float32 fallback backward); 8 is the small system with path-summed
+# outputs (one block per output rank)
+@pytest.mark.parametrize("k", [0, 1, 5, 6, 7, 8])
 def test_full_parity(k):
     case = Case(k)
     nl = case.nbr()

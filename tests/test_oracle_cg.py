@@ -17,7 +17,7 @@ ALL = [(l1, l2, l3) for l1 in range(4) for l2 in range(4) for l3 in range(4)
 def test_path_lists_of_the_configs():
     import workloads
     for k, c in workloads.CONFIGS.items():
-        L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"])
+        L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"], c.get("sum_paths", False))
         assert (L.n_paths, L.d_in, L.d_sh, L.d_out) == (c["n_paths"], c["d_in"], c["d_sh"], c["d_out"])
     L = paths.Layout(1, 2, 1, 8)
     assert L.paths == [(0, 0, 0), (0, 1, 1), (1, 0, 1), (1, 1, 0), (1, 2, 1)]

@@ -71,6 +71,11 @@ CONFIGS = {
     7: dict(name="small_c32_h32", N=4096, dtype="float32", C=32, l1max=2,
             sh_lmax=3, out_lmax=3, r_cut=5.0, hidden=[32, 32], n_paths=17,
             d_in=9, d_sh=16, d_out=71, scale="one", seed=7, geometry="sc"),
+    # the small system with path-summed outputs (one block per output rank)
+    8: dict(name="small_summed", N=4096, dtype="float32", C=128, l1max=2,
+            sh_lmax=3, out_lmax=3, r_cut=5.0, hidden=[64, 64], n_paths=17,
+            d_in=9, d_sh=16, d_out=16, scale="one", seed=8, geometry="sc",
+            sum_paths=True),
 }
 
 N_BESSEL = 8
