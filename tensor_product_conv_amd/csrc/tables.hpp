@@ -228,8 +228,9 @@ constexpr Table make_table(int L1, int L2, int L3, bool summed = false) {
 template <int L1, int L2, int L3, bool SUM = false>
 inline constexpr Table kTable = make_table(L1, L2, L3, SUM);
 
-// Balanced split of the paths over NG waves of one receiver row: greedy by
-// descending per-wave work (coupling-matrix terms plus per-channel FMAs).
+// Split of the paths over NG waves of one receiver row: by whole l1 classes
+// when that balances well enough, else greedy by descending per-wave work
+// (coupling-matrix terms plus per-channel FMAs).
 struct Groups {
   int group[kMaxPaths];
 };
@@ -248,6 +249,42 @@ constexpr Groups make_groups(const Table& t, int ng, int cpl) {
           if (t.cg[p][a][b][c] != 0.0) ++nnz;
       }
     cost[p] = cpl * (m13 + 2 * t.path[p].l1 + 1) + nnz;
+  }
+  // With separate outputs, whole l1 classes go to one wave when some split of
+  // the classes keeps the busiest wave within 5/4 of an even share: each
+  // wave then loads only its classes' rows of the sender features.
+  if (!t.summed && ng > 1) {
+    int ccost[4] = {};
+    for (int p = 0; p < t.np; ++p) ccost[t.path[p].l1] += cost[p];
+    int total = 0;
+    for (int l = 0; l <= t.L1; ++l) total += ccost[l];
+    int best_max = -1, best_code = -1;
+    int n_codes = 1;
+    for (int l = 0; l <= t.L1; ++l) n_codes *= ng;
+    for (int code = 0; code < n_codes; ++code) {
+      int ld[8] = {}, x = code;
+      for (int l = 0; l <= t.L1; ++l) {
+        ld[x % ng] += ccost[l];
+        x /= ng;
+      }
+      int mx = 0, empty = 0;
+      for (int k = 0; k < ng; ++k) {
+        if (ld[k] > mx) mx = ld[k];
+        if (ld[k] == 0) empty = 1;
+      }
+      if (!empty && (best_max < 0 || mx < best_max)) {
+        best_max = mx;
+        best_code = code;
+      }
+    }
+    if (best_code >= 0 && 4 * best_max * ng <= 5 * total) {
+      for (int p = 0; p < t.np; ++p) {
+        int x = best_code;
+        for (int l = 0; l < t.path[p].l1; ++l) x /= ng;
+        g.group[p] = x % ng;
+      }
+      return g;
+    }
   }
   // with summed outputs a wave owns whole output blocks: the paths of one l3
   // move together, at the cost of the class
@@ -283,6 +320,13 @@ constexpr Groups make_groups(const Table& t, int ng, int cpl) {
 
 template <int L1, int L2, int L3, bool SUM, int NG, int CPL>
 inline constexpr Groups kGroups = make_groups(kTable<L1, L2, L3, SUM>, NG, CPL);
+
+// Does wave group g use the sender-feature rows of rank l1?
+constexpr bool group_uses_l1(const Table& t, const Groups& gr, int g, int l1) {
+  for (int p = 0; p < t.np; ++p)
+    if (gr.group[p] == g && t.path[p].l1 == l1) return true;
+  return false;
+}
 
 // Non-zero test for the pattern (m1, m3) of path p: is any C[m1][m2][m3] != 0.
 constexpr bool m13_nonzero(const Table& t, int p, int a, int c) {

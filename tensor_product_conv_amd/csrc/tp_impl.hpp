@@ -315,8 +315,13 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
   auto load_j = [&](int e, int j, Buf& b) __attribute__((always_inline)) {
     const T* __restrict__ hj = h + (int64_t)j * DIN * C;
     const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
-#pragma unroll
-    for (int m = 0; m < DIN; ++m) ld_vec<T, CPL>(hj, m * C + c0, on, b.h[m], MASKED);
+    // only the rows of the l1 ranks this group's paths read
+    static_for<DIN>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int l1 = m >= 9 ? 3 : m >= 4 ? 2 : m >= 1 ? 1 : 0;
+      if constexpr (group_uses_l1(kTable<L1, L2, L3, SUM>, kGroups<L1, L2, L3, SUM, NG, CPL>, G, l1))
+        ld_vec<T, CPL>(hj, m * C + c0, on, b.h[m], MASKED);
+    });
     static_for<NP>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
       if constexpr (kGroups<L1, L2, L3, SUM, NG, CPL>.group[p] == G) ld_vec_nt<T, CPL>(re, p * C + c0, on, b.r[p], MASKED);
