@@ -198,10 +198,11 @@ __device__ __forceinline__ RowWave row_wave(int64_t row_begin, int64_t row_end, 
 }
 
 // ---------------------------------------------------------------------------
-// Forward.  NG waves share a receiver row, each owning a compile-time subset of
-// the paths (kGroups): the per-edge coupling matrices of a path are computed
-// by exactly one wave, from the edge's harmonics held in scalar registers.
-// Lanes own CPL consecutive channels (CPL = 2 for C = 128); MASKED kernels
+// Forward.  NG * NWC waves share a receiver row: NWC channel slices of
+// 64 * CPL channels, and in each slice NG waves that own compile-time subsets
+// of the paths (kGroups; the per-edge coupling matrices of a path are
+// computed by one wave of the slice, from the edge's harmonics broadcast
+// from one vector load).  Lanes own CPL consecutive channels; MASKED kernels
 // serve C < 64 with one channel per lane.
 template <typename T, int CPL>
 __device__ __forceinline__ void ld_vec(const T* __restrict__ base, uint32_t off, bool on, T (&v)[CPL],
@@ -356,7 +357,7 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
   });
 }
 
-template <typename T, int L1, int L2, int L3, bool SUM, int CPL, int NG, bool MASKED>
+template <typename T, int L1, int L2, int L3, bool SUM, int CPL, int NG, bool MASKED, int NWC = 1>
 __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
 k_tp_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, int64_t row_begin,
          int64_t row_end, int64_t edge_begin, int C, T scale, const T* __restrict__ h,
@@ -364,12 +365,13 @@ k_tp_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, i
   constexpr int DOUT = kTable<L1, L2, L3, SUM>.dout;
   const int lane = threadIdx.x % kTPWave;
   const int64_t w = xcd_block() * kTPWavesPerBlock + threadIdx.x / kTPWave;
-  const int64_t row = row_begin + w / NG;
+  const int64_t row = row_begin + w / (NG * NWC);
   if (row >= row_end) return;
   const int i = uniform((int)row);
-  const int g = uniform((int)(w % NG));
-  const int CC = MASKED ? C : 64 * CPL;
-  const uint32_t c0 = (uint32_t)(lane * CPL);
+  const int rem = uniform((int)(w % (NG * NWC)));
+  const int g = rem % NG, cw = rem / NG;
+  const int CC = MASKED ? C : 64 * CPL * NWC;
+  const uint32_t c0 = (uint32_t)(cw * 64 * CPL + lane * CPL);
   const bool on = (int)c0 < C;
   const int e_lo = uniform(row_ptr[i]), e_hi = uniform(row_ptr[i + 1]);
   T* __restrict__ oi = out + (int64_t)i * DOUT * CC;
