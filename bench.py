@@ -151,7 +151,8 @@ def roofline_for(kernel, per_launch_s, N, E, cfg, ctx):
                  frac=ach / HBM_PEAK, algorithmic_bytes_per_launch=nbytes,
                  vector_alu_frac=(flops / per_launch_s) / VALU_F32_PEAK)
     r["kernel"] = kernel
-    r["traffic"] = measured_traffic(kernel)
+    # the committed counters were taken on the default (separate-path) layout
+    r["traffic"] = None if cfg.get("sum_paths") else measured_traffic(kernel)
     return r
 
 
