@@ -50,7 +50,7 @@
  *  - Errors: every entry point returns a tpc_status.  On failure nothing is
  *    enqueued (argument checks run before any device work) and
  *    tpc_last_error() lists every failed check.  There is no silent fallback:
- *    a request this build does not implement returns TPC_ERR_UNSUPPORTED.
+ *    a request this library does not implement returns TPC_ERR_UNSUPPORTED.
  *  - Results are deterministic: the same inputs give bitwise-identical
  *    outputs run to run on the same GPU (no floating-point atomics).
  *  - A context is immutable after creation; concurrent calls on different
@@ -69,7 +69,7 @@ extern "C" {
 typedef enum tpc_status {
   TPC_OK = 0,
   TPC_ERR_INVALID = 1,      /* bad argument: null/misaligned pointer, size, spec value */
-  TPC_ERR_UNSUPPORTED = 2,  /* valid request that this build does not implement */
+  TPC_ERR_UNSUPPORTED = 2,  /* valid request that this library does not implement */
   TPC_ERR_CAPACITY = 3,     /* edge_cap too small; *n_edges holds the needed count */
   TPC_ERR_PRECONDITION = 4, /* input breaks a documented precondition (unwrapped
                                positions, unsorted or inconsistent CSR) */
