@@ -110,3 +110,35 @@ def grads(layout: Layout, pos, cell, row_ptr, src, shift, h, W, G, r_cut, scale)
     L.backward()
     return dict(out=out.detach().numpy(), dh=h_t.grad.numpy(), dR=R.grad.numpy(),
                 dY=Y.grad.numpy(), F=-pos_t.grad.numpy(), L=float(L.detach()))
+
+
+def double_grads(layout: Layout, pos, cell, row_ptr, src, shift, h, W, G, r_cut, scale, uh, uY, uR):
+    """Autograd of the VJP (FlashCart paper, section 3 "Symbolic
+    derivatives": the VJP itself is differentiated for training on forces).
+    The VJP (dh, dY, dR) of L = sum(G * out) is taken with create_graph, then
+    Lam = <uh, dh> + <uY, dY> + <uR, dR> is differentiated with respect to G,
+    h, Y and R, all four treated as independent inputs of the product (Y and R
+    are leaves here, computed once from the geometry)."""
+    N = len(pos)
+    recv = torch.from_numpy(np.repeat(np.arange(N), np.diff(row_ptr)).astype(np.int64))
+    src_t = torch.from_numpy(np.asarray(src, dtype=np.int64))
+    sh_t = torch.from_numpy(np.asarray(shift, dtype=np.int64))
+    pos_t = torch.tensor(np.asarray(pos, dtype=np.float64))
+    cell_t = torch.tensor(np.asarray(cell, dtype=np.float64))
+    W_t = [torch.tensor(np.asarray(w, dtype=np.float64)) for w in W]
+    with torch.no_grad():
+        _, Y0, R0 = forward_torch(layout, pos_t, cell_t, recv, src_t, sh_t, None, W_t, r_cut, scale)
+    Y = Y0.clone().requires_grad_(True)
+    R = R0.clone().requires_grad_(True)
+    h_t = torch.tensor(np.asarray(h, dtype=np.float64), requires_grad=True)
+    G_t = torch.tensor(np.asarray(G, dtype=np.float64), requires_grad=True)
+    out = convolve_torch(layout, Y, R, h_t, recv, src_t, N, scale)
+    L = (G_t * out).sum()
+    dh, dY, dR = torch.autograd.grad(L, (h_t, Y, R), create_graph=True)
+    lam = ((torch.tensor(np.asarray(uh, dtype=np.float64)) * dh).sum()
+           + (torch.tensor(np.asarray(uY, dtype=np.float64)) * dY).sum()
+           + (torch.tensor(np.asarray(uR, dtype=np.float64)) * dR).sum())
+    gG, gh, gY, gR = torch.autograd.grad(lam, (G_t, h_t, Y, R))
+    return dict(g_hat=gG.numpy(), x_hat=gh.numpy(), y_hat=gY.numpy(), w_hat=gR.numpy(),
+                dh=dh.detach().numpy(), dY=dY.detach().numpy(), dR=dR.detach().numpy(),
+                lam=float(lam.detach()))

@@ -170,6 +170,95 @@ class Problem:
             np.add.at(dh, self.src[e], b["dh_contrib"])
         return dict(dR=dR, dY=dY, dh=dh, g=g, F=self.forces_from(g))
 
+    # ---- VJP-of-VJP (double backward) ---------------------------------------
+    def double_backward_edges(self, e, uh, uY, uR):
+        """The VJP-of-VJP terms of edges ``e`` (FlashCart paper, §3 "Symbolic
+        derivatives": training on forces differentiates through the VJP; §4
+        "Receiver-sorted derivatives": the VJP-of-VJP runs over the same
+        receiver-sorted edges).
+
+        The VJP maps (h, Y, R, G) to (dh, dY, dR) above.  Given cotangents
+        uh [N, d_in, C], uY [E, d_sh] and uR [E, P*C] of those three outputs,
+        the scalar Lam = <uh, dh> + <uY, dY> + <uR, dR> is differentiated with
+        respect to each VJP input.  Every output of the VJP is linear in G and
+        in each of h, Y, R it depends on, so with the unweighted product
+        T(a, y)[p, m3, u] = sum_{m1,m2} C^p a[m1,u] y[m2] (and i = recv_e,
+        j = src_e):
+
+          g_hat[i,(p,m3),u]  = s sum_{e in row i} ( uR[e,p,u] T(h_j, Y_e)
+                                 + R[e,p,u] (T(h_j, uY_e) + T(uh_j, Y_e)) )
+          w_hat[e,p,u]       = s sum_m3 G[i,(p,m3),u] (T(h_j,uY_e) + T(uh_j,Y_e))
+          y_hat[e,(l2,m2)]   = s sum_p sum_u sum_{m1,m3} C^p G[i,(p,m3),u]
+                                 ( uR[e,p,u] h[j,m1,u] + R[e,p,u] uh[j,m1,u] )
+          x_hat[j,(l1,m1),u] = s sum_{e: src_e = j} sum_p sum_{m2,m3} C^p G[i,(p,m3),u]
+                                 ( uR[e,p,u] Y[e,m2] + R[e,p,u] uY[e,m2] )
+
+        (dh does not depend on h, dY not on Y, dR not on R.)  Returns the
+        per-edge w_hat, y_hat, the per-edge message to g_hat of the receiver
+        and the per-edge contribution to x_hat of the sender."""
+        L, Cn, s = self.L, self.L.C, self.scale
+        _, _, Y, _, R = self.edge_terms(e)
+        hs = np.asarray(self.h[self.src[e]], dtype=np.float64)
+        uhs = np.asarray(uh[self.src[e]], dtype=np.float64)
+        uYe = np.asarray(uY[e], dtype=np.float64)
+        uRe = np.asarray(uR[e], dtype=np.float64)
+        Gr = np.asarray(self.G[self.recv[e]], dtype=np.float64)
+        w_hat = np.zeros_like(R)
+        y_hat = np.zeros_like(Y)
+        g_msg = np.zeros((len(e), L.d_out, Cn))
+        x_c = np.zeros_like(hs)
+        for p, (l1, l2, l3) in enumerate(L.paths):
+            Cp = self.C[p]
+            a1, a2, rows = L.in_slice(l1), L.sh_slice(l2), L.out_rows(p)
+            Rp, uRp = R[:, p * Cn:(p + 1) * Cn], uRe[:, p * Cn:(p + 1) * Cn]
+            Gp = Gr[:, rows, :]
+            T_hY = np.einsum("abk,eau,eb->eku", Cp, hs[:, a1], Y[:, a2], optimize=True)
+            T_huY = np.einsum("abk,eau,eb->eku", Cp, hs[:, a1], uYe[:, a2], optimize=True)
+            T_uhY = np.einsum("abk,eau,eb->eku", Cp, uhs[:, a1], Y[:, a2], optimize=True)
+            g_msg[:, rows, :] += s * (uRp[:, None, :] * T_hY + Rp[:, None, :] * (T_huY + T_uhY))
+            w_hat[:, p * Cn:(p + 1) * Cn] = s * np.einsum("eku,eku->eu", Gp, T_huY + T_uhY)
+            y_hat[:, a2] += s * np.einsum("abk,eku,eau->eb", Cp, Gp,
+                                          uRp[:, None, :] * hs[:, a1] + Rp[:, None, :] * uhs[:, a1],
+                                          optimize=True)
+            x_c[:, a1] += s * np.einsum("abk,eku,ebu->eau", Cp, Gp,
+                                        uRp[:, None, :] * Y[:, a2, None] + Rp[:, None, :] * uYe[:, a2, None],
+                                        optimize=True)
+        return dict(w_hat=w_hat, y_hat=y_hat, g_msg=g_msg, x_contrib=x_c)
+
+    def double_backward(self, uh, uY, uR, max_edges=4096):
+        """g_hat [N, d_out, C], x_hat [N, d_in, C], y_hat [E, d_sh],
+        w_hat [E, P*C] for the cotangents uh, uY, uR (see
+        ``double_backward_edges``)."""
+        L = self.L
+        E, N = len(self.src), len(self.pos)
+        g_hat = np.zeros((N, L.d_out, L.C))
+        x_hat = np.zeros((N, L.d_in, L.C))
+        y_hat = np.zeros((E, L.d_sh))
+        w_hat = np.zeros((E, L.n_paths * L.C))
+        for lo in range(0, E, max_edges):
+            e = np.arange(lo, min(E, lo + max_edges))
+            b = self.double_backward_edges(e, uh, uY, uR)
+            w_hat[e], y_hat[e] = b["w_hat"], b["y_hat"]
+            np.add.at(g_hat, self.recv[e], b["g_msg"])
+            np.add.at(x_hat, self.src[e], b["x_contrib"])
+        return dict(g_hat=g_hat, x_hat=x_hat, y_hat=y_hat, w_hat=w_hat)
+
+    def double_backward_rows(self, rows, uh, uY, uR):
+        """g_hat of receivers ``rows`` and x_hat of the atoms ``rows``
+        (sampled pieces for large systems)."""
+        rows = np.asarray(rows, dtype=np.int64)
+        where = {int(r): k for k, r in enumerate(rows)}
+        e_in, owner = edges_of_rows(self.row_ptr, rows)
+        g = np.zeros((len(rows), self.L.d_out, self.L.C))
+        if len(e_in):
+            np.add.at(g, owner, self.double_backward_edges(e_in, uh, uY, uR)["g_msg"])
+        e_out = self.edges_with_sender(rows)
+        x = np.zeros((len(rows), self.L.d_in, self.L.C))
+        if len(e_out):
+            np.add.at(x, [where[int(j)] for j in self.src[e_out]],
+                      self.double_backward_edges(e_out, uh, uY, uR)["x_contrib"])
+        return g, x
+
     def forces_from(self, g):
         N = len(self.pos)
         F = np.zeros((N, 3))

@@ -1,9 +1,9 @@
 """Radial basis, envelope and radial MLP: edge length -> per-path weights.
 
-The radial network turns each edge length into the weights of that edge's
-tensor product (FastMACE page "Rewrites and precision options", section
-"Radial network"); FlashCart §2 calls them the distance-dependent weights
-W_{l1 l2 l}(r_uv), one per path and channel.
+Each edge's length is mapped by a small MLP to one weight per coupling path
+and channel for that edge's product (FastMACE page "Rewrites and precision
+options", section "Radial network"; FlashCart §2 writes these weights as
+W_{l1 l2 l}(r_uv)).
 
 Readings (the pages name the pieces but print no formulas):
   * Bessel basis, n = 1..8:  b_n(r) = sqrt(2/r_c) sin(n pi r / r_c) / r

@@ -225,3 +225,120 @@ def test_medium_slice_finite_differences():
     F = prob.forces_atoms(atoms)
     Ffd = fd.fd_forces(prob, atoms, delta=1e-3)
     assert np.abs(F - Ffd).max() / np.abs(F).max() < 1e-7
+
+
+@pytest.mark.parametrize("summed", [False, True])
+def test_dh_atoms_matches_autograd(summed):
+    """The sampled sender gradient (dh of chosen atoms, summed over the edges
+    whose sender they are) against torch autograd of the independent forward,
+    on every atom of the tiny system, with separate and path-summed outputs
+    (FlashCart paper, section 3 "Symbolic derivatives": the input VJP)."""
+    from oracle import autograd_check as ag
+    d = workloads.generate(0)
+    c = d["cfg"]
+    L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"], summed)
+    rp, src, shift = nbr.binned(d["pos"], d["cell"], c["r_cut"])
+    G = d["G"] if not summed else np.random.default_rng(5).standard_normal((c["N"], L.d_out, c["C"]))
+    prob = conv.Problem(L, d["pos"], d["cell"], rp, src, shift, d["h"], d["W"], c["r_cut"], 1.0, G)
+    a = ag.grads(L, d["pos"], d["cell"], rp, src, shift, d["h"], d["W"], G, c["r_cut"], 1.0)
+    atoms = np.arange(c["N"])
+    dh = prob.dh_atoms(atoms)
+    np.testing.assert_allclose(dh, a["dh"], rtol=0, atol=1e-12 * np.abs(a["dh"]).max())
+    # a subset in shuffled order gives the same rows
+    sub = np.random.default_rng(1).permutation(c["N"])[:9]
+    np.testing.assert_allclose(prob.dh_atoms(sub), a["dh"][sub], rtol=0, atol=1e-12 * np.abs(a["dh"]).max())
+    # the test separates sender from receiver grouping: the same per-edge
+    # contributions summed by receiver are far from the gradient
+    e = np.arange(len(src))
+    by_recv = np.zeros_like(dh)
+    np.add.at(by_recv, nbr.receivers_of(rp), prob.edge_backward(e)["dh_contrib"])
+    assert np.abs(by_recv - a["dh"]).max() > 1e-3 * np.abs(a["dh"]).max()
+
+
+def test_dh_atoms_small_sample_matches_full_backward():
+    """On the small system (C = 128), dh of a spread sample of atoms from the
+    sampled routine equals the rows of the full backward's dh (itself pinned to
+    autograd on the tiny system above), so the per-atom edge selection and
+    grouping hold on a large list too."""
+    d = workloads.generate(1)
+    c = d["cfg"]
+    L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"])
+    rp, src, shift = nbr.binned(d["pos"], d["cell"], c["r_cut"])
+    prob = conv.Problem(L, d["pos"], d["cell"], rp, src, shift, d["h"], d["W"], c["r_cut"], 1.0, d["G"])
+    atoms = np.unique(np.concatenate([[0, c["N"] - 1], np.random.default_rng(3).choice(c["N"], 14, replace=False)]))
+    # the reference: every edge whose sender is in the sample, through the
+    # full backward's edge routine, scattered by sender
+    e = np.nonzero(np.isin(src, atoms))[0]
+    contrib = prob.edge_backward(e)["dh_contrib"]
+    ref = np.zeros((c["N"], L.d_in, c["C"]))
+    np.add.at(ref, src[e], contrib)
+    got = prob.dh_atoms(atoms)
+    np.testing.assert_allclose(got, ref[atoms], rtol=0, atol=1e-13 * np.abs(ref).max())
+    # <dh, h> over all atoms equals L (linearity in h) for the sampled rows' share:
+    # sum over the sample of <dh_a, h_a> equals the L of the messages those
+    # atoms send
+    hs = np.asarray(d["h"], dtype=np.float64)
+    lhs = float((got * hs[atoms]).sum())
+    out_part = np.zeros((c["N"], L.d_out, c["C"]))
+    _, _, Y, _, R = prob.edge_terms(e)
+    _, T = prob.products(e, Y)
+    recv = nbr.receivers_of(rp)[e]
+    for p in range(L.n_paths):
+        msg = R[:, None, p * c["C"]:(p + 1) * c["C"]] * T[p]
+        acc = np.zeros((c["N"], msg.shape[1], c["C"]))
+        np.add.at(acc, recv, msg)
+        out_part[:, L.out_rows(p), :] += acc
+    rhs = float((np.asarray(d["G"], dtype=np.float64) * out_part).sum())
+    assert abs(lhs - rhs) < 1e-10 * max(1.0, abs(rhs))
+
+
+def _cotangents(prob, seed):
+    rng = np.random.default_rng(seed)
+    N, E, L = len(prob.pos), len(prob.src), prob.L
+    return (rng.standard_normal((N, L.d_in, L.C)), rng.standard_normal((E, L.d_sh)),
+            rng.standard_normal((E, L.n_paths * L.C)))
+
+
+@pytest.fixture(scope="module")
+def tiny_double(tiny):
+    prob, d, out, b = tiny
+    uh, uY, uR = _cotangents(prob, 21)
+    return prob, d, b, (uh, uY, uR), prob.double_backward(uh, uY, uR)
+
+
+def test_double_backward_matches_double_autograd(tiny_double):
+    """VJP-of-VJP against torch autograd of the independent forward's VJP
+    (FlashCart paper, section 3 "Symbolic derivatives")."""
+    from oracle import autograd_check as ag
+    prob, d, b, (uh, uY, uR), db = tiny_double
+    a = ag.double_grads(prob.L, prob.pos, prob.cell, prob.row_ptr, prob.src, prob.shift, d["h"],
+                        d["W"], d["G"], prob.r_cut, prob.scale, uh, uY, uR)
+    for k in ("g_hat", "x_hat", "y_hat", "w_hat"):
+        np.testing.assert_allclose(db[k], a[k], rtol=0, atol=1e-12 * np.abs(a[k]).max())
+
+
+def test_double_backward_multilinearity(tiny_double):
+    """Each VJP output is linear in G and in each of h, Y, R it depends on
+    (dh does not depend on h, dY not on Y, dR not on R), so
+    <g_hat, G> = Lam, <x_hat, h> = <uY, dY> + <uR, dR>,
+    <y_hat, Y> = <uh, dh> + <uR, dR>, <w_hat, R> = <uh, dh> + <uY, dY>."""
+    prob, d, b, (uh, uY, uR), db = tiny_double
+    _, _, Y, _, R = prob.edge_terms(np.arange(len(prob.src)))
+    t_h = float((uh * b["dh"]).sum())
+    t_Y = float((uY * b["dY"]).sum())
+    t_R = float((uR * b["dR"]).sum())
+    scale = abs(t_h) + abs(t_Y) + abs(t_R)
+    G = np.asarray(d["G"], dtype=np.float64)
+    h = np.asarray(d["h"], dtype=np.float64)
+    assert abs(float((db["g_hat"] * G).sum()) - (t_h + t_Y + t_R)) < 1e-12 * scale
+    assert abs(float((db["x_hat"] * h).sum()) - (t_Y + t_R)) < 1e-12 * scale
+    assert abs(float((db["y_hat"] * Y).sum()) - (t_h + t_R)) < 1e-12 * scale
+    assert abs(float((db["w_hat"] * R).sum()) - (t_h + t_Y)) < 1e-12 * scale
+
+
+def test_double_backward_rows_match_full(tiny_double):
+    prob, d, b, (uh, uY, uR), db = tiny_double
+    rows = np.array([0, 5, 17, 31])
+    g, x = prob.double_backward_rows(rows, uh, uY, uR)
+    np.testing.assert_allclose(g, db["g_hat"][rows], rtol=0, atol=1e-13 * np.abs(db["g_hat"]).max())
+    np.testing.assert_allclose(x, db["x_hat"][rows], rtol=0, atol=1e-13 * np.abs(db["x_hat"]).max())
