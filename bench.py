@@ -1,20 +1,25 @@
 """Benchmark of the equivariant interaction convolution on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload medium]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload medium|small|large]
 
-One step is the whole hot path over the synthetic medium water system
-(32,768 atoms, C = 128, node irreps 0e+1o+2e, harmonics l <= 3, outputs
-l <= 3, radial MLP 8-64-64-64-2176, about 2.97 M directed edges): the
-periodic neighbour build, the forward convolution and its backward
-(dL/dh, dL/dR, forces).  Inputs are resident in HBM before timing starts.
-The metric is directed edges per second through that step.
+One step is the whole hot path over one synthetic system: the periodic
+neighbour build, the forward convolution and its backward (dL/dh, dL/dR,
+forces).  The default workload is the medium water system (32,768 atoms,
+C = 128, node irreps 0e+1o+2e, harmonics l <= 3, outputs l <= 3, radial MLP
+8-64-64-64-2176, about 2.93 M directed edges).  The small system (4,096
+atoms, C = 128) and the large fcc system (262,144 atoms, C = 64, about
+19.8 M edges, processed in 4 receiver chunks) are the other lines.  Inputs
+are resident in HBM before timing starts.  The metric is directed edges per
+second through the step.
 
 Per-kernel durations come from HIP events the library records around each
 launch on the launch stream during the timed steps; the dominant kernel's
-algorithmic bytes (or flops) per launch divided by its average duration gives
-the roofline line.  HBM traffic from rocprofv3 counters is read from
-profiles/traffic.json when it was measured on the current kernel sources.
-The CPU baseline times the float64 oracle on a bounded sample of receivers.
+algorithmic bytes (or flops) per step divided by its time per step (the
+per-launch ratio, chunk by chunk) gives the roofline line.  HBM traffic from
+rocprofv3 counters is read from profiles/traffic_<workload>.json when it was
+measured on the current kernel sources.  The virial and the VJP-of-VJP are
+timed after the steps, outside them.  The CPU baseline times the float64
+oracle on a bounded sample of receivers.
 """
 from __future__ import annotations
 
@@ -35,9 +40,9 @@ VALU_F32_PEAK = 78.6e12    # flop/s, fp32 FMA without packed math: 256 CU x 4 SI
 MFMA_BF16_PEAK = 2.5e15    # flop/s, dense bf16 matrix
 
 KERNEL_SOURCES = {
-    "tp_fwd": ["tp_impl.hpp", "tp_fwd.hip", "tables.hpp"],
-    "tp_bwd_edge": ["tp_impl.hpp", "tp_bwd_edge.hip", "tables.hpp"],
-    "dh_gather": ["tp_impl.hpp", "tp_bwd_edge.hip"],
+    "tp_fwd": ["tp_impl.hpp", "tp_fwd.hip", "tables.hpp", "tp_config.hpp"],
+    "tp_bwd_edge": ["tp_impl.hpp", "tp_bwd.hip", "tables.hpp", "tp_config.hpp"],
+    "dh_gather": ["tp_impl.hpp", "tp_dispatch.hip"],
     "radial_fwd": ["radial.hip"],
     "radial_bwd_dA": ["radial.hip"],
     "radial_bwd_mlp": ["radial.hip"],
@@ -126,7 +131,7 @@ def group_rooflines(per_kernel, N, E, cfg, ctx):
     return out
 
 
-def roofline_for(kernel, per_launch_s, N, E, cfg, ctx):
+def roofline_for(kernel, per_launch_s, N, E, cfg, ctx, workload="medium", launches=1):
     nbytes, flops = algorithmic(kernel, N, E, cfg, ctx)
     if nbytes is None:
         return None
@@ -152,12 +157,19 @@ def roofline_for(kernel, per_launch_s, N, E, cfg, ctx):
                  vector_alu_frac=(flops / per_launch_s) / VALU_F32_PEAK)
     r["kernel"] = kernel
     # the committed counters were taken on the default (separate-path) layout
-    r["traffic"] = None if cfg.get("sum_paths") else measured_traffic(kernel)
+    t = None if cfg.get("sum_paths") else measured_traffic(kernel, workload)
+    r["traffic"] = None if t is None else t * launches
     return r
 
 
-def measured_traffic(kernel):
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per step of ``kernel`` from the committed counters of this
+    workload, when they were taken on the current kernel sources."""
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -241,12 +253,14 @@ def _cpu_task(rows):
     return len(e)
 
 
-def cpu_baseline(case_data, budget_s=10.0):
+def cpu_baseline(case_data, budget_s=10.0, sample_rows=None):
     """The float64 oracle's forward + per-edge backward on random batches of
     receiver rows, one single-threaded worker process per host core of this
     GPU's share (at most 16), for about ``budget_s`` seconds of wall time.
-    Runs before the GPU is touched: the workers are forked from this process.
-    The oracle works on its own neighbour list (built before the timing)."""
+    ``sample_rows`` restricts the batches to a fixed random sample of that
+    many receivers (the large system).  Runs before the GPU is touched: the
+    workers are forked from this process.  The oracle works on its own
+    neighbour list (built before the timing)."""
     global _CPU_PROB
     import multiprocessing as mp
     import numpy as np
@@ -258,8 +272,12 @@ def cpu_baseline(case_data, budget_s=10.0):
     L = paths.Layout(c["l1max"], c["sh_lmax"], c["out_lmax"], c["C"], c.get("sum_paths", False))
     _CPU_PROB = conv.Problem(L, d["pos"], d["cell"], rp, src, shift, d["h"], d["W"], c["r_cut"],
                              conv.scale_for(c, len(d["pos"]), rp[-1]), d["G"])
-    order = np.random.default_rng(0).permutation(len(d["pos"]))
-    batches = [np.sort(order[k:k + 64]) for k in range(0, len(order), 64)]
+    rng = np.random.default_rng(0)
+    pool_rows = rng.permutation(len(d["pos"]))
+    if sample_rows:
+        pool_rows = np.sort(pool_rows[:sample_rows])
+        pool_rows = pool_rows[rng.permutation(len(pool_rows))]
+    batches = [np.sort(pool_rows[k:k + 64]) for k in range(0, len(pool_rows), 64)]
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
     done_edges = done_rows = 0
     with mp.get_context("fork").Pool(workers) as pool:
@@ -272,11 +290,16 @@ def cpu_baseline(case_data, budget_s=10.0):
         wall = time.perf_counter() - t0
         pool.terminate()
     _CPU_PROB = None
+    where = (f"a fixed random sample of {sample_rows} receivers" if sample_rows else "the same system")
     return dict(value=done_edges / wall, unit="edges/s", cores=workers, kind="oracle",
-                sample=f"{done_rows} random receiver rows ({done_edges} edges) of the same system in "
+                sample=f"{done_rows} random receiver rows ({done_edges} edges) of {where} in "
                        f"batches of 64, completed in {wall:.1f} s of wall time by {workers} single-threaded "
                        f"worker processes: float64 oracle forward + per-edge backward (dR, dY, dh "
                        f"contributions, edge gradients); neighbour build not included")
+
+
+WORKLOADS = {"small": 1, "medium": 3, "large": 4}
+DEFAULT_CHUNKS = {"small": 1, "medium": 1, "large": 4}
 
 
 def main(argv=None):
@@ -284,8 +307,12 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="medium", choices=["medium", "small"])
+    ap.add_argument("--workload", default="medium", choices=sorted(WORKLOADS))
+    ap.add_argument("--chunks", type=int, default=None,
+                    help="receiver chunks per step (default: 1, or 4 for the large system)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the separately timed virial and double backward")
     ap.add_argument("--sum-paths", action="store_true",
                     help="path-summed outputs (one block per output rank) on the same system")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -293,11 +320,11 @@ def main(argv=None):
                     help="after the timed steps, copy %d bytes device to device three times "
                          "(counter calibration for rocprofv3 --pmc runs)" % COPY_PROBE_BYTES)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/traffic.json from two rocprofv3 --pmc output folders and exit")
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc output "
+                         "folders and exit")
     a = ap.parse_args(argv)
     if a.traffic_from:
-        return traffic_from(a.traffic_from[0], a.traffic_from[1],
-                            os.path.join(ROOT, "profiles", "traffic.json"))
+        return traffic_from(a.traffic_from[0], a.traffic_from[1], traffic_path(a.workload))
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE={world}); "
@@ -310,7 +337,8 @@ def main(argv=None):
     import tensor_product_conv_amd as tpc
     import workloads
 
-    k = {"small": 1, "medium": 3}[a.workload]
+    k = WORKLOADS[a.workload]
+    chunks = a.chunks or DEFAULT_CHUNKS[a.workload]
     d = workloads.generate(k)
     cfg = d["cfg"]
     if a.sum_paths:
@@ -319,7 +347,8 @@ def main(argv=None):
         d = dict(d, cfg=cfg, G=np.random.default_rng(cfg["seed"] + 100).standard_normal(
             (cfg["N"], cfg["d_out"], cfg["C"])).astype(d["G"].dtype))
     # the CPU leg forks its workers, so it runs before anything touches the GPU
-    cpu = None if a.no_cpu_baseline else cpu_baseline(d, a.cpu_budget)
+    cpu = None if a.no_cpu_baseline else cpu_baseline(
+        d, a.cpu_budget, sample_rows=8192 if a.workload == "large" else None)
     dev = "cuda"
     ctx = tpc.Context(tpc.spec_for(cfg))
     pos = torch.from_numpy(d["pos"]).to(dev)
@@ -333,22 +362,31 @@ def main(argv=None):
     nl = ctx.nbr_build(pos, cell, species)
     E = nl.n_edges
     scale = float(N) / E if cfg["scale"] == "inv_avg_neighbors" else 1.0
+    rp = nl.row_ptr.cpu().numpy()
+    # receiver chunks with about equal edge counts
+    cuts = [0] + [int(np.searchsorted(rp, E * q // chunks)) for q in range(1, chunks)] + [N]
+    bounds = [(r0, r1, int(rp[r0]), int(rp[r1])) for r0, r1 in zip(cuts[:-1], cuts[1:]) if r1 > r0]
+    max_e = max(e1 - e0 for _, _, e0, e1 in bounds)
     out = torch.empty((N, ctx.d_out, cfg["C"]), dtype=ctx.dtype, device=dev)
-    eb = ctx.alloc_edge_buffers(E, dev)
+    eb = ctx.alloc_edge_buffers(max_e, dev)
     dh = torch.empty_like(h)
-    dR = torch.empty((E, ctx.r_width), dtype=ctx.dtype, device=dev)
-    g_edge = torch.empty((E, 3), dtype=ctx.dtype, device=dev)
     dh_edge = torch.empty((E, ctx.d_in, cfg["C"]), dtype=ctx.dtype, device=dev)
+    dR = torch.empty((max_e, ctx.r_width), dtype=ctx.dtype, device=dev)
+    g_edge = torch.empty((E, 3), dtype=ctx.dtype, device=dev)
     forces = torch.empty((N, 3), dtype=ctx.dtype, device=dev)
     ws_n = ctx._workspace(ctx.workspace_bytes(tpc.OP_NBR, N, 0, cell), dev)
-    ws_f = ctx._workspace(ctx.workspace_bytes(tpc.OP_FWD, N, E), dev)
-    ws_b = ctx._workspace(ctx.workspace_bytes(tpc.OP_BWD, N, E), dev)
+    ws_f = ctx._workspace(ctx.workspace_bytes(tpc.OP_FWD, N, max_e), dev)
+    ws_b = ctx._workspace(ctx.workspace_bytes(tpc.OP_BWD, N, max_e), dev)
 
     def step():
         nl2 = ctx.nbr_build(pos, cell, species, edge_cap=E, into=nl, workspace=ws_n)
-        ctx.conv_fwd(pos, cell, nl2, h, W, scale, out=out, eb=eb, workspace=ws_f)
-        ctx.conv_bwd(nl2, h, W, scale, G, eb, dh=dh, dR=dR, g_edge=g_edge, dh_edge=dh_edge,
-                     forces=forces, workspace=ws_b)
+        for q, (r0, r1, e0, e1) in enumerate(bounds):
+            ctx.conv_fwd(pos, cell, nl2, h, W, scale, out=out, eb=eb, rows=(r0, r1), edges=(e0, e1),
+                         workspace=ws_f)
+            last = q == len(bounds) - 1
+            ctx.conv_bwd(nl2, h, W, scale, G, eb, dh=dh if last else None, dR=dR, g_edge=g_edge,
+                         dh_edge=dh_edge, want_dh=last, forces=forces if last else None, want_forces=last,
+                         workspace=ws_b)
 
     for _ in range(a.warmup):
         step()
@@ -372,32 +410,42 @@ def main(argv=None):
     per_kernel = {n: dict(avg_ms=tot / cnt, launches_per_step=cnt / a.steps, ms_per_step=tot / a.steps)
                   for n, (tot, cnt) in kt.items()}
 
-    # the virial (strain derivative) from the step's edge gradients, timed on
-    # its own: it is not part of the step
-    vir = torch.empty((3, 3), dtype=ctx.dtype, device=dev)
-    ws_v = ctx._workspace(ctx.workspace_bytes(tpc.OP_VIRIAL, N), dev)
-    for _ in range(2):
-        ctx.virial(pos, cell, nl, g_edge, out=vir, workspace=ws_v)
-    torch.cuda.synchronize()
-    tpc.timing_enable(True)
-    for _ in range(a.steps):
-        ctx.virial(pos, cell, nl, g_edge, out=vir, workspace=ws_v)
-    torch.cuda.synchronize()
-    tpc.timing_enable(False)
-    vt = tpc.timing_collect()
-    virial_ms = vt["virial"][0] / vt["virial"][1] if "virial" in vt else None
+    extras = {}
+    if not a.no_extras:
+        # the virial (strain derivative) from the step's edge gradients, timed
+        # on its own: it is not part of the step
+        vir = torch.empty((3, 3), dtype=ctx.dtype, device=dev)
+        ws_v = ctx._workspace(ctx.workspace_bytes(tpc.OP_VIRIAL, N), dev)
+        for _ in range(2):
+            ctx.virial(pos, cell, nl, g_edge, out=vir, workspace=ws_v)
+        torch.cuda.synchronize()
+        tpc.timing_enable(True)
+        for _ in range(a.steps):
+            ctx.virial(pos, cell, nl, g_edge, out=vir, workspace=ws_v)
+        torch.cuda.synchronize()
+        tpc.timing_enable(False)
+        vt = tpc.timing_collect()
+        extras["virial_ms"] = vt["virial"][0] / vt["virial"][1] if "virial" in vt else None
+        del ws_v
+        if chunks == 1 and not cfg.get("sum_paths"):
+            extras["double_backward"] = time_double_backward(tpc, ctx, nl, h, G, eb, scale, N, E, cfg, a.steps)
+
     # one launch of each per pass (the weight packing runs once in each pass)
-    fwd_ms = sum(per_kernel.get(n, {}).get("avg_ms", 0.0)
-                 for n in ("geom_fwd", "radial_pack", "radial_fwd", "tp_fwd"))
-    bwd_ms = sum(per_kernel.get(n, {}).get("avg_ms", 0.0)
-                 for n in ("tp_bwd_edge", "radial_pack", "radial_bwd_dA", "radial_bwd_mlp", "geom_bwd",
-                           "dh_gather", "forces"))
+    fwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0)
+                 for n in ("geom_fwd", "radial_fwd", "tp_fwd")) + \
+        per_kernel.get("radial_pack", {}).get("ms_per_step", 0.0) / 2
+    bwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0)
+                 for n in ("tp_bwd_edge", "radial_bwd_dA", "radial_bwd_mlp", "geom_bwd", "dh_gather", "forces")) + \
+        per_kernel.get("radial_pack", {}).get("ms_per_step", 0.0) / 2
     nbr_ms = sum(v["ms_per_step"] for n, v in per_kernel.items() if n.startswith("nbr"))
     dominant = max((n for n in per_kernel if n in KERNEL_SOURCES), key=lambda n: per_kernel[n]["ms_per_step"])
-    roof = roofline_for(dominant, per_kernel[dominant]["avg_ms"] * 1e-3, N, E, cfg, ctx)
+    # algorithmic bytes of a step over the kernel's time in the step: with
+    # equal-edge chunks this is the per-launch ratio of every chunk
+    roof = roofline_for(dominant, per_kernel[dominant]["ms_per_step"] * 1e-3, N, E, cfg, ctx, a.workload,
+                        per_kernel[dominant]["launches_per_step"])
     kernels = {}
     for n, v in per_kernel.items():
-        r = roofline_for(n, v["avg_ms"] * 1e-3, N, E, cfg, ctx) if n in KERNEL_SOURCES else None
+        r = roofline_for(n, v["ms_per_step"] * 1e-3, N, E, cfg, ctx, a.workload) if n in KERNEL_SOURCES else None
         kernels[n] = dict(avg_ms=round(v["avg_ms"], 4), launches_per_step=v["launches_per_step"],
                           **({"bound": r["bound"], "frac": round(r["frac"], 4)} if r else {}))
 
@@ -409,7 +457,7 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src_t, dst_t
 
-
+    geom = {1: "simple cubic", 3: "water", 4: "fcc with vacancies"}[k]
     line = {
         "metric": "edges/s fwd and fwd+bwd, 128ch sh l<=3 TP conv; % of HBM roofline",
         "value": value,
@@ -423,26 +471,70 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{cfg['name']} ({'water' if k == 3 else cfg['geometry']}) "
-                               f"N={N} E={E} C={cfg['C']} node_lmax={cfg['l1max']} "
+        "config": {"workload": f"{cfg['name']} ({geom}) N={N} E={E} C={cfg['C']} node_lmax={cfg['l1max']} "
                                f"sh_lmax={cfg['sh_lmax']} out_lmax={cfg['out_lmax']} "
                                f"mlp={'-'.join(map(str, cfg['layer_dims']))}: "
                                "nbr_build + conv_fwd + conv_bwd (forces)"
+                               + (f" in {len(bounds)} receiver chunks" if len(bounds) > 1 else "")
                                + (", path-summed outputs" if cfg.get("sum_paths") else ""),
                    "n_atoms": N, "n_edges": E, "channels": cfg["C"], "paths": ctx.n_paths,
-                   "parallelism": "single GPU"},
+                   "chunks": len(bounds), "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "fwd_edges_per_s": E / (fwd_ms * 1e-3) if fwd_ms else None,
         "fwd_bwd_edges_per_s": E / ((fwd_ms + bwd_ms) * 1e-3) if fwd_ms else None,
         "nbr_build_ms": nbr_ms,
-        "virial_ms": virial_ms,
+        **extras,
         "kernels": kernels,
         "tp_groups_hbm": group_rooflines(per_kernel, N, E, cfg, ctx),
         "wall_s": wall,
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def time_double_backward(tpc, ctx, nl, h, G, eb, scale, N, E, cfg, steps):
+    """The VJP-of-VJP on the step's per-edge buffers with seeded N(0,1)
+    cotangents, timed on its own (not part of the step): per-launch times of
+    its kernels and edges/s."""
+    import numpy as np
+    import torch
+    dev = h.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    u_dh = torch.randn(h.shape, dtype=ctx.dtype, device=dev, generator=gen)
+    u_dY = torch.randn((E, ctx.d_sh), dtype=ctx.dtype, device=dev, generator=gen)
+    u_dR = torch.randn((E, ctx.r_width), dtype=ctx.dtype, device=dev, generator=gen)
+    g_hat, h_hat = torch.empty_like(G), torch.empty_like(h)
+    Y_hat = torch.empty((E, ctx.d_sh), dtype=ctx.dtype, device=dev)
+    R_hat = torch.empty((E, ctx.r_width), dtype=ctx.dtype, device=dev)
+    ws = ctx._workspace(ctx.workspace_bytes(tpc.OP_DOUBLE_BWD, N, E), dev)
+
+    def call():
+        ctx.conv_double_bwd(nl, h, scale, G, eb, u_dh, u_dY, u_dR, g_hat=g_hat, h_hat=h_hat, Y_hat=Y_hat,
+                            R_hat=R_hat, workspace=ws)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    tpc.timing_collect()
+    tpc.timing_enable(True)
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    tpc.timing_enable(False)
+    kt = tpc.timing_collect()
+    ms = {n: tot / cnt for n, (tot, cnt) in kt.items()}
+    total = sum(ms.values())
+    T, C, PC, din, dsh, dout = 4, cfg["C"], ctx.r_width, ctx.d_in, ctx.d_sh, ctx.d_out
+    # algorithmic bytes: R, u_dR and their reverse-edge rows are read once
+    # (the gather touches each edge's u_dR once more, at its reverse), R_hat
+    # written; Y, u_dY (twice), Y_hat; h, u_dh, G read once per atom, g_hat and
+    # h_hat written once per atom; CSR and reverse index
+    nbytes = (E * T * (3 * PC + PC) + E * T * (3 * dsh + dsh) + N * T * C * (2 * din + dout)
+              + N * T * C * (dout + din) + 4 * (N + 1) + 8 * E)
+    return dict(ms=total, kernels_ms={n: round(v, 4) for n, v in ms.items()}, edges_per_s=E / (total * 1e-3),
+                algorithmic_bytes=nbytes, hbm_frac=nbytes / (total * 1e-3) / HBM_PEAK)
 
 
 if __name__ == "__main__":

@@ -46,7 +46,8 @@
  *      Y          [E][d_sh]      real harmonics, index l*l + (m+l)
  *  - Streams: every call enqueues on `stream` (a hipStream_t; NULL is the
  *    default stream) and returns without waiting, except tpc_nbr_build which
- *    waits once to learn the edge count.
+ *    waits to learn the edge count and the reverse-index status, and calls
+ *    with spec.validate, which wait for their input checks.
  *  - Errors: every entry point returns a tpc_status.  On failure nothing is
  *    enqueued (argument checks run before any device work) and
  *    tpc_last_error() lists every failed check.  There is no silent fallback:
@@ -78,7 +79,7 @@ typedef enum tpc_status {
 } tpc_status;
 
 enum { TPC_F32 = 0, TPC_F64 = 1 };
-enum { TPC_OP_NBR = 0, TPC_OP_FWD = 1, TPC_OP_BWD = 2, TPC_OP_VIRIAL = 3 };
+enum { TPC_OP_NBR = 0, TPC_OP_FWD = 1, TPC_OP_BWD = 2, TPC_OP_VIRIAL = 3, TPC_OP_DOUBLE_BWD = 4 };
 
 #define TPC_MAX_LAYERS 8
 #define TPC_MAX_PATHS 32
@@ -90,7 +91,7 @@ typedef struct tpc_ctx tpc_ctx;
  * harmonics l2 = 0..sh_lmax, outputs keep l3 = 0..out_lmax; every admissible
  * path is formed (FlashCart section 2, "Irreducible Cartesian tensors"). */
 typedef struct tpc_spec {
-  int dtype;                 /* TPC_F32 or TPC_F64 */
+  int dtype;                 /* TPC_F32, or TPC_F64 with node_lmax <= 1 */
   int channels;              /* C: 1..64, or 128 */
   int node_lmax;             /* 0..3 */
   int sh_lmax;               /* 0..3 */
@@ -102,15 +103,24 @@ typedef struct tpc_spec {
   int n_layers;              /* number of weight matrices, 2..TPC_MAX_LAYERS */
   int layer_dims[TPC_MAX_LAYERS + 1]; /* [0] = n_bessel, [n_layers] = P*C; hidden
                                          widths all equal, one of 16, 32, 64 */
-  int validate;              /* nonzero: conv_fwd/conv_bwd also check the CSR
-                                on the device (sorted rows, src in range) and
-                                wait for the result */
+  int validate;              /* nonzero: the calls also check their inputs on
+                                the device and wait for the result: sorted rows
+                                and senders in range (conv_fwd, conv_bwd,
+                                virial), wrapped positions (conv_fwd), a
+                                symmetric reverse index (conv_bwd) */
   int sum_paths;             /* nonzero: paths with the same output rank add
                                 into one block (FlashCart section 3,
                                 "Generating Cartesian tensor products"):
                                 d_out = sum of (2 l3 + 1) over the ranks that
                                 occur, (m3, channel) order inside a block;
                                 G follows the same layout */
+  int fp32_mfma_only;        /* float32 only.  0 (default): the radial last
+                                layer's float32 products run as six bf16
+                                matrix products of three-part operand splits
+                                (about float32 accuracy; the split-product
+                                option of the FastMACE page "Rewrites and
+                                precision options").  Nonzero: every float32
+                                product on float32 matrix cores. */
 } tpc_spec;
 
 typedef struct tpc_info {
@@ -119,6 +129,19 @@ typedef struct tpc_info {
   int r_width;               /* P*C */
   int nnz_cg;                /* non-zero coupling coefficients over all paths */
   int paths[TPC_MAX_PATHS][3];  /* (l1, l2, l3) in path order */
+  /* Sizes of the buffers a caller allocates (bytes). */
+  size_t edge_buffer_bytes;  /* per edge: Y, ef, rv and R of tpc_edge_buffers */
+  size_t dR_bytes;           /* per edge: one row of dR */
+  size_t fwd_workspace_bytes;          /* tpc_conv_fwd workspace (any chunk) */
+  size_t bwd_workspace_bytes_fixed;    /* tpc_conv_bwd workspace: fixed part ... */
+  size_t bwd_workspace_bytes_per_edge; /* ... plus this per chunk edge (dR kept in
+                                          the workspace when the caller passes
+                                          none), up to 16 edges of rounding;
+                                          tpc_workspace_query gives the exact
+                                          figure */
+  int dY_parts;              /* partial dY slices the backward keeps per edge */
+  size_t dh_edge_bytes;      /* per edge: one row of the dh_edge buffer of
+                                tpc_conv_bwd */
 } tpc_info;
 
 /* Per-edge buffers.  conv_fwd writes them for the edges of the rows it
@@ -145,8 +168,8 @@ tpc_status tpc_ctx_info(const tpc_ctx* ctx, tpc_info* info);
 tpc_status tpc_cg_table(const tpc_ctx* ctx, int path, double* out, size_t n);
 
 /* Workspace bytes for an operation: TPC_OP_NBR needs n_atoms and the host
- * cell; TPC_OP_FWD and TPC_OP_BWD need the number of edges of the chunk;
- * TPC_OP_VIRIAL needs n_atoms. */
+ * cell; TPC_OP_FWD, TPC_OP_BWD and TPC_OP_DOUBLE_BWD need the number of edges
+ * of the chunk; TPC_OP_VIRIAL needs n_atoms. */
 tpc_status tpc_workspace_query(const tpc_ctx* ctx, int op, int64_t n_atoms,
                                int64_t n_edges, const double* cell, size_t* bytes);
 
@@ -171,7 +194,9 @@ tpc_status tpc_workspace_query(const tpc_ctx* ctx, int op, int64_t n_atoms,
  *   rev       [edge_cap] int32, device, out: index of the reverse edge
  *             (j <- i, -S); the list is symmetric, so it always exists
  *   n_edges   host, out
- * Waits on `stream` once (to read the edge count). */
+ * Waits on `stream` twice: for the edge count, and after the reverse index is
+ * built for its status (an edge without a reverse returns
+ * TPC_ERR_PRECONDITION). */
 tpc_status tpc_nbr_build(const tpc_ctx* ctx, int64_t n_atoms, const double* pos,
                          const double* cell, const int32_t* species, int64_t edge_cap,
                          int32_t* row_ptr, int32_t* src, int32_t* shift, int32_t* rev,
@@ -219,6 +244,8 @@ tpc_status tpc_conv_fwd(const tpc_ctx* ctx, int64_t n_atoms, const double* pos,
  * dh and forces read the per-edge outputs of every edge, so pass them only on
  * the call that finishes the last chunk (all chunks' per-edge outputs written
  * earlier on this stream); an unchunked call passes everything at once.
+ * With spec.validate the rows, sender indices and the reverse index are
+ * checked first (TPC_ERR_PRECONDITION for an unsorted or non-symmetric list).
  * No atomics: every sum runs in a fixed order.
  */
 tpc_status tpc_conv_bwd(const tpc_ctx* ctx, int64_t n_atoms, int64_t n_edges,
@@ -228,6 +255,46 @@ tpc_status tpc_conv_bwd(const tpc_ctx* ctx, int64_t n_atoms, int64_t n_edges,
                         double scale, const void* grad_out, const tpc_edge_buffers* eb,
                         void* dR, void* g_edge, void* dh_edge, void* dh, void* forces,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* VJP-of-VJP ("double backward") of the tensor product for receivers
+ * [row_begin, row_end) (FlashCart section 3, "Symbolic derivatives": training
+ * on forces differentiates through the VJP; section 4, "Receiver-sorted
+ * derivatives": the same receiver-sorted edges, the incoming gradient of a
+ * receiver loaded once per program).  The VJP of tpc_conv_bwd maps
+ * (h, Y, R, G) to (dh, dY, dR).  Given cotangents u_dh, u_dY, u_dR of those
+ * outputs, this call differentiates
+ *     Lam = <u_dh, dh> + <u_dY, dY> + <u_dR, dR>
+ * with respect to G, h, Y and R (Y and R taken as independent inputs of the
+ * product; chaining into the radial network and the geometry is the
+ * caller's).  With T(a, y) the unweighted product of a path:
+ *     g_hat[i] = s sum_{e in row i} uR T(h_j, Y) + R T(h_j, uY) + R T(uh_j, Y)
+ *     h_hat[j] = s sum_{e: src e = j} sum_p C . (uR Y + R uY) . G[i]
+ *     Y_hat[e] = s sum_u sum_p C . (uR h_j + R uh_j) . G[i]
+ *     R_hat[e] = s sum_m3 G[i] . (T(h_j, uY) + T(uh_j, Y))
+ * h_hat is gathered along each row through the symmetric list (the reverse
+ * edge's cotangents are read at rev[e]); every sum has a fixed order, no
+ * atomics.
+ *   rev       [n_edges] int32 from tpc_nbr_build
+ *   h, grad_out, eb (Y and R of the chunk)   as for tpc_conv_bwd
+ *   u_dh      [n_atoms][d_in][C] device
+ *   u_dY      [n_edges][d_sh] device, every edge (absolute index: the sender
+ *             side reads it at reverse edges outside the chunk)
+ *   u_dR      [n_edges][P*C] device, every edge (absolute index)
+ *   g_hat     [n_atoms][d_out][C] device, out: rows [row_begin, row_end)
+ *   h_hat     [n_atoms][d_in][C] device, out: rows [row_begin, row_end)
+ *   Y_hat     [E_chunk][d_sh] device, out (chunk index)
+ *   R_hat     [E_chunk][P*C] device, out (chunk index)
+ *   workspace tpc_workspace_query(TPC_OP_DOUBLE_BWD, n_atoms, E_chunk)
+ * Separate path outputs only: with spec.sum_paths the call returns
+ * TPC_ERR_UNSUPPORTED.  With spec.validate the rows and the reverse index are
+ * checked first. */
+tpc_status tpc_conv_double_bwd(const tpc_ctx* ctx, int64_t n_atoms, int64_t n_edges,
+                               const int32_t* row_ptr, const int32_t* src, const int32_t* rev,
+                               int64_t row_begin, int64_t row_end, int64_t edge_begin,
+                               int64_t edge_end, const void* h, double scale, const void* grad_out,
+                               const tpc_edge_buffers* eb, const void* u_dh, const void* u_dY,
+                               const void* u_dR, void* g_hat, void* h_hat, void* Y_hat, void* R_hat,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Virial of L: W[a][b] = dL/d(eps_ab) for a homogeneous strain
  * x -> (I + eps) x applied to the positions and the cell rows together.  This
@@ -267,7 +334,10 @@ tpc_status tpc_timing_collect(tpc_kernel_time* out, int max, int* n);
 
 const char* tpc_status_string(tpc_status status);
 
-/* Messages of the last failed call on this thread ("" if none). */
+/* Messages of the last failed call on this thread ("" if none).  Errors are
+ * kept per thread rather than per context: tpc_ctx_create can fail before a
+ * context exists, and concurrent calls on one context from several threads
+ * each see their own messages. */
 const char* tpc_last_error(void);
 
 #ifdef __cplusplus

@@ -70,7 +70,7 @@ class Problem:
     """Inputs of one convolution call, with per-edge quantities on demand."""
 
     def __init__(self, layout: Layout, pos, cell, row_ptr, src, shift, h, W,
-                 r_cut, scale=1.0, G=None):
+                 r_cut, scale=1.0, G=None, radial_table=None):
         self.L = layout
         self.pos = np.asarray(pos, dtype=np.float64)
         self.cell = np.asarray(cell, dtype=np.float64)
@@ -84,6 +84,9 @@ class Problem:
         self.G = G
         self.recv = nbr.receivers_of(self.row_ptr)
         self.C = cg.tables(layout)
+        # optional piecewise Chebyshev table [pieces, degree+1, P*C] standing
+        # in for the radial MLP (``radial.chebyshev_table``)
+        self.table = None if radial_table is None else np.asarray(radial_table, dtype=np.float64)
 
     # ---- per-edge geometry and weights (FlashCart §2; radial module) -------
     def rvec(self, e):
@@ -94,7 +97,10 @@ class Problem:
         r = np.sqrt((v * v).sum(-1))
         Y = sh.sh(v, self.L.sh_lmax)
         ef = radial.edge_features(r, self.r_cut)
-        R, _ = radial.mlp_forward(ef, self.W)
+        if self.table is not None:
+            R, _ = radial.chebyshev_eval(self.table, r, self.r_cut)
+        else:
+            R, _ = radial.mlp_forward(ef, self.W)
         return v, r, Y, ef, R
 
     # ---- the unweighted path products T ------------------------------------
@@ -148,10 +154,16 @@ class Problem:
                                                    hs[:, L.in_slice(l1)], Gp, Rp, optimize=True)
             dh_c[:, L.in_slice(l1)] += s * Rp[:, None, :] * np.einsum(
                 "abk,eb,eku->eau", self.C[p], Y[:, L.sh_slice(l2)], Gp, optimize=True)
-        d_ef = radial.mlp_input_grad(dR, ef, self.W)
         rhat = v / r[:, None]
         g = np.einsum("el,elk->ek", dY, sh.sh_grad(v, L.sh_lmax))
-        g += (d_ef * radial.edge_features_dr(r, self.r_cut)).sum(-1)[:, None] * rhat
+        if self.table is not None:
+            # dL/dr through the table's own derivative series
+            _, dRdr = radial.chebyshev_eval(self.table, r, self.r_cut)
+            d_ef = None
+            g += (dR * dRdr).sum(-1)[:, None] * rhat
+        else:
+            d_ef = radial.mlp_input_grad(dR, ef, self.W)
+            g += (d_ef * radial.edge_features_dr(r, self.r_cut)).sum(-1)[:, None] * rhat
         return dict(dR=dR, dY=dY, d_ef=d_ef, g=g, dh_contrib=dh_c)
 
     def backward(self, max_edges=4096):

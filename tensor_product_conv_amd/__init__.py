@@ -20,14 +20,15 @@ import os
 from dataclasses import dataclass, field
 
 __all__ = ["Spec", "Context", "NeighbourList", "EdgeBuffers", "TpcError", "library",
-           "nbr_build", "conv_fwd", "conv_bwd", "virial", "timing_enable", "timing_collect",
+           "nbr_build", "conv_fwd", "conv_bwd", "conv_double_bwd", "virial", "timing_enable",
+           "timing_collect",
            "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpconv.so")
 
 TPC_MAX_LAYERS = 8
 TPC_MAX_PATHS = 32
-OP_NBR, OP_FWD, OP_BWD, OP_VIRIAL = 0, 1, 2, 3
+OP_NBR, OP_FWD, OP_BWD, OP_VIRIAL, OP_DOUBLE_BWD = 0, 1, 2, 3, 4
 STATUS = {0: "ok", 1: "invalid", 2: "unsupported", 3: "capacity", 4: "precondition",
           5: "workspace", 6: "device"}
 
@@ -44,13 +45,17 @@ class _Spec(ctypes.Structure):
                 ("sh_lmax", ctypes.c_int), ("out_lmax", ctypes.c_int), ("n_bessel", ctypes.c_int),
                 ("poly_p", ctypes.c_int), ("n_species", ctypes.c_int), ("r_cut", ctypes.c_double),
                 ("n_layers", ctypes.c_int), ("layer_dims", ctypes.c_int * (TPC_MAX_LAYERS + 1)),
-                ("validate", ctypes.c_int), ("sum_paths", ctypes.c_int)]
+                ("validate", ctypes.c_int), ("sum_paths", ctypes.c_int), ("fp32_mfma_only", ctypes.c_int)]
 
 
 class _Info(ctypes.Structure):
     _fields_ = [("n_paths", ctypes.c_int), ("d_in", ctypes.c_int), ("d_sh", ctypes.c_int),
                 ("d_out", ctypes.c_int), ("r_width", ctypes.c_int), ("nnz_cg", ctypes.c_int),
-                ("paths", (ctypes.c_int * 3) * TPC_MAX_PATHS)]
+                ("paths", (ctypes.c_int * 3) * TPC_MAX_PATHS),
+                ("edge_buffer_bytes", ctypes.c_size_t), ("dR_bytes", ctypes.c_size_t),
+                ("fwd_workspace_bytes", ctypes.c_size_t), ("bwd_workspace_bytes_fixed", ctypes.c_size_t),
+                ("bwd_workspace_bytes_per_edge", ctypes.c_size_t), ("dY_parts", ctypes.c_int),
+                ("dh_edge_bytes", ctypes.c_size_t)]
 
 
 class _KernelTime(ctypes.Structure):
@@ -92,6 +97,9 @@ def library():
                                  ctypes.POINTER(_VP), ctypes.c_double, _VP,
                                  ctypes.POINTER(_EdgeBuffers), _VP, _VP, _VP, _VP, _VP, _VP,
                                  ctypes.c_size_t, _VP]
+    lib.tpc_conv_double_bwd.argtypes = [_VP, _I64, _I64, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _VP,
+                                        ctypes.c_double, _VP, ctypes.POINTER(_EdgeBuffers), _VP, _VP,
+                                        _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]
     lib.tpc_virial.argtypes = [_VP, _I64, _I64, _VP, ctypes.POINTER(ctypes.c_double), _VP, _VP, _VP,
                                _VP, _VP, _VP, ctypes.c_size_t, _VP]
     lib.tpc_timing_enable.argtypes = [ctypes.c_int]
@@ -102,8 +110,8 @@ def library():
     lib.tpc_last_error.argtypes = []
     lib.tpc_last_error.restype = ctypes.c_char_p
     for name in ("tpc_ctx_create", "tpc_ctx_info", "tpc_cg_table", "tpc_workspace_query",
-                 "tpc_nbr_build", "tpc_conv_fwd", "tpc_conv_bwd", "tpc_virial", "tpc_timing_enable",
-                 "tpc_timing_collect"):
+                 "tpc_nbr_build", "tpc_conv_fwd", "tpc_conv_bwd", "tpc_conv_double_bwd", "tpc_virial",
+                 "tpc_timing_enable", "tpc_timing_collect"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -162,6 +170,7 @@ class Spec:
     poly_p: int = 5
     validate: bool = False
     sum_paths: bool = False
+    fp32_mfma_only: bool = False
 
     def to_c(self):
         s = _Spec()
@@ -175,6 +184,7 @@ class Spec:
             s.layer_dims[k] = int(d)
         s.validate = int(bool(self.validate))
         s.sum_paths = int(bool(self.sum_paths))
+        s.fp32_mfma_only = int(bool(self.fp32_mfma_only))
         return s
 
 
@@ -216,6 +226,9 @@ class Context:
         self.n_paths, self.d_in, self.d_sh, self.d_out = info.n_paths, info.d_in, info.d_sh, info.d_out
         self.r_width, self.nnz_cg = info.r_width, info.nnz_cg
         self.paths = [tuple(info.paths[p]) for p in range(info.n_paths)]
+        self.sizes = {k: getattr(info, k) for k in (
+            "edge_buffer_bytes", "dR_bytes", "fwd_workspace_bytes", "bwd_workspace_bytes_fixed",
+            "bwd_workspace_bytes_per_edge", "dY_parts", "dh_edge_bytes")}
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -350,6 +363,36 @@ class Context:
                                       _ptr(ws), ws.numel(), _stream()))
         return dh, dR, forces, g_edge
 
+    # ---- VJP-of-VJP -------------------------------------------------------------
+    def conv_double_bwd(self, nl: NeighbourList, h, scale, G, eb: EdgeBuffers, u_dh, u_dY, u_dR,
+                        g_hat=None, h_hat=None, Y_hat=None, R_hat=None, workspace=None):
+        """Double backward of the chunk in ``eb`` for cotangents u_dh
+        [N, d_in, C], u_dY [n_edges, d_sh] and u_dR [n_edges, P*C] (every edge)
+        of the VJP outputs dh, dY, dR.  Returns (g_hat, h_hat, Y_hat, R_hat):
+        the gradients of <u_dh, dh> + <u_dY, dY> + <u_dR, dR> with respect to
+        G, h, Y and R (rows of the chunk's receivers for g_hat and h_hat; the
+        chunk's edges for Y_hat and R_hat)."""
+        t = _torch()
+        N = h.shape[0]
+        ne = eb.edge_end - eb.edge_begin
+        if g_hat is None:
+            g_hat = t.empty_like(G)
+        if h_hat is None:
+            h_hat = t.empty_like(h)
+        if Y_hat is None:
+            Y_hat = t.empty((ne, self.d_sh), dtype=self.dtype, device=h.device)
+        if R_hat is None:
+            R_hat = t.empty((ne, self.r_width), dtype=self.dtype, device=h.device)
+        ebc = eb.to_c()
+        ws = workspace if workspace is not None else \
+            self._workspace(self.workspace_bytes(OP_DOUBLE_BWD, N, ne), h.device)
+        _check(library().tpc_conv_double_bwd(self._h, N, nl.n_edges, _ptr(nl.row_ptr), _ptr(nl.src),
+                                             _ptr(nl.rev), eb.row_begin, eb.row_end, eb.edge_begin,
+                                             eb.edge_end, _ptr(h), float(scale), _ptr(G), ctypes.byref(ebc),
+                                             _ptr(u_dh), _ptr(u_dY), _ptr(u_dR), _ptr(g_hat), _ptr(h_hat),
+                                             _ptr(Y_hat), _ptr(R_hat), _ptr(ws), ws.numel(), _stream()))
+        return g_hat, h_hat, Y_hat, R_hat
+
     # ---- virial ----------------------------------------------------------------
     def virial(self, pos, cell, nl: NeighbourList, g_edge, out=None, workspace=None):
         """W [3, 3] = dL/d(strain) = sum_e g_e r_e^T from the edge gradients of
@@ -364,6 +407,10 @@ class Context:
                                     _ptr(nl.row_ptr), _ptr(nl.src), _ptr(nl.shift), _ptr(g_edge),
                                     _ptr(out), _ptr(ws), ws.numel(), _stream()))
         return out
+
+
+def conv_double_bwd(ctx: Context, *a, **k):
+    return ctx.conv_double_bwd(*a, **k)
 
 
 def virial(ctx: Context, *a, **k):
@@ -382,8 +429,9 @@ def conv_bwd(ctx: Context, *a, **k):
     return ctx.conv_bwd(*a, **k)
 
 
-def spec_for(cfg, validate=False):
+def spec_for(cfg, validate=False, fp32_mfma_only=False):
     """Spec of a workload configuration dict (see ``workloads.config``)."""
     return Spec(channels=cfg["C"], node_lmax=cfg["l1max"], sh_lmax=cfg["sh_lmax"],
                 out_lmax=cfg["out_lmax"], r_cut=cfg["r_cut"], layer_dims=list(cfg["layer_dims"]),
-                dtype=cfg["dtype"], validate=validate, sum_paths=bool(cfg.get("sum_paths", False)))
+                dtype=cfg["dtype"], validate=validate, sum_paths=bool(cfg.get("sum_paths", False)),
+                fp32_mfma_only=fp32_mfma_only)

@@ -3,9 +3,12 @@
     python -m tensor_product_conv_amd.build [--incremental] [--jobs N]
 
 Each source compiles to an object under _build/ (in parallel), then the
-objects link into tensor_product_conv_amd/libtpconv.so.  The neighbour build
-is compiled without floating-point contraction so its float64 edge test is
-bitwise reproducible; every file is compiled without packed-FP32 instructions.
+objects link into tensor_product_conv_amd/libtpconv.so.  The tensor-product
+kernel sources compile once per built configuration (-DTPC_CFG=<index>, see
+csrc/tp_config.hpp), so the heavy instantiations build side by side.  The
+neighbour build is compiled without floating-point contraction so its
+float64 edge test is bitwise reproducible; every file is compiled without
+packed-FP32 instructions.
 """
 from __future__ import annotations
 
@@ -22,9 +25,29 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtpconv.so")
 
-SOURCES = ["api.cpp", "nbr.hip", "scan.hip", "geom.hip", "radial.hip", "tp_fwd.hip",
-           "tp_bwd_edge.hip", "forces.hip"]
-HEADERS = ["common.hpp", "kernels.hpp", "nbr.hpp", "tables.hpp", "tp_impl.hpp"]
+PLAIN_SOURCES = ["api.cpp", "nbr.hip", "scan.hip", "geom.hip", "radial.hip", "tp_dispatch.hip",
+                 "forces.hip"]
+PER_CONFIG_SOURCES = ["tp_fwd.hip", "tp_bwd.hip", "tp_dbl.hip"]
+HEADERS = ["common.hpp", "kernels.hpp", "nbr.hpp", "tables.hpp", "tp_impl.hpp", "tp_config.hpp"]
+
+
+def n_configs():
+    with open(os.path.join(CSRC, "tp_config.hpp")) as f:
+        for line in f:
+            if line.startswith("#define TPC_TP_N_CONFIGS"):
+                return int(line.split()[2])
+    raise RuntimeError("TPC_TP_N_CONFIGS not found in tp_config.hpp")
+
+
+def units(only=None):
+    """(source, extra flags, object name) for every object of the library;
+    ``only`` restricts the per-configuration sources to those indices."""
+    out = [(src, [], src + ".o") for src in PLAIN_SOURCES]
+    for src in PER_CONFIG_SOURCES:
+        for k in range(n_configs()):
+            if only is None or k in only:
+                out.append((src, [f"-DTPC_CFG={k}"], f"{src}.{k}.o"))
+    return out
 
 ARCH = "gfx950"
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC", "-fconstexpr-steps=200000000",
@@ -40,15 +63,16 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm is required to build libtpconv.so)")
 
 
-def _compile(src, incremental):
-    obj = os.path.join(BUILD, src + ".o")
+def _compile(unit, incremental):
+    src, extra, name = unit
+    obj = os.path.join(BUILD, name)
     path = os.path.join(CSRC, src)
     if incremental and os.path.exists(obj):
         newest = max(os.path.getmtime(os.path.join(CSRC, f)) for f in [src] + HEADERS)
         newest = max(newest, os.path.getmtime(os.path.join(ROOT, "include", "tpconv.h")))
         if os.path.getmtime(obj) >= newest:
             return obj, None
-    cmd = [hipcc()] + COMMON + PER_FILE.get(src, []) + ["-c", path, "-o", obj]
+    cmd = [hipcc()] + COMMON + PER_FILE.get(src, []) + extra + ["-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         return obj, f"{' '.join(cmd)}\n{r.stdout}\n{r.stderr}"
@@ -57,10 +81,13 @@ def _compile(src, incremental):
 
 def build(incremental=False, jobs=None, verbose=True):
     os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
+    us = units()
+    # the slowest objects first, so they do not start last
+    us.sort(key=lambda u: (u[0] not in PER_CONFIG_SOURCES, u[2]))
+    jobs = jobs or min(len(us), max(1, (os.cpu_count() or 4)))
     objs, errs = [], []
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        for obj, err in ex.map(lambda s: _compile(s, incremental), SOURCES):
+        for obj, err in ex.map(lambda u: _compile(u, incremental), us):
             objs.append(obj)
             if err:
                 errs.append(err)

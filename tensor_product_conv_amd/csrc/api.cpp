@@ -2,8 +2,9 @@
 // context, workspace planning, argument checks and kernel sequencing.
 //
 // Every check runs before any device work, so a failing call enqueues nothing,
-// and every failed check is reported (the "PlanRefused lists every reason"
-// convention of the FastMACE page "Rewrites and precision options").
+// and all the failed checks are reported together, as the refusal of an
+// unsupported plan does on the FastMACE page "Rewrites and precision options"
+// (section "Toggle values").
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -202,7 +203,8 @@ struct BwdWs {
 };
 
 tpc::RadialPack pack_layout(const tpc_ctx* c) {
-  return tpc::radial_pack_layout(c->hidden, c->n_hidden, c->tab.np * c->spec.channels);
+  return tpc::radial_pack_layout(c->hidden, c->n_hidden, c->tab.np * c->spec.channels,
+                                 c->spec.fp32_mfma_only == 0);
 }
 
 struct FwdWs {
@@ -235,14 +237,15 @@ VirialWs virial_layout(int64_t n) {
   return w;
 }
 
-int waves_per_row(int C) { return C <= 64 ? 1 : C / 64; }
+int dy_parts(const tpc_ctx* c) { return tpc::tp_bwd_parts(c->spec.channels); }
+int yh_parts(const tpc_ctx* c) { return tpc::tp_dbl_parts(c->spec.dtype, c->spec.node_lmax, c->spec.channels); }
 
 BwdWs bwd_layout(const tpc_ctx* c, int64_t ne) {
   BwdWs w{};
   const size_t T = c->tsize;
   size_t off = 0;
-  w.dY = off;  // one partial dY slice per 64-channel wave of a row
-  off += align_up(T * (size_t)ne * c->tab.dsh * waves_per_row(c->spec.channels));
+  w.dY = off;  // one partial dY slice per wave of a row
+  off += align_up(T * (size_t)ne * c->tab.dsh * dy_parts(c));
   w.d_ef = off;
   off += align_up(T * (size_t)ne * 8);
   w.status = off;
@@ -254,6 +257,21 @@ BwdWs bwd_layout(const tpc_ctx* c, int64_t ne) {
   w.total_without_dR = off;
   w.dR = off;
   off += align_up(T * (size_t)ne * c->tab.np * c->spec.channels);
+  w.total = off;
+  return w;
+}
+
+struct DblWs {
+  size_t status, yh, total;
+};
+
+DblWs dbl_layout(const tpc_ctx* c, int64_t ne) {
+  DblWs w{};
+  size_t off = 0;
+  w.status = off;
+  off += align_up(sizeof(int32_t) * 8);
+  w.yh = off;  // one partial y_hat slice per wave of a row
+  off += align_up(c->tsize * (size_t)ne * c->tab.dsh * yh_parts(c));
   w.total = off;
   return w;
 }
@@ -369,8 +387,8 @@ tpc_status tpc_ctx_create(const tpc_spec* spec, tpc_ctx** out) {
       !tpc::tp_supported(s.dtype, s.node_lmax, s.sh_lmax, s.out_lmax, s.channels))
     E.add(TPC_ERR_UNSUPPORTED,
           "no fused kernel for dtype=%d node_lmax=%d sh_lmax=%d out_lmax=%d channels=%d "
-          "(built: (node_lmax, sh_lmax, out_lmax) in (1,2,1),(1,3,3),(2,3,3),(3,3,3), float32 "
-          "or float64, channels 1..64 or 128)",
+          "(built: (node_lmax, sh_lmax, out_lmax) in (1,2,1),(1,3,3),(2,3,3),(3,3,3) in float32, "
+          "(1,2,1),(1,3,3) in float64; channels 1..64 or 128)",
           s.dtype, s.node_lmax, s.sh_lmax, s.out_lmax, s.channels);
   tpc_status st = E.finish();
   if (st != TPC_OK) return st;
@@ -399,6 +417,15 @@ tpc_status tpc_ctx_info(const tpc_ctx* c, tpc_info* info) {
   info->d_out = c->tab.dout;
   info->r_width = c->tab.np * c->spec.channels;
   info->nnz_cg = c->tab.nnz;
+  const size_t T = c->tsize;
+  info->edge_buffer_bytes = T * (size_t)(c->tab.dsh + 8 + 4 + c->tab.np * c->spec.channels);
+  info->dR_bytes = T * (size_t)c->tab.np * c->spec.channels;
+  info->fwd_workspace_bytes = fwd_layout(c).total;
+  info->bwd_workspace_bytes_per_edge =
+      T * (size_t)(c->tab.dsh * dy_parts(c) + 8 + c->hidden) + T * (size_t)c->tab.np * c->spec.channels;
+  info->bwd_workspace_bytes_fixed = bwd_layout(c, 0).total;
+  info->dY_parts = dy_parts(c);
+  info->dh_edge_bytes = T * (size_t)c->tab.din * c->spec.channels;
   for (int p = 0; p < c->tab.np; ++p) {
     info->paths[p][0] = c->tab.path[p].l1;
     info->paths[p][1] = c->tab.path[p].l2;
@@ -454,6 +481,8 @@ tpc_status tpc_workspace_query(const tpc_ctx* c, int op, int64_t n_atoms, int64_
     *bytes = bwd_layout(c, n_edges).total;
   } else if (op == TPC_OP_VIRIAL) {
     *bytes = virial_layout(n_atoms).total;
+  } else if (op == TPC_OP_DOUBLE_BWD) {
+    *bytes = dbl_layout(c, n_edges).total;
   } else {
     E.add(TPC_ERR_INVALID, "unknown op %d", op);
   }
@@ -549,14 +578,13 @@ tpc_status tpc_nbr_build(const tpc_ctx* c, int64_t n, const double* pos, const d
   TPC_LAUNCH("nbr_fill", s, tpc::launch_nbr_fill(n, pos, g, bin_of, bin_start, bin_atoms, row_ptr, src, shift, s),
              "nbr_build: fill");
   TPC_LAUNCH("nbr_reverse", s, tpc::launch_nbr_reverse(n, row_ptr, src, shift, rev, status, s), "nbr_build: reverse");
-  if (c->spec.validate) {
-    TPC_HIP(hipMemcpyAsync(&host_status[0], status, sizeof(int32_t), hipMemcpyDeviceToHost, s),
-            "nbr_build: read status");
-    TPC_HIP(hipStreamSynchronize(s), "nbr_build: wait");
-    if (host_status[0]) {
-      flag_messages(host_status[0], E);
-      return E.finish();
-    }
+  // every edge must have found its reverse: the backward relies on symmetry
+  TPC_HIP(hipMemcpyAsync(&host_status[0], status, sizeof(int32_t), hipMemcpyDeviceToHost, s),
+          "nbr_build: read status");
+  TPC_HIP(hipStreamSynchronize(s), "nbr_build: wait");
+  if (host_status[0]) {
+    flag_messages(host_status[0], E);
+    return E.finish();
   }
   g_last_error.clear();
   return TPC_OK;
@@ -581,12 +609,17 @@ void need_ptr(const void* p, const char* name, size_t align, Errors& E) {
     E.add(TPC_ERR_INVALID, "%s must be %zu-byte aligned", name, align);
 }
 
+// Device checks of the inputs (spec.validate): the CSR rows of the call and,
+// when given, the reverse index (symmetry) and the wrapping of the positions
+// into the cell.  One wait for the combined status word.
 tpc_status run_csr_check(int64_t n, int64_t n_edges, const int32_t* row_ptr, const int32_t* src,
-                         const int32_t* shift, int64_t rb, int64_t re, int64_t eb, int64_t ee,
-                         int32_t* status, hipStream_t s) {
+                         const int32_t* shift, const int32_t* rev, int64_t rb, int64_t re,
+                         int64_t eb, int64_t ee, int32_t* status, hipStream_t s,
+                         const double* pos = nullptr, const tpc::NbrGrid* grid = nullptr) {
   TPC_HIP(tpc::launch_fill_i32(status, 1, 0, s), "csr check");
-  TPC_HIP(tpc::launch_csr_check(n, n_edges, row_ptr, src, shift, rb, re, eb, ee, status, s),
+  TPC_HIP(tpc::launch_csr_check(n, n_edges, row_ptr, src, shift, rev, rb, re, eb, ee, status, s),
           "csr check");
+  if (pos && grid) TPC_HIP(tpc::launch_wrap_check(n, pos, *grid, status, s), "position check");
   int32_t h = 0;
   TPC_HIP(hipMemcpyAsync(&h, status, sizeof(int32_t), hipMemcpyDeviceToHost, s), "csr check");
   TPC_HIP(hipStreamSynchronize(s), "csr check");
@@ -650,8 +683,15 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (c->spec.validate) {
-    st = run_csr_check(n, edge_end, row_ptr, src, shift, row_begin, row_end, edge_begin, edge_end,
-                       reinterpret_cast<int32_t*>(static_cast<char*>(ws) + FL.status), s);
+    tpc::NbrGrid grid{};
+    std::string why;
+    if (!make_grid(cell, c->spec.r_cut, &grid, &why)) {
+      E.add(TPC_ERR_INVALID, "%s", why.c_str());
+      return E.finish();
+    }
+    st = run_csr_check(n, edge_end, row_ptr, src, shift, nullptr, row_begin, row_end, edge_begin,
+                       edge_end, reinterpret_cast<int32_t*>(static_cast<char*>(ws) + FL.status), s,
+                       n > 0 ? pos : nullptr, &grid);
     if (st != TPC_OK) return st;
   }
   const int dt = c->spec.dtype;
@@ -759,7 +799,7 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
   char* w = static_cast<char*>(ws);
   int32_t* status = reinterpret_cast<int32_t*>(w + L.status);
   if (c->spec.validate) {
-    st = run_csr_check(n, n_edges, row_ptr, src, nullptr, row_begin, row_end, edge_begin, edge_end,
+    st = run_csr_check(n, n_edges, row_ptr, src, nullptr, rev, row_begin, row_end, edge_begin, edge_end,
                        status, s);
     if (st != TPC_OK) return st;
   }
@@ -771,7 +811,6 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
   tpc::TPArgs ta{};
   ta.row_ptr = row_ptr;
   ta.src = src;
-  ta.rev = rev;
   ta.row_begin = row_begin;
   ta.row_end = row_end;
   ta.edge_begin = edge_begin;
@@ -783,11 +822,12 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
   ta.R = eb->R;
   ta.n_chunk_edges = ne;
   ta.G = grad_out;
+  ta.rev = rev;
   ta.dR = dRp;
   ta.dY = dY;
   ta.dh_edge = dh_edge;
   if (ne > 0) {
-    TPC_LAUNCH("tp_bwd_edge", s, tpc::launch_tp_bwd_edge(dt, L1, L2, L3, ta, s), "conv_bwd: tensor product (edges)");
+    TPC_LAUNCH("tp_bwd_edge", s, tpc::launch_tp_bwd(dt, L1, L2, L3, ta, s), "conv_bwd: tensor product (edges)");
     const tpc::RadialPack PL = pack_layout(c);
     void* pk = w + L.pack;
     void* dA = w + L.dA;
@@ -798,8 +838,8 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
     TPC_LAUNCH("radial_bwd_mlp", s, tpc::launch_radial_bwd_mlp(dt, PL, ne, eb->ef, dA, pk, d_ef, s),
                "conv_bwd: radial hidden layers");
     TPC_LAUNCH("geom_bwd", s,
-               tpc::launch_geom_bwd(dt, L2, ne, edge_begin, c->spec.r_cut, eb->rv, dY,
-                                    waves_per_row(c->spec.channels), d_ef, g_edge, s),
+               tpc::launch_geom_bwd(dt, L2, ne, edge_begin, c->spec.r_cut, eb->rv, dY, dy_parts(c),
+                                    d_ef, g_edge, s),
                "conv_bwd: geometry");
   }
   if (dh)
@@ -808,6 +848,91 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
                "conv_bwd: dh row sums");
   if (forces)
     TPC_LAUNCH("forces", s, tpc::launch_forces(dt, n, row_ptr, rev, g_edge, forces, s), "conv_bwd: forces");
+  g_last_error.clear();
+  return TPC_OK;
+}
+
+tpc_status tpc_conv_double_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int32_t* row_ptr,
+                               const int32_t* src, const int32_t* rev, int64_t row_begin, int64_t row_end,
+                               int64_t edge_begin, int64_t edge_end, const void* h, double scale,
+                               const void* grad_out, const tpc_edge_buffers* eb, const void* u_dh,
+                               const void* u_dY, const void* u_dR, void* g_hat, void* h_hat, void* Y_hat,
+                               void* R_hat, void* ws, size_t ws_bytes, void* stream) {
+  Errors E;
+  if (!c) {
+    E.add(TPC_ERR_INVALID, "ctx must be non-null");
+    return E.finish();
+  }
+  check_chunk(c, n, row_begin, row_end, edge_begin, edge_end, E);
+  if (n_edges < edge_end) E.add(TPC_ERR_INVALID, "n_edges must be >= edge_end");
+  if (!std::isfinite(scale)) E.add(TPC_ERR_INVALID, "scale must be finite");
+  if (c->spec.sum_paths)
+    E.add(TPC_ERR_UNSUPPORTED, "the double backward needs separate path outputs (sum_paths = 0)");
+  const size_t va = 16;
+  need_ptr(row_ptr, "row_ptr", 4, E);
+  if (row_end > row_begin) {
+    need_ptr(h, "h", va, E);
+    need_ptr(grad_out, "grad_out", va, E);
+    need_ptr(u_dh, "u_dh", va, E);
+    need_ptr(g_hat, "g_hat", va, E);
+    need_ptr(h_hat, "h_hat", va, E);
+  }
+  if (edge_end > edge_begin) {
+    need_ptr(src, "src", 4, E);
+    need_ptr(rev, "rev", 4, E);
+    need_ptr(u_dY, "u_dY", c->tsize, E);
+    need_ptr(u_dR, "u_dR", va, E);
+    need_ptr(Y_hat, "Y_hat", c->tsize, E);
+    need_ptr(R_hat, "R_hat", va, E);
+  }
+  if (!eb) {
+    E.add(TPC_ERR_INVALID, "edge buffers must be non-null");
+  } else if (edge_end > edge_begin) {
+    need_ptr(eb->Y, "eb.Y", va, E);
+    need_ptr(eb->R, "eb.R", va, E);
+  }
+  const int64_t ne = edge_end - edge_begin;
+  const DblWs L = dbl_layout(c, ne > 0 ? ne : 0);
+  if (!ws) E.add(TPC_ERR_INVALID, "workspace must be non-null");
+  else if (!aligned(ws, 256)) E.add(TPC_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (ws && ws_bytes < L.total) E.add(TPC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  tpc_status st = E.finish();
+  if (st != TPC_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  if (c->spec.validate) {
+    st = run_csr_check(n, n_edges, row_ptr, src, nullptr, rev, row_begin, row_end, edge_begin, edge_end,
+                       reinterpret_cast<int32_t*>(w + L.status), s);
+    if (st != TPC_OK) return st;
+  }
+  tpc::TPArgs ta{};
+  ta.row_ptr = row_ptr;
+  ta.src = src;
+  ta.rev = rev;
+  ta.row_begin = row_begin;
+  ta.row_end = row_end;
+  ta.edge_begin = edge_begin;
+  ta.n_chunk_edges = ne;
+  ta.C = c->spec.channels;
+  ta.sum_paths = false;
+  ta.scale = scale;
+  ta.h = h;
+  ta.Y = eb->Y;
+  ta.R = eb->R;
+  ta.G = grad_out;
+  ta.uh = u_dh;
+  ta.uY = u_dY;
+  ta.uR = u_dR;
+  ta.g_hat = g_hat;
+  ta.x_hat = h_hat;
+  ta.w_hat = R_hat;
+  ta.dY = w + L.yh;
+  TPC_LAUNCH("tp_double_bwd", s,
+             tpc::launch_tp_dbl(c->spec.dtype, c->spec.node_lmax, c->spec.sh_lmax, c->spec.out_lmax, ta, s),
+             "conv_double_bwd: tensor product");
+  TPC_LAUNCH("part_sum", s, tpc::launch_part_sum(c->spec.dtype, yh_parts(c), ne, c->tab.dsh, w + L.yh, Y_hat, s),
+             "conv_double_bwd: y_hat slices");
   g_last_error.clear();
   return TPC_OK;
 }
@@ -849,7 +974,7 @@ tpc_status tpc_virial(const tpc_ctx* c, int64_t n, int64_t n_edges, const double
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   if (c->spec.validate && n > 0) {
-    st = run_csr_check(n, n_edges, row_ptr, src, shift, 0, n, 0, n_edges,
+    st = run_csr_check(n, n_edges, row_ptr, src, shift, nullptr, 0, n, 0, n_edges,
                        reinterpret_cast<int32_t*>(w + L.status), s);
     if (st != TPC_OK) return st;
   }

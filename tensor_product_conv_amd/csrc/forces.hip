@@ -35,11 +35,15 @@ k_forces(int64_t n, const int32_t* __restrict__ row_ptr, const int32_t* __restri
 
 // One thread per row: monotone row pointers, senders in range, rows strictly
 // increasing in (src, s1, s2, s3) (or non-decreasing in src when no shifts
-// are given), and the chunk's edge range consistent.
+// are given), and the chunk's edge range consistent.  With a reverse index,
+// every edge e = (i <- j) of the row must name an edge r = rev[e] of row j
+// whose sender is i and whose reverse is e (and, with shifts, whose shift is
+// the negated one): the list is symmetric.
 __global__ void __launch_bounds__(256)
 k_csr_check(int64_t n, int64_t n_edges, const int32_t* __restrict__ row_ptr,
-            const int32_t* __restrict__ src, const int32_t* __restrict__ shift, int64_t row_begin,
-            int64_t row_end, int64_t edge_begin, int64_t edge_end, int32_t* __restrict__ status) {
+            const int32_t* __restrict__ src, const int32_t* __restrict__ shift,
+            const int32_t* __restrict__ rev, int64_t row_begin, int64_t row_end,
+            int64_t edge_begin, int64_t edge_end, int32_t* __restrict__ status) {
   const int64_t i = row_begin + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= row_end) return;
   int flags = 0;
@@ -79,6 +83,18 @@ k_csr_check(int64_t n, int64_t n_edges, const int32_t* __restrict__ row_ptr,
         break;
       }
       prev = key;
+    }
+  }
+  if (!flags && rev) {
+    for (int e = lo; e < hi; ++e) {
+      const int r = rev[e];
+      const int j = src[e];
+      if (r < 0 || r >= n_edges || r < row_ptr[j] || r >= row_ptr[j + 1] || src[r] != i || rev[r] != e ||
+          (shift && (shift[3 * r] != -shift[3 * e] || shift[3 * r + 1] != -shift[3 * e + 1] ||
+                     shift[3 * r + 2] != -shift[3 * e + 2]))) {
+        flags |= kFlagNoReverse;
+        break;
+      }
     }
   }
   if (flags) atomicOr(status, flags);
@@ -188,14 +204,36 @@ hipError_t launch_forces(int dtype, int64_t n, const int32_t* row_ptr, const int
   return hipGetLastError();
 }
 
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_part_sum(int n_parts, int64_t n, const T* __restrict__ in, T* __restrict__ out) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  T acc = in[t];
+  for (int q = 1; q < n_parts; ++q) acc += in[q * n + t];
+  out[t] = acc;
+}
+
+hipError_t launch_part_sum(int dtype, int n_parts, int64_t ne, int width, const void* in, void* out,
+                           hipStream_t s) {
+  const int64_t n = ne * width;
+  if (n <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (dtype == 1)
+    k_part_sum<double><<<blocks, 256, 0, s>>>(n_parts, n, static_cast<const double*>(in), static_cast<double*>(out));
+  else
+    k_part_sum<float><<<blocks, 256, 0, s>>>(n_parts, n, static_cast<const float*>(in), static_cast<float*>(out));
+  return hipGetLastError();
+}
+
 hipError_t launch_csr_check(int64_t n, int64_t n_edges, const int32_t* row_ptr,
-                            const int32_t* src, const int32_t* shift, int64_t row_begin,
-                            int64_t row_end, int64_t edge_begin, int64_t edge_end,
-                            int32_t* status, hipStream_t s) {
+                            const int32_t* src, const int32_t* shift, const int32_t* rev,
+                            int64_t row_begin, int64_t row_end, int64_t edge_begin,
+                            int64_t edge_end, int32_t* status, hipStream_t s) {
   const int64_t rows = row_end - row_begin;
   if (rows <= 0) return hipSuccess;
   k_csr_check<<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(
-      n, n_edges, row_ptr, src, shift, row_begin, row_end, edge_begin, edge_end, status);
+      n, n_edges, row_ptr, src, shift, rev, row_begin, row_end, edge_begin, edge_end, status);
   return hipGetLastError();
 }
 

@@ -27,7 +27,6 @@ struct RadialWeights {
 struct TPArgs {
   const int32_t* row_ptr;
   const int32_t* src;
-  const int32_t* rev;     // reverse-edge index (backward)
   int64_t row_begin, row_end, edge_begin;
   int64_t n_chunk_edges;  // edges of the chunk (stride of the partial dY slices)
   int C;           // channels
@@ -39,8 +38,18 @@ struct TPArgs {
   const void* G;   // [N][d_out][C]  (backward)
   void* out;       // forward: out [N][d_out][C]
   void* dR;        // backward edge kernel: [E][P*C]
-  void* dY;        // backward edge kernel: partial dY [C/64 slices][E][d_sh]
-  void* dh_edge;   // backward edge kernel: [n_edges][d_in][C], absolute edge index
+  void* dY;        // backward: partial dY [parts][E][d_sh], parts = tp_bwd_parts
+                   // (double backward: partial y_hat, parts = tp_dbl_parts)
+  void* dh_edge;   // backward: [n_edges][d_in][C] per-edge dh contributions,
+                   // absolute edge index (stored at the reverse edge's slot)
+  // double backward: cotangents of the VJP outputs and its results
+  const int32_t* rev;  // reverse-edge index [n_edges]
+  const void* uh;  // [N][d_in][C]
+  const void* uY;  // [n_edges][d_sh], absolute edge index
+  const void* uR;  // [n_edges][P*C], absolute edge index
+  void* g_hat;     // [N][d_out][C], rows [row_begin, row_end)
+  void* x_hat;     // [N][d_in][C], rows [row_begin, row_end)
+  void* w_hat;     // [E_chunk][P*C]
 };
 
 hipError_t launch_geom_fwd(int dtype, int L2, const GeomArgs& a, void* Y, void* ef, void* rv,
@@ -64,13 +73,16 @@ hipError_t launch_geom_bwd(int dtype, int L2, int64_t ne, int64_t edge_begin, do
 // every weight), a bf16 section counted in float slots (two values per slot):
 //   fs  forward last layer     [nblk][64][H/32][3 parts][8]
 //   bs  backward last layer    [pc/32][64][H/16][3 parts][8]
+// x6 off keeps every float32 product on float32 matrix cores.
 struct RadialPack {
   int H, NH, pc, nblk;
+  bool x6;
   int64_t f0, fh, fl, bl, bh, b0, fs, bs, total;
 };
-inline RadialPack radial_pack_layout(int H, int NH, int pc) {
+inline RadialPack radial_pack_layout(int H, int NH, int pc, bool x6 = true) {
   auto up = [](int64_t v) { return (v + 63) / 64 * 64; };
   RadialPack L{};
+  L.x6 = x6;
   L.H = H;
   L.NH = NH;
   L.pc = pc;
@@ -113,10 +125,23 @@ hipError_t launch_radial_bwd_mlp(int dtype, const RadialPack& L, int64_t ne, con
 // Which (node_lmax, sh_lmax, out_lmax, channels) the fused kernels are built for.
 bool tp_supported(int dtype, int L1, int L2, int L3, int C);
 hipError_t launch_tp_fwd(int dtype, int L1, int L2, int L3, const TPArgs& a, hipStream_t s);
-hipError_t launch_tp_bwd_edge(int dtype, int L1, int L2, int L3, const TPArgs& a, hipStream_t s);
+// dR, the partial dY slices and the per-edge dh contributions of rows
+// [row_begin, row_end)
+hipError_t launch_tp_bwd(int dtype, int L1, int L2, int L3, const TPArgs& a, hipStream_t s);
+// number of partial dY slices launch_tp_bwd writes (one per 64-channel wave)
+int tp_bwd_parts(int C);
+// number of partial y_hat slices launch_tp_dbl writes (one per wave of a row)
+int tp_dbl_parts(int dtype, int L1, int C);
 // dh[j] = scale * sum_{e in row j} dh_edge[e] for every atom
 hipError_t launch_dh_gather(int dtype, int64_t n, int din_c, const int32_t* row_ptr, double scale,
                             const void* dh_edge, void* dh, hipStream_t s);
+// VJP-of-VJP of rows [row_begin, row_end): g_hat, x_hat of the rows, w_hat
+// and tp_bwd_parts partial slices of y_hat (in TPArgs::dY) of the chunk's
+// edges; separate (not path-summed) outputs only
+hipError_t launch_tp_dbl(int dtype, int L1, int L2, int L3, const TPArgs& a, hipStream_t s);
+// out[e][k] = sum over the n_parts slices of in[part][e][k], in slice order
+hipError_t launch_part_sum(int dtype, int n_parts, int64_t ne, int width, const void* in, void* out,
+                           hipStream_t s);
 
 hipError_t launch_forces(int dtype, int64_t n, const int32_t* row_ptr, const int32_t* rev,
                          const void* g, void* forces, hipStream_t s);
@@ -125,9 +150,10 @@ constexpr int kVirialBlock = 256;
 inline int64_t virial_blocks(int64_t n) { return n > 0 ? (n + kVirialBlock - 1) / kVirialBlock : 0; }
 hipError_t launch_virial(int dtype, int64_t n, const GeomArgs& a, const void* g, double* part,
                          void* W, hipStream_t s);
+// rows [row_begin, row_end): order, ranges, and (rev non-null) symmetry
 hipError_t launch_csr_check(int64_t n, int64_t n_edges, const int32_t* row_ptr,
-                            const int32_t* src, const int32_t* shift, int64_t row_begin,
-                            int64_t row_end, int64_t edge_begin, int64_t edge_end,
-                            int32_t* status, hipStream_t s);
+                            const int32_t* src, const int32_t* shift, const int32_t* rev,
+                            int64_t row_begin, int64_t row_end, int64_t edge_begin,
+                            int64_t edge_end, int32_t* status, hipStream_t s);
 
 }  // namespace tpc

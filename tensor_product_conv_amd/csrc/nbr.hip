@@ -64,6 +64,22 @@ __global__ void k_bin(int64_t n, const double* __restrict__ pos, NbrGrid g,
   atomicAdd(&bin_count[flat], 1);
 }
 
+// Wrapped positions: every fractional coordinate in [0, 1) (the same test
+// and tolerance as the binning above), for the checks of the convolution
+// calls.
+__global__ void k_wrap_check(int64_t n, const double* __restrict__ pos, NbrGrid g,
+                             int32_t* __restrict__ status) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const double x = pos[3 * i], y = pos[3 * i + 1], z = pos[3 * i + 2];
+  int flags = 0;
+  for (int k = 0; k < 3; ++k) {
+    const double f = (x * g.inv[0][k] + y * g.inv[1][k]) + z * g.inv[2][k];
+    if (!(f >= -1e-10 && f < 1.0 + 1e-10)) flags |= kFlagUnwrapped;
+  }
+  if (flags) atomicOr(status, flags);
+}
+
 __global__ void k_scatter(int64_t n, const int32_t* __restrict__ bin_of,
                           const int32_t* __restrict__ bin_start, int32_t* __restrict__ cursor,
                           int32_t* __restrict__ bin_atoms) {
@@ -210,6 +226,13 @@ k_reverse(int64_t n, const int32_t* __restrict__ row_ptr, const int32_t* __restr
 }
 
 }  // namespace
+
+hipError_t launch_wrap_check(int64_t n, const double* pos, const NbrGrid& g, int32_t* status,
+                             hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_wrap_check<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(n, pos, g, status);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;

@@ -34,6 +34,8 @@ hipError_t launch_nbr_count(int64_t n, const double* pos, const NbrGrid& g, cons
 hipError_t launch_nbr_fill(int64_t n, const double* pos, const NbrGrid& g, const int32_t* bin_of,
                            const int32_t* bin_start, const int32_t* bin_atoms,
                            const int32_t* row_ptr, int32_t* src, int32_t* shift, hipStream_t s);
+hipError_t launch_wrap_check(int64_t n, const double* pos, const NbrGrid& g, int32_t* status,
+                             hipStream_t s);
 hipError_t launch_nbr_reverse(int64_t n, const int32_t* row_ptr, const int32_t* src,
                               const int32_t* shift, int32_t* rev, int32_t* status, hipStream_t s);
 

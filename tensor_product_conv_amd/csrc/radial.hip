@@ -555,7 +555,8 @@ __device__ __forceinline__ void radial_last_pairs_x6(int64_t e0, int64_t ne, int
 // VEC: 16-byte stores of whole 16-column blocks (float32, width a multiple
 // of 16); PAIRS: width also a multiple of 32, full waves use the paired
 // line-wide stores.
-template <typename T, int H, int NH, int S, bool VEC, bool PAIRS>
+// X6: float32 last layer as bf16-split products (off: float32 matrix cores).
+template <typename T, int H, int NH, int S, bool VEC, bool PAIRS, bool X6>
 __global__ void __launch_bounds__(256)
 k_radial_fwd(int64_t ne, int pc, const T* __restrict__ ef, const T* __restrict__ pk, RadialPack L,
              T* __restrict__ R) {
@@ -563,7 +564,7 @@ k_radial_fwd(int64_t ne, int pc, const T* __restrict__ ef, const T* __restrict__
   const int lane = threadIdx.x % kWave;
   const int64_t e0 = (blockIdx.x * (int64_t)(blockDim.x / kWave) + threadIdx.x / kWave) * (16 * S);
   // the shared-weight path keeps waves without edges for its barriers
-  constexpr bool kX6 = PAIRS && x6_shape(H, 32);
+  constexpr bool kX6 = X6 && PAIRS && x6_shape(H, 32);
   if (!kX6 && e0 >= ne) return;
 
   T act[S][NB][4];
@@ -916,14 +917,17 @@ hipError_t fwd_impl(int64_t ne, int pc, const T* ef, const T* pk, const RadialPa
                    reinterpret_cast<uintptr_t>(R) % 16 == 0;
   if constexpr (std::is_same<T, float>::value) {
     if (vec && pc % 32 == 0) {
-      k_radial_fwd<T, H, NH, kFwdStrips, true, true><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
+      if (L.x6)
+        k_radial_fwd<T, H, NH, kFwdStrips, true, true, true><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
+      else
+        k_radial_fwd<T, H, NH, kFwdStrips, true, true, false><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
       return hipGetLastError();
     }
   }
   if (vec)
-    k_radial_fwd<T, H, NH, kFwdStrips, true, false><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
+    k_radial_fwd<T, H, NH, kFwdStrips, true, false, false><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
   else
-    k_radial_fwd<T, H, NH, kFwdStrips, false, false><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
+    k_radial_fwd<T, H, NH, kFwdStrips, false, false, false><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
   return hipGetLastError();
 }
 
@@ -934,7 +938,7 @@ template <typename T, int H>
 hipError_t bwd_dA_impl(int64_t ne, int pc, const T* dR, const T* pk, const RadialPack& L, T* dA3,
                        hipStream_t s) {
   if constexpr (std::is_same<T, float>::value && x6_shape(H, 32)) {
-    if (x6_shape(H, pc) && pc % 64 == 0 && reinterpret_cast<uintptr_t>(dR) % 16 == 0) {
+    if (L.x6 && x6_shape(H, pc) && pc % 64 == 0 && reinterpret_cast<uintptr_t>(dR) % 16 == 0) {
       const int64_t per_block = 4 * 16 * kBwdStripsX6;
       const __bf16* bs = reinterpret_cast<const __bf16*>(pk + L.bs);
       k_radial_bwd_dA_x6<H, kBwdStripsX6><<<(unsigned)((ne + per_block - 1) / per_block), 256, 0, s>>>(
@@ -1007,7 +1011,7 @@ hipError_t pack_impl(const RadialPack& L, const void* const* w, void* pk, hipStr
   const int64_t blocks = (L.total + 255) / 256;
   k_radial_pack<T><<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, s>>>(L, W, static_cast<T*>(pk));
   if constexpr (std::is_same<T, float>::value) {
-    if (x6_shape(L.H, L.pc)) {
+    if (L.x6 && x6_shape(L.H, L.pc)) {
       float* base = static_cast<float*>(pk);
       k_radial_pack_x6<<<1024, 256, 0, s>>>(L, W.w[L.NH], reinterpret_cast<__bf16*>(base + L.fs),
                                             reinterpret_cast<__bf16*>(base + L.bs));

@@ -335,4 +335,110 @@ constexpr bool m13_nonzero(const Table& t, int p, int a, int c) {
   return false;
 }
 
+// Path groups of the fused backward: NG waves of one receiver row and one
+// channel slice own whole l1 classes, so the sender-gradient rows (dh) that
+// different waves accumulate never overlap.  Among the ways to place the
+// classes on NG non-empty waves, the one with the smallest busiest wave is
+// taken (cost per edge: the per-channel multiply-adds of dR, dY and dh plus
+// the coupling matrix of the edge).  kofs[p] is the offset of path p's
+// entries in its wave's per-row coupling array K[(m1, m2)] (the non-zero
+// (m1, m2) pairs of the path, m1-major); nk[g] is that array's length.
+struct BwdGroups {
+  int ng;
+  int group[kMaxPaths];
+  int kofs[kMaxPaths];
+  int nk[8];
+  bool ok;  // every group non-empty
+};
+
+constexpr int m12_count(const Table& t, int p) {
+  int n = 0;
+  for (int a = 0; a <= 2 * t.path[p].l1; ++a)
+    for (int b = 0; b <= 2 * t.path[p].l2; ++b)
+      if (t.m12nz(p, a, b)) ++n;
+  return n;
+}
+
+// index of (m1, m2) among the non-zero pairs of path p (m1-major), -1 if zero
+constexpr int m12_index(const Table& t, int p, int m1, int m2) {
+  int n = 0;
+  for (int a = 0; a <= 2 * t.path[p].l1; ++a)
+    for (int b = 0; b <= 2 * t.path[p].l2; ++b)
+      if (t.m12nz(p, a, b)) {
+        if (a == m1 && b == m2) return n;
+        ++n;
+      }
+  return -1;
+}
+
+constexpr int bwd_path_cost(const Table& t, int p) {
+  int m13 = 0, nnz = 0;
+  for (int a = 0; a < 7; ++a)
+    for (int c = 0; c < 7; ++c) {
+      if (t.midx[p][a][c] >= 0) ++m13;
+      for (int b = 0; b < 7; ++b)
+        if (t.cg[p][a][b][c] != 0.0) ++nnz;
+    }
+  const int n2 = 2 * t.path[p].l2 + 1, n3 = 2 * t.path[p].l3 + 1;
+  return m12_count(t, p) + 2 * n2 + n3 + m13 + nnz;
+}
+
+constexpr BwdGroups make_bwd_groups(const Table& t, int ng) {
+  BwdGroups g{};
+  g.ng = ng;
+  int ccost[4] = {};
+  for (int p = 0; p < t.np; ++p) ccost[t.path[p].l1] += bwd_path_cost(t, p);
+  int n_codes = 1;
+  for (int l = 0; l <= t.L1; ++l) n_codes *= ng;
+  int best_max = -1, best_code = -1;
+  for (int code = 0; code < n_codes; ++code) {
+    int ld[8] = {}, used[8] = {}, x = code;
+    for (int l = 0; l <= t.L1; ++l) {
+      ld[x % ng] += ccost[l];
+      used[x % ng] = 1;
+      x /= ng;
+    }
+    int mx = 0, empty = 0;
+    for (int k = 0; k < ng; ++k) {
+      if (ld[k] > mx) mx = ld[k];
+      if (!used[k]) empty = 1;
+    }
+    if (!empty && (best_max < 0 || mx < best_max)) {
+      best_max = mx;
+      best_code = code;
+    }
+  }
+  g.ok = best_code >= 0;
+  if (!g.ok) return g;
+  for (int p = 0; p < t.np; ++p) {
+    int x = best_code;
+    for (int l = 0; l < t.path[p].l1; ++l) x /= ng;
+    g.group[p] = x % ng;
+  }
+  for (int p = 0; p < t.np; ++p) {
+    g.kofs[p] = g.nk[g.group[p]];
+    g.nk[g.group[p]] += m12_count(t, p);
+  }
+  return g;
+}
+
+template <int L1, int L2, int L3, bool SUM, int NG>
+inline constexpr BwdGroups kBwdGroups = make_bwd_groups(kTable<L1, L2, L3, SUM>, NG);
+
+// Does backward group g own the l1 class l (its sender-gradient rows)?
+constexpr bool bwd_group_owns_l1(const Table& t, const BwdGroups& gr, int g, int l1) {
+  for (int p = 0; p < t.np; ++p)
+    if (gr.group[p] == g && t.path[p].l1 == l1) return true;
+  return false;
+}
+
+// Does backward group g read output row o (of G) for any of its paths?
+constexpr bool bwd_group_reads_row(const Table& t, const BwdGroups& gr, int g, int o) {
+  for (int p = 0; p < t.np; ++p)
+    if (gr.group[p] == g)
+      for (int m3 = 0; m3 <= 2 * t.path[p].l3; ++m3)
+        if (t.out_row(p, m3) == o) return true;
+  return false;
+}
+
 }  // namespace tpc

@@ -1,18 +1,13 @@
-// Instantiations of the fused forward tensor-product kernel.
+// Fused forward tensor-product kernel for one built configuration (compiled
+// once per configuration index, -DTPC_CFG=<index>).
+#include "tp_config.hpp"
 #include "tp_impl.hpp"
 
+#ifndef TPC_CFG
+#error "tp_fwd.hip is compiled once per configuration with -DTPC_CFG=<index>"
+#endif
+
 namespace tpc {
-
-bool tp_supported(int dtype, int L1, int L2, int L3, int C) {
-  if (!tp_channels_ok(C)) return false;
-#define TPC_X(T, A, B, D) \
-  if (dtype == tp_detail::dtype_id<T>() && L1 == A && L2 == B && L3 == D) return true;
-  TPC_TP_CONFIGS(TPC_X)
-#undef TPC_X
-  return false;
-}
-
-namespace {
 
 // Waves of a row: C = 128 takes two 64-channel waves, each over every path
 // (sender features and radial weights are then read once per edge); C = 64
@@ -46,16 +41,13 @@ hipError_t fwd_launch(const TPArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_tp_fwd(int dtype, int L1, int L2, int L3, const TPArgs& a, hipStream_t s) {
+template <typename T, int L1, int L2, int L3>
+hipError_t tp_fwd_cfg(const TPArgs& a, hipStream_t s) {
   if (a.row_end - a.row_begin <= 0) return hipSuccess;
-#define TPC_X(T, A, B, D) \
-  if (dtype == tp_detail::dtype_id<T>() && L1 == A && L2 == B && L3 == D)                  \
-    return a.sum_paths ? fwd_launch<T, A, B, D, true>(a, s) : fwd_launch<T, A, B, D, false>(a, s);
-  TPC_TP_CONFIGS(TPC_X)
-#undef TPC_X
-  return hipErrorInvalidValue;
+  return a.sum_paths ? fwd_launch<T, L1, L2, L3, true>(a, s) : fwd_launch<T, L1, L2, L3, false>(a, s);
 }
+
+using Cfg = TpCfg<TPC_CFG>;
+template hipError_t tp_fwd_cfg<Cfg::T, Cfg::L1, Cfg::L2, Cfg::L3>(const TPArgs&, hipStream_t);
 
 }  // namespace tpc

@@ -18,22 +18,9 @@
 // Backward of L = sum(G * out) (FlashCart section 3 "Symbolic derivatives":
 // the weight gradient is the inner product of the incoming gradient with the
 // unweighted product; the input gradients are the other factors times the
-// weight).  One wave per receiver row and 64 channels loads G[i] once per row;
-// per edge and path it forms K[m1][m2] = sum_m3 C^p[m1,m2,m3] G[i,(p,m3),u] and
-// from it
-//     W[m1]  = sum_m2 Y[e,(l2,m2)] K[m1][m2]
-//     dR[e,p,u] = s * sum_m1 h[src_e,m1,u] W[m1]
-//     t[m1]  += R[e,p,u] W[m1]                 (contribution to dh of the sender)
-//     Q[m2]  = sum_m1 h[src_e,m1,u] K[m1][m2]
-//     dY[e,(l2,m2)] = s * sum_u R[e,p,u] Q[m2]  (channel reduction)
-// The channel reduction of dY is a wave reduce-scatter; with several waves per
-// row each writes its partial sum and the geometry backward adds them in a
-// fixed order.  The sender contribution t is stored at the reverse edge's
-// slot: the list is symmetric, and the reverse of e = (i <- j, S) is
-// (j <- i, -S) in row j.  k_dh_gather then sums row j in CSR order,
-//     dh[j] = s * sum_{e in row j} t_stored[e],
-// so sender gradients are gathered per row instead of scattered with atomics
-// (FlashCart's VJP uses atomics there) or through a sender permutation.
+// weight): k_tp_bwd below, one pass over the receiver-sorted list that writes
+// dR, the channel sums of dY and, by a gather along each receiver's own row
+// (the list is symmetric), the sender-feature gradient dh.
 #pragma once
 
 #include "common.hpp"
@@ -149,31 +136,6 @@ __device__ __forceinline__ int channels(int C) {
   } else {
     return C;
   }
-}
-
-// Coupling-matrix row of one edge from its harmonics (compile-time sparsity).
-template <typename T, int L1, int L2, int L3>
-__device__ __forceinline__ void coupling_row(const T* y, T* out) {
-  static_for<kTable<L1, L2, L3>.np>([&](auto pc) {
-    constexpr int p = decltype(pc)::value;
-    constexpr Path P = kTable<L1, L2, L3>.path[p];
-    static_for<2 * P.l3 + 1>([&](auto m3c) {
-      constexpr int m3 = decltype(m3c)::value;
-      static_for<2 * P.l1 + 1>([&](auto m1c) {
-        constexpr int m1 = decltype(m1c)::value;
-        constexpr int k = kTable<L1, L2, L3>.midx[p][m1][m3];
-        if constexpr (k >= 0) {
-          T M = T(0);
-          static_for<2 * P.l2 + 1>([&](auto m2c) {
-            constexpr int m2 = decltype(m2c)::value;
-            constexpr double cv = kTable<L1, L2, L3>.cg[p][m1][m2][m3];
-            if constexpr (cv != 0.0) M += T(cv) * y[P.l2 * P.l2 + m2];
-          });
-          out[k] = M;
-        }
-      });
-    });
-  });
 }
 
 struct RowWave {
@@ -637,26 +599,350 @@ k_dh_gather(int64_t n, int din_c, const int32_t* __restrict__ row_ptr, T scale,
 }
 
 // ---------------------------------------------------------------------------
-inline int tp_waves_per_row(int C) { return C <= kTPWave ? 1 : C / kTPWave; }
-
-inline unsigned tp_blocks(int64_t rows, int C) {
-  const int64_t waves = rows * tp_waves_per_row(C);
-  return (unsigned)((waves + kTPWavesPerBlock - 1) / kTPWavesPerBlock);
+// VJP-of-VJP (double backward; FlashCart paper, section 3 "Symbolic
+// derivatives": training on forces differentiates through the VJP; section 4
+// "Receiver-sorted derivatives": the same receiver-sorted edges, the incoming
+// gradient of a receiver loaded once per row).  Given cotangents uh, uY, uR of
+// the VJP outputs dh, dY, dR, the scalar <uh,dh> + <uY,dY> + <uR,dR> is
+// differentiated with respect to G, h, Y and R.  With T(a, y) the unweighted
+// product of path p, i the receiver and j the sender of edge e:
+//   g_hat[i,(p,m3)] = s sum_{e in row i} T(h_j, uR Y + R uY) + R T(uh_j, Y)
+//   w_hat[e,p]      = s sum_{m1,m2} K[m1][m2] (h_j[m1] uY[m2] + uh_j[m1] Y[m2])
+//   y_hat[e,m2]     = s sum_u sum_p sum_m1 K[m1][m2] (uR h_j[m1] + R uh_j[m1])
+// with K = C . G[i] per row (as in the VJP), and, gathered along each row
+// through the symmetric list (the reverse edge of e has e's R and harmonics
+// (-1)^l2 Y[e], and its own cotangents uR[rev e], uY[rev e]):
+//   x_hat[i,(l1,m1)] = s sum_{e in row i} sum_p sum_{m2,m3} C^p G[j,(p,m3)]
+//                      ((-1)^l2 uR[rev e,p] Y[e,m2] + R[e,p] uY[rev e,m2])
+// Two kernels, each over rows with whole l1 classes per wave (kBwdGroups):
+// k_tp_dbl_recv (g_hat, w_hat, partial y_hat) and k_tp_dbl_send (x_hat).
+// Every sum is a fixed-order register accumulation: deterministic, no atomics.
+// Separate (not path-summed) outputs only: each path then owns its rows of
+// g_hat, so the waves of a row write disjoint rows.
+#define TBL kTable<L1, L2, L3, false>
+#define BGR kBwdGroups<L1, L2, L3, false, NG>
+template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int G>
+__device__ __forceinline__ void tp_dbl_recv_group(
+    const int32_t* __restrict__ src, int i, int e_lo, int e_hi, int64_t edge_begin, int64_t n_chunk_edges,
+    int CC, uint32_t c0, bool on, int part, T scale, const T* __restrict__ h, const T* __restrict__ uh,
+    const T* __restrict__ Y, const T* __restrict__ uY, const T* __restrict__ R, const T* __restrict__ uR,
+    const T* __restrict__ Gr, T* __restrict__ g_hat, T* __restrict__ w_hat, T* __restrict__ yhp) {
+  constexpr int NP = TBL.np, DIN = TBL.din, DSH = TBL.dsh, DOUT = TBL.dout;
+  constexpr int NK = BGR.nk[G] > 0 ? BGR.nk[G] : 1;
+  static_assert(BGR.ok, "every wave group owns an l1 class");
+  // float32 keeps K = s C . G[i] for the whole row; float64 (twice as wide)
+  // keeps the scaled G[i] rows and forms each K entry where it is used
+  constexpr bool kHoldK = sizeof(T) == 4;
+  const int PC = NP * CC;
+  const int lane = threadIdx.x % kTPWave;
+  T K[kHoldK ? NK : 1];
+  T gi[DOUT];
+  {
+    const T* __restrict__ gr = Gr + (int64_t)i * DOUT * CC;
+    static_for<DOUT>([&](auto oc) {
+      constexpr int o = decltype(oc)::value;
+      if constexpr (bwd_group_reads_row(TBL, BGR, G, o)) gi[o] = scale * ldc<MASKED ? 0 : 1>(gr, o * CC + c0, on);
+    });
+    if constexpr (kHoldK) static_for<NP>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      if constexpr (BGR.group[p] == G) {
+        constexpr Path P = TBL.path[p];
+        static_for<2 * P.l1 + 1>([&](auto m1c) {
+          constexpr int m1 = decltype(m1c)::value;
+          static_for<2 * P.l2 + 1>([&](auto m2c) {
+            constexpr int m2 = decltype(m2c)::value;
+            constexpr int k = m12_index(TBL, p, m1, m2);
+            if constexpr (k >= 0) {
+              constexpr int kk = BGR.kofs[p] + k;
+              T acc = T(0);
+              static_for<2 * P.l3 + 1>([&](auto m3c) {
+                constexpr int m3 = decltype(m3c)::value;
+                constexpr double cv = TBL.cg[p][m1][m2][m3];
+                constexpr int o = TBL.out_row(p, m3);
+                if constexpr (cv != 0.0) acc += T(cv) * gi[o];
+              });
+              K[kk] = acc;
+            }
+          });
+        });
+      }
+    });
+  }
+  T ga[DOUT];
+#pragma unroll
+  for (int o = 0; o < DOUT; ++o) ga[o] = T(0);
+  struct Buf {
+    T h[DIN];
+    T uh[DIN];
+    T r[NP];
+    T ur[NP];
+    T y, uy;
+  };
+  const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
+  auto load_j = [&](int e, int j, Buf& b) __attribute__((always_inline)) {
+    const T* __restrict__ hj = h + (int64_t)j * DIN * CC;
+    const T* __restrict__ uhj = uh + (int64_t)j * DIN * CC;
+    const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
+    const T* __restrict__ ure = uR + (int64_t)e * PC;
+    static_for<DIN>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int l1 = m >= 9 ? 3 : m >= 4 ? 2 : m >= 1 ? 1 : 0;
+      if constexpr (bwd_group_owns_l1(TBL, BGR, G, l1)) {
+        b.h[m] = ldc<MASKED ? 0 : 1>(hj, m * CC + c0, on);
+        b.uh[m] = ldc<MASKED ? 0 : 1>(uhj, m * CC + c0, on);
+      }
+    });
+    static_for<NP>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      if constexpr (BGR.group[p] == G) {
+        b.r[p] = ldc_nt<MASKED ? 0 : 1>(re, p * CC + c0, on);
+        b.ur[p] = ldc_nt<MASKED ? 0 : 1>(ure, p * CC + c0, on);
+      }
+    });
+    b.y = Y[((int64_t)e - edge_begin) * DSH + ylane];
+    b.uy = uY[(int64_t)e * DSH + ylane];
+  };
+  auto compute = [&](int e, const Buf& b) __attribute__((always_inline)) {
+    const int64_t el = (int64_t)e - edge_begin;
+    T ye[16], uye[16];
+#pragma unroll
+    for (int k = 0; k < DSH; ++k) {
+      ye[k] = lane_value(b.y, k);
+      uye[k] = lane_value(b.uy, k);
+    }
+    T* __restrict__ we = w_hat + el * PC;
+    T dy[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dy[k] = T(0);
+    static_for<NP>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      if constexpr (BGR.group[p] == G) {
+        constexpr Path P = TBL.path[p];
+        constexpr int n1 = 2 * P.l1 + 1, n2 = 2 * P.l2 + 1, n3 = 2 * P.l3 + 1;
+        // w_hat and the y_hat partial from X1 = h . K and X2 = uh . K
+        T w = T(0);
+        static_for<n2>([&](auto m2c) {
+          constexpr int m2 = decltype(m2c)::value;
+          T x1 = T(0), x2 = T(0);
+          static_for<n1>([&](auto m1c) {
+            constexpr int m1 = decltype(m1c)::value;
+            constexpr int k = m12_index(TBL, p, m1, m2);
+            if constexpr (k >= 0) {
+              T kv;
+              if constexpr (kHoldK) {
+                constexpr int kk = BGR.kofs[p] + k;
+                kv = K[kk];
+              } else {
+                kv = T(0);
+                static_for<n3>([&](auto m3c) {
+                  constexpr int m3 = decltype(m3c)::value;
+                  constexpr double cv = TBL.cg[p][m1][m2][m3];
+                  constexpr int o = TBL.out_row(p, m3);
+                  if constexpr (cv != 0.0) kv += T(cv) * gi[o];
+                });
+              }
+              x1 += b.h[P.l1 * P.l1 + m1] * kv;
+              x2 += b.uh[P.l1 * P.l1 + m1] * kv;
+            }
+          });
+          w += uye[P.l2 * P.l2 + m2] * x1 + ye[P.l2 * P.l2 + m2] * x2;
+          dy[P.l2 * P.l2 + m2] += b.ur[p] * x1 + b.r[p] * x2;
+        });
+        stc_nt<MASKED ? 0 : 1>(we, p * CC + c0, on, w);
+        // g_hat: T(h, uR Y + R uY) + T(uh, R Y)
+        T z[n2], zr[n2];
+        static_for<n2>([&](auto m2c) {
+          constexpr int m2 = decltype(m2c)::value;
+          z[m2] = b.ur[p] * ye[P.l2 * P.l2 + m2] + b.r[p] * uye[P.l2 * P.l2 + m2];
+          zr[m2] = b.r[p] * ye[P.l2 * P.l2 + m2];
+        });
+        static_for<n3>([&](auto m3c) {
+          constexpr int m3 = decltype(m3c)::value;
+          constexpr int o = TBL.out_row(p, m3);
+          static_for<n1>([&](auto m1c) {
+            constexpr int m1 = decltype(m1c)::value;
+            if constexpr (TBL.midx[p][m1][m3] >= 0) {
+              T t1 = T(0), t2 = T(0);
+              static_for<n2>([&](auto m2c) {
+                constexpr int m2 = decltype(m2c)::value;
+                constexpr double cv = TBL.cg[p][m1][m2][m3];
+                if constexpr (cv != 0.0) {
+                  t1 += T(cv) * z[m2];
+                  t2 += T(cv) * zr[m2];
+                }
+              });
+              ga[o] += b.h[P.l1 * P.l1 + m1] * t1 + b.uh[P.l1 * P.l1 + m1] * t2;
+            }
+          });
+        });
+      }
+    });
+    const T tot = wave_reduce_scatter16<T>(dy);
+    if (DSH == 16 || (lane >> 2) < DSH)
+      yhp[((int64_t)part * n_chunk_edges + el) * DSH + (lane >> 2)] = tot;
+  };
+  if (e_hi - e_lo > 64 * kIdxWindows) {
+    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, uniform(src[e]), b); },
+                   compute);
+  } else if (e_hi > e_lo) {
+    RowIdx<kIdxWindows> si;
+    si.init(src, e_lo, e_hi, lane);
+    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, si.get(e - e_lo), b); },
+                   compute);
+  }
+  T* __restrict__ gh = g_hat + (int64_t)i * DOUT * CC;
+  static_for<DOUT>([&](auto oc) {
+    constexpr int o = decltype(oc)::value;
+    if constexpr (bwd_group_reads_row(TBL, BGR, G, o)) stc<MASKED ? 0 : 1>(gh, o * CC + c0, on, scale * ga[o]);
+  });
 }
 
-inline bool tp_channels_ok(int C) { return (C >= 1 && C <= 64) || C == 128; }
+template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int G>
+__device__ __forceinline__ void tp_dbl_send_group(
+    const int32_t* __restrict__ src, const int32_t* __restrict__ rev, int i, int e_lo, int e_hi,
+    int64_t edge_begin, int CC, uint32_t c0, bool on, T scale, const T* __restrict__ Y,
+    const T* __restrict__ uY, const T* __restrict__ R, const T* __restrict__ uR,
+    const T* __restrict__ Gr, T* __restrict__ x_hat) {
+  constexpr int NP = TBL.np, DIN = TBL.din, DSH = TBL.dsh, DOUT = TBL.dout;
+  static_assert(BGR.ok, "every wave group owns an l1 class");
+  const int PC = NP * CC;
+  const int lane = threadIdx.x % kTPWave;
+  T xa[DIN];
+#pragma unroll
+  for (int m = 0; m < DIN; ++m) xa[m] = T(0);
+  struct Buf {
+    T g[DOUT];
+    T r[NP];
+    T ur[NP];
+    T y, uy;
+  };
+  const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
+  auto load_j = [&](int e, int j, int er, Buf& b) __attribute__((always_inline)) {
+    const T* __restrict__ gj = Gr + (int64_t)j * DOUT * CC;
+    const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
+    const T* __restrict__ urr = uR + (int64_t)er * PC;
+    static_for<DOUT>([&](auto oc) {
+      constexpr int o = decltype(oc)::value;
+      if constexpr (bwd_group_reads_row(TBL, BGR, G, o)) b.g[o] = ldc<MASKED ? 0 : 1>(gj, o * CC + c0, on);
+    });
+    static_for<NP>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      if constexpr (BGR.group[p] == G) {
+        b.r[p] = ldc_nt<MASKED ? 0 : 1>(re, p * CC + c0, on);
+        b.ur[p] = ldc<MASKED ? 0 : 1>(urr, p * CC + c0, on);
+      }
+    });
+    b.y = Y[((int64_t)e - edge_begin) * DSH + ylane];
+    b.uy = uY[(int64_t)er * DSH + ylane];
+  };
+  auto compute = [&](int, const Buf& b) __attribute__((always_inline)) {
+    T ye[16], uye[16];
+#pragma unroll
+    for (int k = 0; k < DSH; ++k) {
+      ye[k] = lane_value(b.y, k);
+      uye[k] = lane_value(b.uy, k);
+    }
+    static_for<NP>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      if constexpr (BGR.group[p] == G) {
+        constexpr Path P = TBL.path[p];
+        constexpr int n1 = 2 * P.l1 + 1, n2 = 2 * P.l2 + 1, n3 = 2 * P.l3 + 1;
+        constexpr T sg = (P.l2 & 1) ? T(-1) : T(1);
+        T wv[n2];
+        static_for<n2>([&](auto m2c) {
+          constexpr int m2 = decltype(m2c)::value;
+          wv[m2] = (sg * b.ur[p]) * ye[P.l2 * P.l2 + m2] + b.r[p] * uye[P.l2 * P.l2 + m2];
+        });
+        static_for<n1>([&](auto m1c) {
+          constexpr int m1 = decltype(m1c)::value;
+          static_for<n2>([&](auto m2c) {
+            constexpr int m2 = decltype(m2c)::value;
+            if constexpr (TBL.m12nz(p, m1, m2)) {
+              T kb = T(0);
+              static_for<n3>([&](auto m3c) {
+                constexpr int m3 = decltype(m3c)::value;
+                constexpr double cv = TBL.cg[p][m1][m2][m3];
+                constexpr int o = TBL.out_row(p, m3);
+                if constexpr (cv != 0.0) kb += T(cv) * b.g[o];
+              });
+              xa[P.l1 * P.l1 + m1] += wv[m2] * kb;
+            }
+          });
+        });
+      }
+    });
+  };
+  if (e_hi - e_lo > 64 * kIdxWindows) {
+    edge_loop<Buf>(e_lo, e_hi,
+                   [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, uniform(src[e]), uniform(rev[e]), b); },
+                   compute);
+  } else if (e_hi > e_lo) {
+    RowIdx<kIdxWindows> si, ri;
+    si.init(src, e_lo, e_hi, lane);
+    ri.init(rev, e_lo, e_hi, lane);
+    edge_loop<Buf>(e_lo, e_hi,
+                   [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, si.get(e - e_lo), ri.get(e - e_lo), b); },
+                   compute);
+  }
+  T* __restrict__ xi = x_hat + (int64_t)i * DIN * CC;
+  static_for<DIN>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    constexpr int l1 = m >= 9 ? 3 : m >= 4 ? 2 : m >= 1 ? 1 : 0;
+    if constexpr (bwd_group_owns_l1(TBL, BGR, G, l1)) stc<MASKED ? 0 : 1>(xi, m * CC + c0, on, scale * xa[m]);
+  });
+}
+#undef TBL
+#undef BGR
 
-// Compile-time waves per row for a channel count (0: fewer than 64 channels).
-inline int tp_nw(int C) { return C < 64 ? 0 : C / 64; }
+template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int NWC>
+__global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
+k_tp_dbl_recv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, int64_t row_begin,
+              int64_t row_end, int64_t edge_begin, int64_t n_chunk_edges, int C, T scale,
+              const T* __restrict__ h, const T* __restrict__ uh, const T* __restrict__ Y,
+              const T* __restrict__ uY, const T* __restrict__ R, const T* __restrict__ uR,
+              const T* __restrict__ Gr, T* __restrict__ g_hat, T* __restrict__ w_hat, T* __restrict__ yhp) {
+  const int lane = threadIdx.x % kTPWave;
+  const int64_t w = xcd_block() * kTPWavesPerBlock + threadIdx.x / kTPWave;
+  const int64_t row = row_begin + w / (NG * NWC);
+  if (row >= row_end) return;
+  const int i = uniform((int)row);
+  const int rem = uniform((int)(w % (NG * NWC)));
+  const int g = rem % NG, cw = rem / NG;
+  const int CC = MASKED ? C : 64 * NWC;
+  const uint32_t c0 = (uint32_t)(cw * 64 + lane);
+  const bool on = (int)c0 < C;
+  const int e_lo = uniform(row_ptr[i]), e_hi = uniform(row_ptr[i + 1]);
+  static_for<NG>([&](auto gc) {
+    constexpr int G = decltype(gc)::value;
+    if (g == G)
+      tp_dbl_recv_group<T, L1, L2, L3, NG, MASKED, G>(src, i, e_lo, e_hi, edge_begin, n_chunk_edges, CC, c0, on,
+                                                      rem, scale, h, uh, Y, uY, R, uR, Gr, g_hat, w_hat, yhp);
+  });
+}
 
-namespace tp_detail {
-template <typename T>
-constexpr int dtype_id() { return std::is_same<T, double>::value ? 1 : 0; }
-}  // namespace tp_detail
+template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int NWC>
+__global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
+k_tp_dbl_send(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src,
+              const int32_t* __restrict__ rev, int64_t row_begin, int64_t row_end, int64_t edge_begin,
+              int C, T scale, const T* __restrict__ Y, const T* __restrict__ uY, const T* __restrict__ R,
+              const T* __restrict__ uR, const T* __restrict__ Gr, T* __restrict__ x_hat) {
+  const int lane = threadIdx.x % kTPWave;
+  const int64_t w = xcd_block() * kTPWavesPerBlock + threadIdx.x / kTPWave;
+  const int64_t row = row_begin + w / (NG * NWC);
+  if (row >= row_end) return;
+  const int i = uniform((int)row);
+  const int rem = uniform((int)(w % (NG * NWC)));
+  const int g = rem % NG, cw = rem / NG;
+  const int CC = MASKED ? C : 64 * NWC;
+  const uint32_t c0 = (uint32_t)(cw * 64 + lane);
+  const bool on = (int)c0 < C;
+  const int e_lo = uniform(row_ptr[i]), e_hi = uniform(row_ptr[i + 1]);
+  static_for<NG>([&](auto gc) {
+    constexpr int G = decltype(gc)::value;
+    if (g == G)
+      tp_dbl_send_group<T, L1, L2, L3, NG, MASKED, G>(src, rev, i, e_lo, e_hi, edge_begin, CC, c0, on, scale, Y,
+                                                      uY, R, uR, Gr, x_hat);
+  });
+}
 
 }  // namespace tpc
-
-// Built (dtype, node_lmax, sh_lmax, out_lmax) sets.  Channels: 1..64 or 128.
-#define TPC_TP_CONFIGS(X)                                                    \
-  X(float, 1, 2, 1) X(float, 1, 3, 3) X(float, 2, 3, 3) X(float, 3, 3, 3)   \
-  X(double, 1, 2, 1) X(double, 1, 3, 3) X(double, 2, 3, 3) X(double, 3, 3, 3)

@@ -34,10 +34,10 @@ def torch():
 class Case:
     """Inputs of configuration k on the GPU plus an oracle problem."""
 
-    def __init__(self, k, validate=False, with_grad=True):
+    def __init__(self, k, validate=False, with_grad=True, data=None):
         t = torch()
         self.k = k
-        self.d = workloads.generate(k, with_grad=with_grad)
+        self.d = data if data is not None else workloads.generate(k, with_grad=with_grad)
         self.cfg = self.d["cfg"]
         self.ctx = tpc.Context(tpc.spec_for(self.cfg, validate))
         self.layout = paths.Layout(self.cfg["l1max"], self.cfg["sh_lmax"], self.cfg["out_lmax"],
@@ -126,3 +126,48 @@ def run_chunked(case, nl, chunks=1, keep_edges=None, want_forces=True):
                 kept[int(e)] = v
         t.cuda.synchronize()
     return dict(out=out, dh=dh, forces=forces, g_edge=g_edge, dR=kept, eb=eb)
+
+
+def cotangents(case, n_edges, seed):
+    """Seeded N(0,1) cotangents of the VJP outputs (dh, dY, dR), in the
+    context dtype: u_dh [N, d_in, C], u_dY [E, d_sh], u_dR [E, P*C]."""
+    rng = np.random.default_rng(seed)
+    dt = np.dtype(case.cfg["dtype"])
+    ctx = case.ctx
+    return (rng.standard_normal((case.N, ctx.d_in, case.cfg["C"])).astype(dt),
+            rng.standard_normal((n_edges, ctx.d_sh)).astype(dt),
+            rng.standard_normal((n_edges, ctx.r_width)).astype(dt))
+
+
+def run_double(case, nl, u, chunks=1, keep_edges=None):
+    """Forward (for the per-edge buffers) then the double backward over
+    receiver chunks.  Returns g_hat, h_hat and the Y_hat / R_hat rows of
+    ``keep_edges`` (absolute edge indices)."""
+    t = torch()
+    ctx = case.ctx
+    rp = nl.row_ptr.cpu().numpy()
+    s = case.scale(nl)
+    uh, uY, uR = [t.from_numpy(a).to("cuda") for a in u]
+    out = t.empty((case.N, ctx.d_out, case.cfg["C"]), dtype=ctx.dtype, device="cuda")
+    g_hat = t.empty_like(case.G)
+    h_hat = t.empty_like(case.h)
+    bounds = row_bounds(rp, chunks)
+    max_e = max(int(rp[b] - rp[a]) for a, b in bounds)
+    eb = ctx.alloc_edge_buffers(max_e, "cuda")
+    Yh = t.empty((max_e, ctx.d_sh), dtype=ctx.dtype, device="cuda")
+    Rh = t.empty((max_e, ctx.r_width), dtype=ctx.dtype, device="cuda")
+    keep = np.asarray([] if keep_edges is None else keep_edges, dtype=np.int64)
+    kept_Y, kept_R = {}, {}
+    for a, b in bounds:
+        e0, e1 = int(rp[a]), int(rp[b])
+        say(f"[gpu] conv_fwd/double_bwd cfg={case.k} rows=[{a},{b}) edges=[{e0},{e1})")
+        ctx.conv_fwd(case.pos, case.cell, nl, case.h, case.W, s, out=out, eb=eb, rows=(a, b), edges=(e0, e1))
+        ctx.conv_double_bwd(nl, case.h, s, case.G, eb, uh, uY, uR, g_hat=g_hat, h_hat=h_hat,
+                            Y_hat=Yh, R_hat=Rh)
+        sel = keep[(keep >= e0) & (keep < e1)]
+        if len(sel):
+            idx = t.from_numpy(sel - e0).to("cuda")
+            for e, y, r in zip(sel, Yh.index_select(0, idx).cpu().numpy(), Rh.index_select(0, idx).cpu().numpy()):
+                kept_Y[int(e)], kept_R[int(e)] = y, r
+        t.cuda.synchronize()
+    return dict(g_hat=g_hat, h_hat=h_hat, Y_hat=kept_Y, R_hat=kept_R)

@@ -76,6 +76,9 @@ def _spec(**over):
     (dict(layer_dims=[8, 64, 64, 64, 999]), 1, "paths*channels"),
     (dict(layer_dims=[8, 48, 1280]), 2, "radial MLP"),
     (dict(layer_dims=[7, 64, 1280]), 1, "layer_dims[0]"),
+    # float64 is built for node_lmax <= 1 only
+    (dict(dtype="float64", node_lmax=2, layer_dims=[8, 64, 64, 64, 17 * 128]), 2, "no fused kernel"),
+    (dict(dtype="float64", node_lmax=3, layer_dims=[8, 64, 64, 64, 23 * 128]), 2, "no fused kernel"),
 ])
 def test_spec_validation(over, status, needle):
     with pytest.raises(tpc.TpcError) as ei:

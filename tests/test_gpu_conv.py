@@ -25,8 +25,10 @@ def _prob(case, nl):
 # radial kernels that the wider networks do not take, and in 7 a radial
 # width of 17 column steps of 32: a half-filled last weight tile forward and
 # the float32 fallback backward); 8 is the small system with path-summed
-# outputs (one block per output rank)
-@pytest.mark.parametrize("k", [0, 1, 5, 6, 7, 8])
+# outputs (one block per output rank); 9 and 10 are dense systems whose rows
+# hold 114-176 edges (the loops for rows longer than 128 edges)
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("k", [0, 1, 5, 6, 7, 8, 9, 10])
 def test_full_parity(k):
     case = Case(k)
     nl = case.nbr()
@@ -63,11 +65,18 @@ def _sampled_check(case, nl, res, rows, atoms, edges):
     assert rel(res["forces"][atoms].cpu().numpy(), prob.forces_atoms(atoms)) < tol
 
 
-def _samples(case, n_rows, seed):
+def _spread(sorted_rows, k):
+    """k entries of a sorted sample, evenly spaced over it, so the checks
+    see every part of the row range (each XCD's share of the grid)."""
+    idx = np.unique(np.linspace(0, len(sorted_rows) - 1, k).round().astype(int))
+    return sorted_rows[idx]
+
+
+def _samples(case, n_rows, seed, n_edge_rows=16):
     rp, N = case.oracle_csr()[0], case.N
     rng = np.random.default_rng(seed)
     rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, n_rows, replace=False)]))
-    edges = np.concatenate([np.arange(rp[i], rp[i + 1]) for i in rows[:16]])
+    edges = np.concatenate([np.arange(rp[i], rp[i + 1]) for i in _spread(rows, n_edge_rows)])
     return rows, edges
 
 
@@ -75,7 +84,7 @@ def test_medium_parity_sampled():
     case = Case(3)
     nl = case.nbr()
     rows, edges = _samples(case, 96, 11)
-    atoms = np.unique(np.concatenate([np.arange(64), rows[:32]]))   # includes the 0-63 slice
+    atoms = np.unique(np.concatenate([np.arange(64), _spread(rows, 32)]))   # includes the 0-63 slice
     res = run_chunked(case, nl, chunks=1, keep_edges=edges)
     _sampled_check(case, nl, res, rows, atoms, edges)
 
@@ -86,7 +95,7 @@ def test_large_parity_sampled_chunked():
     nl = case.nbr()
     rows, edges = _samples(case, 40, 12)
     res = run_chunked(case, nl, chunks=3, keep_edges=edges)
-    _sampled_check(case, nl, res, rows, rows[:24], edges)
+    _sampled_check(case, nl, res, rows, _spread(rows, 24), edges)
 
 
 def test_chunked_equals_unchunked():
@@ -220,3 +229,29 @@ def test_empty_rows_and_zero_edges():
     W2 = ctx.virial(pos2, cell, nl2, t.empty((0, 3), dtype=ctx.dtype, device="cuda"))
     t.cuda.synchronize()
     assert float(W2.abs().max()) == 0.0
+
+
+def test_validation_refuses_unwrapped_positions_and_a_broken_reverse_index():
+    """With spec.validate, conv_fwd refuses positions outside the cell and
+    conv_bwd refuses a reverse index that does not pair every edge with its
+    reverse (the backward gathers sender gradients through that symmetry)."""
+    t = torch()
+    case = Case(0, validate=True)
+    nl = case.nbr()
+    out, eb = case.ctx.conv_fwd(case.pos, case.cell, nl, case.h, case.W, 1.0)
+    t.cuda.synchronize()
+    bad_pos = case.pos.clone()
+    bad_pos[3, 0] += float(case.cell[0, 0])            # one atom moved out by a cell vector
+    say("[gpu] conv_fwd with validate on unwrapped positions")
+    with pytest.raises(tpc.TpcError) as ei:
+        case.ctx.conv_fwd(bad_pos, case.cell, nl, case.h, case.W, 1.0)
+    assert ei.value.status == 4 and "wrapped" in ei.value.message
+    bad_rev = nl.rev.clone()
+    bad_rev[0], bad_rev[1] = nl.rev[1].item(), nl.rev[0].item()
+    bad_nl = tpc.NeighbourList(nl.row_ptr, nl.src, nl.shift, bad_rev, nl.n_edges)
+    say("[gpu] conv_bwd with validate on a broken reverse index")
+    with pytest.raises(tpc.TpcError) as ei:
+        case.ctx.conv_bwd(bad_nl, case.h, case.W, 1.0, case.G, eb)
+    assert ei.value.status == 4 and "reverse" in ei.value.message
+    dh, _, F, _ = case.ctx.conv_bwd(nl, case.h, case.W, 1.0, case.G, eb)
+    t.cuda.synchronize()

@@ -24,6 +24,9 @@ are not used here):
 * large  -- fcc at 0.085 sites/A^3 (a = 3.6103 A) on a 40x41x41 supercell,
             6,816 random vacancies (N = 262,144), Gaussian jitter
             sigma = 0.15 A, 89 species drawn Zipf(1.1), r_c = 6.0, float32.
+* dense  -- 1,024 atoms uniform at 0.286 atoms/A^3 (sequential rejection at
+            0.8 A), about 150 neighbours within r_c = 5.0 (rows longer than
+            128 edges), parity inputs only.
 
 Atoms of the small, medium and large systems are numbered along a Morton
 curve over 3 A bins (molecules kept whole), the order an MD engine keeps for
@@ -38,7 +41,7 @@ import math
 
 import numpy as np
 
-__all__ = ["CONFIGS", "config", "generate", "geometry", "values", "morton_order"]
+__all__ = ["CONFIGS", "config", "generate", "variant", "geometry", "values", "morton_order"]
 
 # Literal per-configuration data.  d_in = sum over node irreps of (2l+1),
 # d_sh = (sh_lmax+1)^2, d_out = sum over paths of (2 l3 + 1).
@@ -76,6 +79,16 @@ CONFIGS = {
             sh_lmax=3, out_lmax=3, r_cut=5.0, hidden=[64, 64], n_paths=17,
             d_in=9, d_sh=16, d_out=16, scale="one", seed=8, geometry="sc",
             sum_paths=True),
+    # Dense systems whose rows hold more than 128 edges (the long-row loops of
+    # the tensor-product kernels): 1,024 atoms at about 150 neighbours each,
+    # near the FlashCart microbenchmark shape (1,024 nodes, 128 neighbours,
+    # 128 channels, rank <= 3); parity inputs only.
+    9: dict(name="dense_c128", N=1024, dtype="float32", C=128, l1max=2,
+            sh_lmax=3, out_lmax=3, r_cut=5.0, hidden=[64, 64], n_paths=17,
+            d_in=9, d_sh=16, d_out=71, scale="one", seed=9, geometry="dense"),
+    10: dict(name="dense_c64_l3", N=1024, dtype="float32", C=64, l1max=3,
+             sh_lmax=3, out_lmax=3, r_cut=5.0, hidden=[32, 32, 32], n_paths=23,
+             d_in=16, d_sh=16, d_out=99, scale="one", seed=10, geometry="dense"),
 }
 
 N_BESSEL = 8
@@ -214,6 +227,14 @@ def _geometry_cached(k):
         pos = _wrap(g * a + rng.normal(0.0, 0.1, size=(N, 3)), box)
         pos = pos[morton_order(pos, box)]
         species = rng.integers(0, 10, size=N).astype(np.int32)
+    elif c["geometry"] == "dense":
+        # uniform at 0.286 atoms/A^3 (about 150 neighbours within 5 A), no
+        # pair closer than 0.8 A, numbered along the Morton curve
+        L = (N / 0.286) ** (1.0 / 3.0)
+        pos = _uniform_tiny(rng, N, L, 0.8)
+        box = np.array([L, L, L])
+        pos = pos[morton_order(pos, box, bin_size=2.0)]
+        species = rng.integers(0, 4, size=N).astype(np.int32)
     elif c["geometry"] == "water":
         L = (N / 0.1) ** (1.0 / 3.0)
         box = np.array([L, L, L])
@@ -259,6 +280,36 @@ def values(k, with_grad=True):
         W.append((rng.standard_normal((a, b)) / math.sqrt(a)).astype(dt))
     G = rng.standard_normal((N, c["d_out"], C), dtype=dt) if with_grad else None
     return h, W, G
+
+
+def variant(k, C, l1max, sh_lmax, out_lmax, hidden, dtype, seed, sum_paths=False):
+    """Configuration ``k``'s geometry with other feature shapes and widths
+    (every kernel instantiation gets a small parity case).  The path count
+    and widths are derived by the caller's layout; values are drawn from
+    ``default_rng(seed)``: h, W (layer order), G.  Returns the same dict as
+    ``generate``."""
+    from itertools import product
+    pos, cell, species = geometry(k)
+    n_paths = sum(1 for l1, l2, l3 in product(range(l1max + 1), range(sh_lmax + 1), range(out_lmax + 1))
+                  if abs(l1 - l2) <= l3 <= l1 + l2 and (l1 + l2 + l3) % 2 == 0)
+    l3s = sorted({l3 for l1, l2, l3 in product(range(l1max + 1), range(sh_lmax + 1), range(out_lmax + 1))
+                  if abs(l1 - l2) <= l3 <= l1 + l2 and (l1 + l2 + l3) % 2 == 0})
+    d_out = sum(2 * l3 + 1 for l3 in l3s) if sum_paths else sum(
+        2 * l3 + 1 for l1, l2, l3 in product(range(l1max + 1), range(sh_lmax + 1), range(out_lmax + 1))
+        if abs(l1 - l2) <= l3 <= l1 + l2 and (l1 + l2 + l3) % 2 == 0)
+    base = config(k)
+    c = dict(base, name=f"{base['name']}_v{seed}", C=C, l1max=l1max, sh_lmax=sh_lmax, out_lmax=out_lmax,
+             hidden=list(hidden), dtype=dtype, seed=seed, n_paths=n_paths, d_in=(l1max + 1) ** 2,
+             d_sh=(sh_lmax + 1) ** 2, d_out=d_out, sum_paths=sum_paths, scale="one")
+    c["layer_dims"] = [N_BESSEL] + list(hidden) + [n_paths * C]
+    rng = np.random.default_rng(seed)
+    dt = np.dtype(dtype)
+    N = len(pos)
+    h = rng.standard_normal((N, c["d_in"], C)).astype(dt)
+    W = [(rng.standard_normal((a, b)) / math.sqrt(a)).astype(dt)
+         for a, b in zip(c["layer_dims"][:-1], c["layer_dims"][1:])]
+    G = rng.standard_normal((N, d_out, C)).astype(dt)
+    return dict(cfg=c, pos=pos, cell=cell, species=species, h=h, W=W, G=G, r_cut=c["r_cut"])
 
 
 def generate(k, with_grad=True):
