@@ -225,6 +225,26 @@ tpc_status tpc_conv_fwd(const tpc_ctx* ctx, int64_t n_atoms, const double* pos,
                         const tpc_edge_buffers* eb, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* tpc_conv_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Its scratch (the radial weights in
+ * matrix-core operand order and a status word) lives in a fixed array of
+ * device memory inside the library, 16 MiB per GPU, held from the first call
+ * on that GPU until the process ends; the device address of each GPU's copy
+ * is looked up once per device.  The call allocates nothing.  Specs whose
+ * forward needs more scratch than the array holds (never for the built
+ * configurations at up to 128 channels) return TPC_ERR_UNSUPPORTED.  Every
+ * call on one GPU uses the same array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race on it and must be
+ * ordered by the caller.  Arguments, outputs and errors otherwise as for
+ * tpc_conv_fwd. */
+tpc_status tpc_conv_fwd_noalloc(const tpc_ctx* ctx, int64_t n_atoms, const double* pos,
+                                const double* cell, const int32_t* row_ptr, const int32_t* src,
+                                const int32_t* shift, int64_t row_begin, int64_t row_end,
+                                int64_t edge_begin, int64_t edge_end, const void* h,
+                                const void* const* weights, double scale, void* out,
+                                const tpc_edge_buffers* eb, void* stream);
+
 /* Backward of L = sum(G * out) for receivers [row_begin, row_end).
  *   n_edges   total edges of the list (g_edge, dh_edge and rev span all of them)
  *   rev       [n_edges] int32 from tpc_nbr_build

@@ -738,6 +738,30 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
   return TPC_OK;
 }
 
+tpc_status tpc_conv_fwd_noalloc(const tpc_ctx* c, int64_t n, const double* pos, const double* cell,
+                                const int32_t* row_ptr, const int32_t* src, const int32_t* shift,
+                                int64_t row_begin, int64_t row_end, int64_t edge_begin, int64_t edge_end,
+                                const void* h, const void* const* weights, double scale, void* out,
+                                const tpc_edge_buffers* eb, void* stream) {
+  Errors E;
+  if (!c) {
+    E.add(TPC_ERR_INVALID, "ctx must be non-null");
+    return E.finish();
+  }
+  void* scratch = nullptr;
+  size_t cap = 0;
+  const hipError_t e = tpc::scratch_for_current_device(&scratch, &cap);
+  if (e != hipSuccess) return device_error(e, "conv_fwd_noalloc: device scratch address");
+  const size_t need = fwd_layout(c).total;
+  if (need > cap) {
+    E.add(TPC_ERR_UNSUPPORTED, "this spec's forward needs %zu bytes of scratch; the fixed device scratch holds %zu",
+          need, cap);
+    return E.finish();
+  }
+  return tpc_conv_fwd(c, n, pos, cell, row_ptr, src, shift, row_begin, row_end, edge_begin, edge_end, h,
+                      weights, scale, out, eb, scratch, cap, stream);
+}
+
 tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int32_t* row_ptr,
                         const int32_t* src, const int32_t* rev, int64_t row_begin, int64_t row_end,
                         int64_t edge_begin, int64_t edge_end, const void* h,

@@ -151,6 +151,12 @@ inline int64_t virial_blocks(int64_t n) { return n > 0 ? (n + kVirialBlock - 1) 
 hipError_t launch_virial(int dtype, int64_t n, const GeomArgs& a, const void* g, double* part,
                          void* W, hipStream_t s);
 // rows [row_begin, row_end): order, ranges, and (rev non-null) symmetry
+// Fixed device scratch of the entry point that allocates nothing: its size,
+// and the device address of the current GPU's copy (looked up on first use
+// per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t scratch_for_current_device(void** ptr, size_t* bytes);
+
 hipError_t launch_csr_check(int64_t n, int64_t n_edges, const int32_t* row_ptr,
                             const int32_t* src, const int32_t* shift, const int32_t* rev,
                             int64_t row_begin, int64_t row_end, int64_t edge_begin,
