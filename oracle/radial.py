@@ -35,16 +35,29 @@ def bessel_dr(r, r_cut, n=N_BESSEL):
     return np.sqrt(2.0 / r_cut) * (k * np.cos(k * r) / r - np.sin(k * r) / (r * r))
 
 
-def envelope(x, p=P_ENVELOPE):
+def envelope_expanded(x, p=P_ENVELOPE):
+    """u(x) = 1 - (p+1)(p+2)/2 x^p + p(p+2) x^(p+1) - p(p+1)/2 x^(p+2)."""
     x = np.asarray(x, dtype=np.float64)
     return (1.0 - (p + 1) * (p + 2) / 2.0 * x ** p + p * (p + 2) * x ** (p + 1)
             - p * (p + 1) / 2.0 * x ** (p + 2))
 
 
-def envelope_dx(x, p=P_ENVELOPE):
+def envelope(x, p=P_ENVELOPE):
+    """The same polynomial in the form (1-x)^3 sum_{k<p} C(k+2, 2) x^k (for
+    p = 5: (1-x)^3 (1 + 3x + 6x^2 + 10x^3 + 15x^4)): u has a triple zero at
+    x = 1, and this form keeps its relative accuracy there, where the
+    expanded terms of size ~ p^2 cancel to a value of size (1-x)^3."""
     x = np.asarray(x, dtype=np.float64)
-    return (-(p + 1) * (p + 2) / 2.0 * p * x ** (p - 1) + p * (p + 2) * (p + 1) * x ** p
-            - p * (p + 1) / 2.0 * (p + 2) * x ** (p + 1))
+    q = np.zeros_like(x)
+    for k in range(p - 1, -1, -1):
+        q = q * x + (k + 2) * (k + 1) / 2.0
+    return (1.0 - x) ** 3 * q
+
+
+def envelope_dx(x, p=P_ENVELOPE):
+    """u'(x) = -p(p+1)(p+2)/2 x^(p-1) (1-x)^2."""
+    x = np.asarray(x, dtype=np.float64)
+    return -p * (p + 1) * (p + 2) / 2.0 * x ** (p - 1) * (1.0 - x) ** 2
 
 
 def edge_features(r, r_cut):

@@ -62,3 +62,27 @@ def test_mlp_input_gradient_by_differences():
         fp = (radial.mlp_forward(ef + d, W)[0] * dR).sum(1)
         fm = (radial.mlp_forward(ef - d, W)[0] * dR).sum(1)
         np.testing.assert_allclose(g[:, k], (fp - fm) / (2 * e), atol=1e-7)
+
+
+def test_envelope_factored_form_is_the_polynomial():
+    """The envelope in the form (1-x)^3 sum_{k<p} C(k+2,2) x^k equals the
+    polynomial 1 - (p+1)(p+2)/2 x^p + p(p+2) x^(p+1) - p(p+1)/2 x^(p+2) exactly
+    (rational arithmetic), its derivative is -p(p+1)(p+2)/2 x^(p-1) (1-x)^2,
+    and near x = 1 it keeps the relative accuracy the expanded sum loses."""
+    from fractions import Fraction
+    from math import comb
+    for p in (3, 5, 6):
+        for xq in (Fraction(0), Fraction(1, 3), Fraction(5, 7), Fraction(99, 100), Fraction(1)):
+            expanded = 1 - Fraction((p + 1) * (p + 2), 2) * xq ** p + p * (p + 2) * xq ** (p + 1) \
+                - Fraction(p * (p + 1), 2) * xq ** (p + 2)
+            factored = (1 - xq) ** 3 * sum(comb(k + 2, 2) * xq ** k for k in range(p))
+            assert expanded == factored
+            assert abs(radial.envelope(float(xq), p) - float(expanded)) <= 1e-15
+            dexp = -Fraction((p + 1) * (p + 2) * p, 2) * xq ** (p - 1) + p * (p + 2) * (p + 1) * xq ** p \
+                - Fraction(p * (p + 1) * (p + 2), 2) * xq ** (p + 1)
+            assert abs(radial.envelope_dx(float(xq), p) - float(dexp)) <= 1e-13
+    # relative accuracy near the cutoff: exact value from rationals
+    x = 1 - 2.0 ** -20
+    exact = float((1 - Fraction(x)) ** 3 * sum(comb(k + 2, 2) * Fraction(x) ** k for k in range(5)))
+    assert abs(radial.envelope(x) - exact) <= 1e-14 * abs(exact)
+    assert abs(radial.envelope_expanded(x) - exact) > 0.5 * abs(exact)   # all relative accuracy lost
