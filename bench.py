@@ -48,6 +48,8 @@ KERNEL_SOURCES = {
     "radial_bwd_mlp": ["radial.hip"],
     "geom_fwd": ["geom.hip"],
     "geom_bwd": ["geom.hip"],
+    "table_fwd": ["radial_table.hip"],
+    "table_bwd": ["radial_table.hip"],
 }
 
 
@@ -61,6 +63,8 @@ KERNEL_SYMBOLS = {
     "radial_bwd_mlp": "k_radial_bwd_mlp<",
     "geom_fwd": "k_geom_fwd<",
     "geom_bwd": "k_geom_bwd<",
+    "table_fwd": "k_table_fwd<",
+    "table_bwd": "k_table_bwd<",
 }
 COPY_PROBE_BYTES = 1 << 30   # one plain device-to-device copy of this size calibrates the counters
 
@@ -103,6 +107,12 @@ def algorithmic(kernel, N, E, cfg, ctx):
     if kernel == "radial_bwd_dA":
         # reads dR, writes dA (H per edge)
         return E * (T * PC + T * H), E * 2 * H * PC
+    if kernel == "table_fwd":
+        # reads the edge length, writes R (the coefficients are cache traffic)
+        return E * (T + T * PC), E * PC * 2 * 2 * (cfg.get("_table_degree", 8) + 1)
+    if kernel == "table_bwd":
+        # reads the edge length and dR, writes dL/dr
+        return E * (2 * T + T * PC), E * PC * 2 * 2 * cfg.get("_table_degree", 8)
     if kernel == "radial_bwd_mlp":
         # reads ef and dA, writes d(ef); recomputes the hidden layers
         return E * (8 * T + T * H + 8 * T), E * 2 * hidden
@@ -181,10 +191,13 @@ def measured_traffic(kernel, workload):
 
 
 def _counter_rows(directory):
-    """(kernel name, dispatch id, counter, value) from every rocprofv3
-    counter_collection.csv under ``directory``."""
+    """(kernel name, dispatch id, counter, value) from every rocprofv3 counter
+    output under ``directory``: counter_collection.csv files, or the SQLite
+    databases (*_results.db, view counters_collection) that rocprofv3 writes
+    by default."""
     import csv
     import glob
+    import sqlite3
     rows = []
     for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
         with open(path, newline="") as f:
@@ -192,7 +205,65 @@ def _counter_rows(directory):
                 k = {key.lower(): v for key, v in r.items()}
                 rows.append((k.get("kernel_name", ""), k.get("dispatch_id", ""), k.get("counter_name", ""),
                              float(k.get("counter_value", "nan"))))
+    for path in glob.glob(os.path.join(directory, "**", "*_results.db"), recursive=True):
+        db = sqlite3.connect(path)
+        try:
+            rows += [(n, str(d), c, float(v)) for n, d, c, v in db.execute(
+                "select kernel_name, dispatch_id, counter_name, value from counters_collection")]
+        finally:
+            db.close()
     return rows
+
+
+def _kernel_rows(directory):
+    """(kernel name, duration ns) of every dispatch in the rocprofv3 kernel
+    traces (SQLite databases) under ``directory``."""
+    import glob
+    import sqlite3
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*_results.db"), recursive=True):
+        db = sqlite3.connect(path)
+        try:
+            rows += [(n, float(d)) for n, d in db.execute("select name, duration from kernels")]
+        finally:
+            db.close()
+    return rows
+
+
+def _short_name(name):
+    import re
+    m = re.match(r"(?:void )?(?:tpc::)?(?:\(anonymous namespace\)::)?(\w+)(<[^(]*>)?", name)
+    return (m.group(1) + (m.group(2) or "")) if m else name
+
+
+def profile_summary(directory, counter_dirs=()):
+    """Markdown tables: per-kernel dispatch count, mean and total duration of
+    a rocprofv3 --kernel-trace run, and per-kernel mean counters of --pmc
+    runs (one folder each)."""
+    stats = {}
+    for n, d in _kernel_rows(directory):
+        c = stats.setdefault(_short_name(n), [0, 0.0])
+        c[0] += 1
+        c[1] += d
+    lines = ["| kernel | dispatches | mean (ms) | total (ms) |", "|---|---|---|---|"]
+    for k, (c, t) in sorted(stats.items(), key=lambda kv: -kv[1][1]):
+        if t < 1e5:
+            continue
+        lines.append(f"| `{k}` | {c} | {t / c / 1e6:.3f} | {t / 1e6:.2f} |")
+    for d in counter_dirs:
+        per = {}
+        for n, did, cname, v in _counter_rows(d):
+            per.setdefault(_short_name(n), {}).setdefault(cname, {})[did] = v
+        names = sorted({c for k in per.values() for c in k})
+        lines += ["", "| kernel | " + " | ".join(names) + " |", "|---" * (len(names) + 1) + "|"]
+        rank = lambda kv: -max(sum(x.values()) / len(x) for x in kv[1].values())
+        for k, cs in sorted(per.items(), key=rank):
+            vals = [sum(cs[c].values()) / len(cs[c]) if c in cs else float("nan") for c in names]
+            if max(vals) < 1e6:
+                continue
+            lines.append(f"| `{k}` | " + " | ".join(f"{v:.4g}" for v in vals) + " |")
+    print("\n".join(lines))
+    return 0
 
 
 def _per_dispatch(rows, counter):
@@ -315,6 +386,10 @@ def main(argv=None):
                     help="skip the separately timed virial and double backward")
     ap.add_argument("--sum-paths", action="store_true",
                     help="path-summed outputs (one block per output rank) on the same system")
+    ap.add_argument("--radial-table", default=None, metavar="PIECES,DEGREE",
+                    help="radial weights from certified piecewise Chebyshev tables (fitted before timing)")
+    ap.add_argument("--fp32-mfma-only", action="store_true",
+                    help="float32 radial products on float32 matrix cores only (no bf16 split)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, copy %d bytes device to device three times "
@@ -322,7 +397,12 @@ def main(argv=None):
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc output "
                          "folders and exit")
+    ap.add_argument("--profile-summary", nargs="+", metavar="DIR",
+                    help="print markdown tables of a rocprofv3 kernel trace (first folder) and the "
+                         "mean counters of --pmc runs (further folders), then exit")
     a = ap.parse_args(argv)
+    if a.profile_summary:
+        return profile_summary(a.profile_summary[0], a.profile_summary[1:])
     if a.traffic_from:
         return traffic_from(a.traffic_from[0], a.traffic_from[1], traffic_path(a.workload))
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -350,11 +430,23 @@ def main(argv=None):
     cpu = None if a.no_cpu_baseline else cpu_baseline(
         d, a.cpu_budget, sample_rows=8192 if a.workload == "large" else None)
     dev = "cuda"
-    ctx = tpc.Context(tpc.spec_for(cfg))
+    table = tuple(int(v) for v in a.radial_table.split(",")) if a.radial_table else None
+    if table:
+        cfg = dict(cfg, _table_degree=table[1])
+    ctx = tpc.Context(tpc.spec_for(cfg, fp32_mfma_only=a.fp32_mfma_only, table=table))
     pos = torch.from_numpy(d["pos"]).to(dev)
     species = torch.from_numpy(d["species"]).to(dev)
     h = torch.from_numpy(d["h"]).to(dev)
     W = [torch.from_numpy(w).to(dev) for w in d["W"]]
+    table_info = None
+    if table:
+        torch.cuda.synchronize()
+        t_fit = time.perf_counter()
+        tab, cert = ctx.radial_table_fit(W)
+        torch.cuda.synchronize()
+        table_info = {"pieces": table[0], "degree": table[1], "certificate": list(cert),
+                      "fit_s": time.perf_counter() - t_fit, "table_bytes": ctx.sizes["table_bytes"]}
+        W = [tab]
     G = torch.from_numpy(d["G"]).to(dev)
     cell = d["cell"]
     N = cfg["N"]
@@ -427,15 +519,16 @@ def main(argv=None):
         vt = tpc.timing_collect()
         extras["virial_ms"] = vt["virial"][0] / vt["virial"][1] if "virial" in vt else None
         del ws_v
-        if chunks == 1 and not cfg.get("sum_paths"):
+        if chunks == 1 and not cfg.get("sum_paths") and not table:
             extras["double_backward"] = time_double_backward(tpc, ctx, nl, h, G, eb, scale, N, E, cfg, a.steps)
 
     # one launch of each per pass (the weight packing runs once in each pass)
     fwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0)
-                 for n in ("geom_fwd", "radial_fwd", "tp_fwd")) + \
+                 for n in ("geom_fwd", "radial_fwd", "table_fwd", "tp_fwd")) + \
         per_kernel.get("radial_pack", {}).get("ms_per_step", 0.0) / 2
     bwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0)
-                 for n in ("tp_bwd_edge", "radial_bwd_dA", "radial_bwd_mlp", "geom_bwd", "dh_gather", "forces")) + \
+                 for n in ("tp_bwd_edge", "radial_bwd_dA", "radial_bwd_mlp", "table_bwd", "geom_bwd", "dh_gather",
+                           "forces")) + \
         per_kernel.get("radial_pack", {}).get("ms_per_step", 0.0) / 2
     nbr_ms = sum(v["ms_per_step"] for n, v in per_kernel.items() if n.startswith("nbr"))
     dominant = max((n for n in per_kernel if n in KERNEL_SOURCES), key=lambda n: per_kernel[n]["ms_per_step"])
@@ -476,7 +569,9 @@ def main(argv=None):
                                f"mlp={'-'.join(map(str, cfg['layer_dims']))}: "
                                "nbr_build + conv_fwd + conv_bwd (forces)"
                                + (f" in {len(bounds)} receiver chunks" if len(bounds) > 1 else "")
-                               + (", path-summed outputs" if cfg.get("sum_paths") else ""),
+                               + (", path-summed outputs" if cfg.get("sum_paths") else "")
+                               + (f", radial tables {table[0]}x{table[1]}" if table else "")
+                               + (", float32 radial products on fp32 matrix cores" if a.fp32_mfma_only else ""),
                    "n_atoms": N, "n_edges": E, "channels": cfg["C"], "paths": ctx.n_paths,
                    "chunks": len(bounds), "parallelism": "single GPU"},
         "roofline": roof,
@@ -485,6 +580,7 @@ def main(argv=None):
         "fwd_bwd_edges_per_s": E / ((fwd_ms + bwd_ms) * 1e-3) if fwd_ms else None,
         "nbr_build_ms": nbr_ms,
         **extras,
+        **({"radial_table": table_info} if table_info else {}),
         "kernels": kernels,
         "tp_groups_hbm": group_rooflines(per_kernel, N, E, cfg, ctx),
         "wall_s": wall,

@@ -79,7 +79,8 @@ typedef enum tpc_status {
 } tpc_status;
 
 enum { TPC_F32 = 0, TPC_F64 = 1 };
-enum { TPC_OP_NBR = 0, TPC_OP_FWD = 1, TPC_OP_BWD = 2, TPC_OP_VIRIAL = 3, TPC_OP_DOUBLE_BWD = 4 };
+enum { TPC_OP_NBR = 0, TPC_OP_FWD = 1, TPC_OP_BWD = 2, TPC_OP_VIRIAL = 3, TPC_OP_DOUBLE_BWD = 4,
+       TPC_OP_TABLE_FIT = 5 };
 
 #define TPC_MAX_LAYERS 8
 #define TPC_MAX_PATHS 32
@@ -121,6 +122,15 @@ typedef struct tpc_spec {
                                 option of the FastMACE page "Rewrites and
                                 precision options").  Nonzero: every float32
                                 product on float32 matrix cores. */
+  int radial_table_pieces;   /* 0 (default): radial weights from the radial
+                                network.  n > 0: from piecewise Chebyshev
+                                tables of n equal pieces on [0, r_cut]
+                                (FastMACE "Rewrites and precision options",
+                                "Radial network", radial_tables), fitted and
+                                certified by tpc_radial_table_fit; the
+                                convolution calls then take one weights
+                                pointer, the table */
+  int radial_table_degree;   /* polynomial degree per piece, 1..16 */
 } tpc_spec;
 
 typedef struct tpc_info {
@@ -142,6 +152,7 @@ typedef struct tpc_info {
   int dY_parts;              /* partial dY slices the backward keeps per edge */
   size_t dh_edge_bytes;      /* per edge: one row of the dh_edge buffer of
                                 tpc_conv_bwd */
+  size_t table_bytes;        /* the radial table (0 without one) */
 } tpc_info;
 
 /* Per-edge buffers.  conv_fwd writes them for the edges of the rows it
@@ -315,6 +326,43 @@ tpc_status tpc_conv_double_bwd(const tpc_ctx* ctx, int64_t n_atoms, int64_t n_ed
                                const tpc_edge_buffers* eb, const void* u_dh, const void* u_dY,
                                const void* u_dR, void* g_hat, void* h_hat, void* Y_hat, void* R_hat,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fit and certify the piecewise Chebyshev radial table of a context with
+ * spec.radial_table_pieces > 0 (FastMACE page "Rewrites and precision
+ * options", section "Radial network", radial_tables: the radial chain is
+ * replaced by per-piece Chebyshev tables fitted when the plan is built; the
+ * "certified" class of the rewrite classes: the table's error, measured
+ * against a float64 evaluation of the same weights, must not exceed the
+ * rounding error of the computation it replaces, for values and first
+ * derivatives).  The radial weights here depend on the edge length only, so
+ * one table serves every species pair.
+ *   weights      n_layers device pointers of the radial network (as for
+ *                tpc_conv_fwd without a table)
+ *   table        device, out: [pieces][2 degree + 1][P*C] in the context
+ *                dtype: degree + 1 rows of Chebyshev coefficients of R(r) on
+ *                each piece, then degree rows of its r-derivative series
+ *   certificate  host double[2], out: over the pieces and columns, the
+ *                largest ratio of the table's largest error on a piece
+ *                (evaluated as the convolution evaluates it) to the largest
+ *                float rounding scale of the replaced computation on that
+ *                piece, for values and for r-derivatives; each piece is
+ *                checked at 8 points (its start and points between its
+ *                interpolation nodes)
+ *   workspace    tpc_workspace_query(TPC_OP_TABLE_FIT)
+ * The rounding scale at a point is H eps sum_k |a_k W_kc| + eps |r R'| for
+ * values and H eps sum_k |a'_k W_kc| + eps |R'| for derivatives (a the last
+ * hidden activations, H their count, eps the unit roundoff of the dtype):
+ * the last layer's dot product and the rounding of the distance it is given.
+ * Both are taken as maxima over the piece (the range the table serves)
+ * because the weights and their scale vanish together at points (the
+ * derivative at r = 0, the envelope's triple zero at r_cut) where no float
+ * table's absolute rounding follows the network's relative accuracy.
+ * Waits for the certificate.  Returns TPC_OK when both ratios are at most 1,
+ * TPC_ERR_PRECONDITION otherwise (the table is written but must not be used;
+ * keep the radial network). */
+tpc_status tpc_radial_table_fit(const tpc_ctx* ctx, const void* const* weights, void* table,
+                                size_t table_bytes, double* certificate, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Virial of L: W[a][b] = dL/d(eps_ab) for a homogeneous strain
  * x -> (I + eps) x applied to the positions and the cell rows together.  This

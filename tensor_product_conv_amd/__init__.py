@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpconv.s
 
 TPC_MAX_LAYERS = 8
 TPC_MAX_PATHS = 32
-OP_NBR, OP_FWD, OP_BWD, OP_VIRIAL, OP_DOUBLE_BWD = 0, 1, 2, 3, 4
+OP_NBR, OP_FWD, OP_BWD, OP_VIRIAL, OP_DOUBLE_BWD, OP_TABLE_FIT = 0, 1, 2, 3, 4, 5
 STATUS = {0: "ok", 1: "invalid", 2: "unsupported", 3: "capacity", 4: "precondition",
           5: "workspace", 6: "device"}
 
@@ -45,7 +45,8 @@ class _Spec(ctypes.Structure):
                 ("sh_lmax", ctypes.c_int), ("out_lmax", ctypes.c_int), ("n_bessel", ctypes.c_int),
                 ("poly_p", ctypes.c_int), ("n_species", ctypes.c_int), ("r_cut", ctypes.c_double),
                 ("n_layers", ctypes.c_int), ("layer_dims", ctypes.c_int * (TPC_MAX_LAYERS + 1)),
-                ("validate", ctypes.c_int), ("sum_paths", ctypes.c_int), ("fp32_mfma_only", ctypes.c_int)]
+                ("validate", ctypes.c_int), ("sum_paths", ctypes.c_int), ("fp32_mfma_only", ctypes.c_int),
+                ("radial_table_pieces", ctypes.c_int), ("radial_table_degree", ctypes.c_int)]
 
 
 class _Info(ctypes.Structure):
@@ -55,7 +56,7 @@ class _Info(ctypes.Structure):
                 ("edge_buffer_bytes", ctypes.c_size_t), ("dR_bytes", ctypes.c_size_t),
                 ("fwd_workspace_bytes", ctypes.c_size_t), ("bwd_workspace_bytes_fixed", ctypes.c_size_t),
                 ("bwd_workspace_bytes_per_edge", ctypes.c_size_t), ("dY_parts", ctypes.c_int),
-                ("dh_edge_bytes", ctypes.c_size_t)]
+                ("dh_edge_bytes", ctypes.c_size_t), ("table_bytes", ctypes.c_size_t)]
 
 
 class _KernelTime(ctypes.Structure):
@@ -102,6 +103,8 @@ def library():
                                         _VP, _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP]
     lib.tpc_virial.argtypes = [_VP, _I64, _I64, _VP, ctypes.POINTER(ctypes.c_double), _VP, _VP, _VP,
                                _VP, _VP, _VP, ctypes.c_size_t, _VP]
+    lib.tpc_radial_table_fit.argtypes = [_VP, ctypes.POINTER(_VP), _VP, ctypes.c_size_t,
+                                         ctypes.POINTER(ctypes.c_double), _VP, ctypes.c_size_t, _VP]
     lib.tpc_timing_enable.argtypes = [ctypes.c_int]
     lib.tpc_timing_collect.argtypes = [ctypes.POINTER(_KernelTime), ctypes.c_int,
                                        ctypes.POINTER(ctypes.c_int)]
@@ -111,7 +114,7 @@ def library():
     lib.tpc_last_error.restype = ctypes.c_char_p
     for name in ("tpc_ctx_create", "tpc_ctx_info", "tpc_cg_table", "tpc_workspace_query",
                  "tpc_nbr_build", "tpc_conv_fwd", "tpc_conv_bwd", "tpc_conv_double_bwd", "tpc_virial",
-                 "tpc_timing_enable", "tpc_timing_collect"):
+                 "tpc_radial_table_fit", "tpc_timing_enable", "tpc_timing_collect"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -171,6 +174,8 @@ class Spec:
     validate: bool = False
     sum_paths: bool = False
     fp32_mfma_only: bool = False
+    radial_table_pieces: int = 0
+    radial_table_degree: int = 0
 
     def to_c(self):
         s = _Spec()
@@ -185,6 +190,8 @@ class Spec:
         s.validate = int(bool(self.validate))
         s.sum_paths = int(bool(self.sum_paths))
         s.fp32_mfma_only = int(bool(self.fp32_mfma_only))
+        s.radial_table_pieces = int(self.radial_table_pieces)
+        s.radial_table_degree = int(self.radial_table_degree)
         return s
 
 
@@ -228,7 +235,7 @@ class Context:
         self.paths = [tuple(info.paths[p]) for p in range(info.n_paths)]
         self.sizes = {k: getattr(info, k) for k in (
             "edge_buffer_bytes", "dR_bytes", "fwd_workspace_bytes", "bwd_workspace_bytes_fixed",
-            "bwd_workspace_bytes_per_edge", "dY_parts", "dh_edge_bytes")}
+            "bwd_workspace_bytes_per_edge", "dY_parts", "dh_edge_bytes", "table_bytes")}
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -363,6 +370,27 @@ class Context:
                                       _ptr(ws), ws.numel(), _stream()))
         return dh, dR, forces, g_edge
 
+    # ---- radial tables ------------------------------------------------------------
+    def radial_table_fit(self, W, table=None, workspace=None, check=True):
+        """Fit and certify the piecewise Chebyshev table of R(r) from the
+        radial network's weights W (a context with radial_table_pieces > 0).
+        Returns (table, certificate ratios (values, derivatives)); with
+        ``check`` an uncertified table raises TpcError (status precondition).
+        The convolution calls of this context then take [table] as weights."""
+        t = _torch()
+        dev = W[0].device
+        nbytes = self.sizes["table_bytes"]
+        if table is None:
+            table = t.empty(nbytes // (8 if self.spec.dtype == "float64" else 4), dtype=self.dtype, device=dev)
+        ws = workspace if workspace is not None else self._workspace(self.workspace_bytes(OP_TABLE_FIT), dev)
+        wp = (_VP * len(W))(*[w.data_ptr() for w in W])
+        cert = (ctypes.c_double * 2)()
+        st = library().tpc_radial_table_fit(self._h, wp, _ptr(table), table.numel() * table.element_size(), cert,
+                                            _ptr(ws), ws.numel(), _stream())
+        if st != 0 and (check or st != 4):
+            _check(st)
+        return table, (cert[0], cert[1])
+
     # ---- VJP-of-VJP -------------------------------------------------------------
     def conv_double_bwd(self, nl: NeighbourList, h, scale, G, eb: EdgeBuffers, u_dh, u_dY, u_dR,
                         g_hat=None, h_hat=None, Y_hat=None, R_hat=None, workspace=None):
@@ -429,9 +457,11 @@ def conv_bwd(ctx: Context, *a, **k):
     return ctx.conv_bwd(*a, **k)
 
 
-def spec_for(cfg, validate=False, fp32_mfma_only=False):
-    """Spec of a workload configuration dict (see ``workloads.config``)."""
+def spec_for(cfg, validate=False, fp32_mfma_only=False, table=None):
+    """Spec of a workload configuration dict (see ``workloads.config``);
+    ``table`` = (pieces, degree) selects the radial tables."""
     return Spec(channels=cfg["C"], node_lmax=cfg["l1max"], sh_lmax=cfg["sh_lmax"],
                 out_lmax=cfg["out_lmax"], r_cut=cfg["r_cut"], layer_dims=list(cfg["layer_dims"]),
                 dtype=cfg["dtype"], validate=validate, sum_paths=bool(cfg.get("sum_paths", False)),
-                fp32_mfma_only=fp32_mfma_only)
+                fp32_mfma_only=fp32_mfma_only,
+                radial_table_pieces=table[0] if table else 0, radial_table_degree=table[1] if table else 0)

@@ -26,6 +26,7 @@ struct tpc_ctx {
   int hidden;    // hidden width H
   int n_hidden;  // number of hidden layers
   size_t tsize;  // bytes per feature value
+  bool table;    // radial weights from a piecewise Chebyshev table
 };
 
 namespace {
@@ -217,9 +218,31 @@ FwdWs fwd_layout(const tpc_ctx* c) {
   w.status = off;
   off += align_up(sizeof(int32_t) * 8);
   w.pack = off;
-  off += align_up(c->tsize * (size_t)pack_layout(c).total);
+  if (!c->table) off += align_up(c->tsize * (size_t)pack_layout(c).total);
   w.total = off;
   return w;
+}
+
+struct TableWs {
+  size_t nodes, cert, total;
+};
+
+TableWs table_layout(const tpc_ctx* c) {
+  TableWs w{};
+  const int pieces = c->spec.radial_table_pieces, n = c->spec.radial_table_degree + 1;
+  size_t off = 0;
+  w.nodes = off;
+  off += align_up(sizeof(double) * (size_t)pieces * n * c->tab.np * c->spec.channels);
+  w.cert = off;
+  off += align_up(sizeof(double) * 2 * (size_t)pieces);
+  w.total = off;
+  return w;
+}
+
+size_t table_bytes(const tpc_ctx* c) {
+  if (!c->table) return 0;
+  return c->tsize * (size_t)tpc::table_elems(c->spec.radial_table_pieces, c->spec.radial_table_degree,
+                                             c->tab.np * c->spec.channels);
 }
 
 struct VirialWs {
@@ -251,9 +274,9 @@ BwdWs bwd_layout(const tpc_ctx* c, int64_t ne) {
   w.status = off;
   off += align_up(sizeof(int32_t) * 8);
   w.pack = off;
-  off += align_up(T * (size_t)pack_layout(c).total);
+  if (!c->table) off += align_up(T * (size_t)pack_layout(c).total);
   w.dA = off;
-  off += align_up(T * (size_t)tpc::radial_dA_elems(c->hidden, ne));
+  if (!c->table) off += align_up(T * (size_t)tpc::radial_dA_elems(c->hidden, ne));
   w.total_without_dR = off;
   w.dR = off;
   off += align_up(T * (size_t)ne * c->tab.np * c->spec.channels);
@@ -383,6 +406,10 @@ tpc_status tpc_ctx_create(const tpc_spec* spec, tpc_ctx** out) {
     if (lok && tab.np > 0 && s.layer_dims[s.n_layers] != tab.np * s.channels)
       E.add(TPC_ERR_INVALID, "layer_dims[n_layers] must equal paths*channels = %d", tab.np * s.channels);
   }
+  if (s.radial_table_pieces < 0 || s.radial_table_pieces > 4096)
+    E.add(TPC_ERR_INVALID, "radial_table_pieces must be 0 (radial network) or 1..4096");
+  if (s.radial_table_pieces > 0 && (s.radial_table_degree < 1 || s.radial_table_degree > tpc::kTableMaxDegree))
+    E.add(TPC_ERR_INVALID, "radial_table_degree must be 1..%d", tpc::kTableMaxDegree);
   if (lok && s.channels >= 1 && (s.dtype == TPC_F32 || s.dtype == TPC_F64) &&
       !tpc::tp_supported(s.dtype, s.node_lmax, s.sh_lmax, s.out_lmax, s.channels))
     E.add(TPC_ERR_UNSUPPORTED,
@@ -398,6 +425,7 @@ tpc_status tpc_ctx_create(const tpc_spec* spec, tpc_ctx** out) {
   c->hidden = H;
   c->n_hidden = NH;
   c->tsize = s.dtype == TPC_F64 ? 8 : 4;
+  c->table = s.radial_table_pieces > 0;
   *out = c;
   return TPC_OK;
 }
@@ -422,10 +450,12 @@ tpc_status tpc_ctx_info(const tpc_ctx* c, tpc_info* info) {
   info->dR_bytes = T * (size_t)c->tab.np * c->spec.channels;
   info->fwd_workspace_bytes = fwd_layout(c).total;
   info->bwd_workspace_bytes_per_edge =
-      T * (size_t)(c->tab.dsh * dy_parts(c) + 8 + c->hidden) + T * (size_t)c->tab.np * c->spec.channels;
+      T * (size_t)(c->tab.dsh * dy_parts(c) + 8 + (c->table ? 0 : c->hidden)) +
+      T * (size_t)c->tab.np * c->spec.channels;
   info->bwd_workspace_bytes_fixed = bwd_layout(c, 0).total;
   info->dY_parts = dy_parts(c);
   info->dh_edge_bytes = T * (size_t)c->tab.din * c->spec.channels;
+  info->table_bytes = table_bytes(c);
   for (int p = 0; p < c->tab.np; ++p) {
     info->paths[p][0] = c->tab.path[p].l1;
     info->paths[p][1] = c->tab.path[p].l2;
@@ -483,6 +513,9 @@ tpc_status tpc_workspace_query(const tpc_ctx* c, int op, int64_t n_atoms, int64_
     *bytes = virial_layout(n_atoms).total;
   } else if (op == TPC_OP_DOUBLE_BWD) {
     *bytes = dbl_layout(c, n_edges).total;
+  } else if (op == TPC_OP_TABLE_FIT) {
+    if (!c->table) E.add(TPC_ERR_INVALID, "the context has no radial table (radial_table_pieces = 0)");
+    else *bytes = table_layout(c).total;
   } else {
     E.add(TPC_ERR_INVALID, "unknown op %d", op);
   }
@@ -602,6 +635,18 @@ void check_chunk(const tpc_ctx* c, int64_t n, int64_t row_begin, int64_t row_end
   (void)c;
 }
 
+// The radial weights: n_layers matrices, or with a table context one
+// pointer to the table written by tpc_radial_table_fit.
+void check_weights(const tpc_ctx* c, const void* const* weights, Errors& E) {
+  if (!weights) {
+    E.add(TPC_ERR_INVALID, "weights must be non-null");
+    return;
+  }
+  const int n = c->table ? 1 : c->spec.n_layers;
+  for (int k = 0; k < n; ++k)
+    if (!weights[k]) E.add(TPC_ERR_INVALID, "weights[%d] must be non-null", k);
+}
+
 void need_ptr(const void* p, const char* name, size_t align, Errors& E) {
   if (!p)
     E.add(TPC_ERR_INVALID, "%s must be non-null", name);
@@ -665,12 +710,7 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
     need_ptr(eb->rv, "eb.rv", va, E);
     need_ptr(eb->R, "eb.R", va, E);
   }
-  if (!weights) {
-    E.add(TPC_ERR_INVALID, "weights must be non-null");
-  } else {
-    for (int k = 0; k < c->spec.n_layers; ++k)
-      if (!weights[k]) E.add(TPC_ERR_INVALID, "weights[%d] must be non-null", k);
-  }
+  check_weights(c, weights, E);
   const FwdWs FL = fwd_layout(c);
   if (edge_end > edge_begin || c->spec.validate) {
     if (!ws) E.add(TPC_ERR_INVALID, "workspace must be non-null");
@@ -711,12 +751,19 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
   if (ne > 0) {
     TPC_LAUNCH("geom_fwd", s, tpc::launch_geom_fwd(dt, c->spec.sh_lmax, ga, eb->Y, eb->ef, eb->rv, s),
                "conv_fwd: geometry");
-    const tpc::RadialPack PL = pack_layout(c);
-    void* pk = static_cast<char*>(ws) + FL.pack;
-    TPC_LAUNCH("radial_pack", s, tpc::launch_radial_pack(dt, PL, weights, pk, s),
-               "conv_fwd: radial weight packing");
-    TPC_LAUNCH("radial_fwd", s, tpc::launch_radial_fwd(dt, PL, ne, eb->ef, pk, eb->R, s),
-               "conv_fwd: radial MLP");
+    if (c->table) {
+      TPC_LAUNCH("table_fwd", s,
+                 tpc::launch_table_fwd(dt, ne, c->tab.np * c->spec.channels, c->spec.radial_table_pieces,
+                                       c->spec.radial_table_degree, c->spec.r_cut, eb->rv, weights[0], eb->R, s),
+                 "conv_fwd: radial table");
+    } else {
+      const tpc::RadialPack PL = pack_layout(c);
+      void* pk = static_cast<char*>(ws) + FL.pack;
+      TPC_LAUNCH("radial_pack", s, tpc::launch_radial_pack(dt, PL, weights, pk, s),
+                 "conv_fwd: radial weight packing");
+      TPC_LAUNCH("radial_fwd", s, tpc::launch_radial_fwd(dt, PL, ne, eb->ef, pk, eb->R, s),
+                 "conv_fwd: radial MLP");
+    }
   }
   tpc::TPArgs ta{};
   ta.row_ptr = row_ptr;
@@ -804,12 +851,7 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
     need_ptr(eb->rv, "eb.rv", va, E);
     need_ptr(eb->R, "eb.R", va, E);
   }
-  if (!weights) {
-    E.add(TPC_ERR_INVALID, "weights must be non-null");
-  } else {
-    for (int k = 0; k < c->spec.n_layers; ++k)
-      if (!weights[k]) E.add(TPC_ERR_INVALID, "weights[%d] must be non-null", k);
-  }
+  check_weights(c, weights, E);
   const int64_t ne = edge_end - edge_begin;
   const BwdWs L = bwd_layout(c, ne > 0 ? ne : 0);
   const size_t need = dR ? L.total_without_dR : L.total;
@@ -852,19 +894,32 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
   ta.dh_edge = dh_edge;
   if (ne > 0) {
     TPC_LAUNCH("tp_bwd_edge", s, tpc::launch_tp_bwd(dt, L1, L2, L3, ta, s), "conv_bwd: tensor product (edges)");
-    const tpc::RadialPack PL = pack_layout(c);
-    void* pk = w + L.pack;
-    void* dA = w + L.dA;
-    TPC_LAUNCH("radial_pack", s, tpc::launch_radial_pack(dt, PL, weights, pk, s),
-               "conv_bwd: radial weight packing");
-    TPC_LAUNCH("radial_bwd_dA", s, tpc::launch_radial_bwd_dA(dt, PL, ne, dRp, pk, dA, s),
-               "conv_bwd: radial last layer");
-    TPC_LAUNCH("radial_bwd_mlp", s, tpc::launch_radial_bwd_mlp(dt, PL, ne, eb->ef, dA, pk, d_ef, s),
-               "conv_bwd: radial hidden layers");
-    TPC_LAUNCH("geom_bwd", s,
-               tpc::launch_geom_bwd(dt, L2, ne, edge_begin, c->spec.r_cut, eb->rv, dY, dy_parts(c),
-                                    d_ef, g_edge, s),
-               "conv_bwd: geometry");
+    if (c->table) {
+      // dL/dr from the table's derivative series, into the d_ef region
+      TPC_LAUNCH("table_bwd", s,
+                 tpc::launch_table_bwd(dt, ne, c->tab.np * c->spec.channels, c->spec.radial_table_pieces,
+                                       c->spec.radial_table_degree, c->spec.r_cut, eb->rv, weights[0], dRp,
+                                       d_ef, s),
+                 "conv_bwd: radial table");
+      TPC_LAUNCH("geom_bwd", s,
+                 tpc::launch_geom_bwd(dt, L2, ne, edge_begin, c->spec.r_cut, eb->rv, dY, dy_parts(c), nullptr,
+                                      d_ef, g_edge, s),
+                 "conv_bwd: geometry");
+    } else {
+      const tpc::RadialPack PL = pack_layout(c);
+      void* pk = w + L.pack;
+      void* dA = w + L.dA;
+      TPC_LAUNCH("radial_pack", s, tpc::launch_radial_pack(dt, PL, weights, pk, s),
+                 "conv_bwd: radial weight packing");
+      TPC_LAUNCH("radial_bwd_dA", s, tpc::launch_radial_bwd_dA(dt, PL, ne, dRp, pk, dA, s),
+                 "conv_bwd: radial last layer");
+      TPC_LAUNCH("radial_bwd_mlp", s, tpc::launch_radial_bwd_mlp(dt, PL, ne, eb->ef, dA, pk, d_ef, s),
+                 "conv_bwd: radial hidden layers");
+      TPC_LAUNCH("geom_bwd", s,
+                 tpc::launch_geom_bwd(dt, L2, ne, edge_begin, c->spec.r_cut, eb->rv, dY, dy_parts(c), d_ef,
+                                      nullptr, g_edge, s),
+                 "conv_bwd: geometry");
+    }
   }
   if (dh)
     TPC_LAUNCH("dh_gather", s,
@@ -957,6 +1012,64 @@ tpc_status tpc_conv_double_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, con
              "conv_double_bwd: tensor product");
   TPC_LAUNCH("part_sum", s, tpc::launch_part_sum(c->spec.dtype, yh_parts(c), ne, c->tab.dsh, w + L.yh, Y_hat, s),
              "conv_double_bwd: y_hat slices");
+  g_last_error.clear();
+  return TPC_OK;
+}
+
+tpc_status tpc_radial_table_fit(const tpc_ctx* c, const void* const* weights, void* table, size_t table_bytes_,
+                                double* certificate, void* ws, size_t ws_bytes, void* stream) {
+  Errors E;
+  if (!c) {
+    E.add(TPC_ERR_INVALID, "ctx must be non-null");
+    return E.finish();
+  }
+  if (!c->table) E.add(TPC_ERR_INVALID, "the context has no radial table (radial_table_pieces = 0)");
+  if (!weights) {
+    E.add(TPC_ERR_INVALID, "weights must be non-null");
+  } else {
+    for (int k = 0; k < c->spec.n_layers; ++k)
+      if (!weights[k]) E.add(TPC_ERR_INVALID, "weights[%d] must be non-null", k);
+  }
+  if (!certificate) E.add(TPC_ERR_INVALID, "certificate (host double[2]) must be non-null");
+  need_ptr(table, "table", 16, E);
+  if (E.status == TPC_OK && table_bytes_ < table_bytes(c))
+    E.add(TPC_ERR_INVALID, "table holds %zu bytes, needs %zu", table_bytes_, table_bytes(c));
+  const TableWs L = c->table ? table_layout(c) : TableWs{};
+  if (!ws) E.add(TPC_ERR_INVALID, "workspace must be non-null");
+  else if (!aligned(ws, 256)) E.add(TPC_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (ws && c->table && ws_bytes < L.total)
+    E.add(TPC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  tpc_status st = E.finish();
+  if (st != TPC_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  double* cert_dev = reinterpret_cast<double*>(w + L.cert);
+  const int pieces = c->spec.radial_table_pieces, deg = c->spec.radial_table_degree;
+  TPC_LAUNCH("table_fit", s,
+             tpc::launch_table_fit(c->spec.dtype, c->n_hidden, c->hidden, c->tab.np * c->spec.channels, pieces,
+                                   deg, c->spec.r_cut, weights, reinterpret_cast<double*>(w + L.nodes), table,
+                                   cert_dev, s),
+             "radial_table_fit");
+  const int npts = pieces;
+  std::vector<double> cert(2 * (size_t)npts);
+  TPC_HIP(hipMemcpyAsync(cert.data(), cert_dev, sizeof(double) * cert.size(), hipMemcpyDeviceToHost, s),
+          "radial_table_fit: read certificate");
+  TPC_HIP(hipStreamSynchronize(s), "radial_table_fit: wait");
+  double rv = 0.0, rd = 0.0;
+  for (int k = 0; k < npts; ++k) {
+    rv = cert[2 * k] > rv ? cert[2 * k] : rv;
+    rd = cert[2 * k + 1] > rd ? cert[2 * k + 1] : rd;
+  }
+  certificate[0] = rv;
+  certificate[1] = rd;
+  if (!(rv <= 1.0) || !(rd <= 1.0)) {
+    E.add(TPC_ERR_PRECONDITION,
+          "the table is not certified: error / rounding scale %.3g (values), %.3g (derivatives); "
+          "more pieces or a higher degree are needed",
+          rv, rd);
+    return E.finish();
+  }
   g_last_error.clear();
   return TPC_OK;
 }

@@ -11,7 +11,10 @@
 // Harmonics: component-normalised real harmonics (sum_m Y_lm^2 = 2l+1, z polar,
 // no Condon-Shortley phase), as Cartesian polynomials of the unit vector.
 // Radial basis: b_n(r) = sqrt(2/r_c) sin(n pi r/r_c)/r, n = 1..8, times the
-// p = 5 envelope u(x) = 1 - 21 x^5 + 35 x^6 - 15 x^7, x = r/r_c.
+// p = 5 envelope u(x) = 1 - 21 x^5 + 35 x^6 - 15 x^7, x = r/r_c, evaluated as
+// (1-x)^3 (1 + 3x + 6x^2 + 10x^3 + 15x^4): the same polynomial, whose triple
+// zero at the cutoff this form keeps to full relative accuracy (the expanded
+// terms cancel there to a value far below their rounding).
 //
 // One thread per edge; stores are row-contiguous per edge so the fused
 // tensor-product kernels read an edge's harmonics as one scalar block.
@@ -147,8 +150,8 @@ k_geom_fwd(GeomArgs a, T* __restrict__ Y, T* __restrict__ ef, T* __restrict__ rv
   for (int k = 0; k < DSH; ++k) Y[t * DSH + k] = Yv[k];
   const T rc = (T)a.r_cut;
   const T xr = r / rc;
-  const T x2 = xr * xr, x5 = x2 * x2 * xr;
-  const T env = T(1) - T(21) * x5 + T(35) * x5 * xr - T(15) * x5 * x2;
+  const T omx = T(1) - xr;
+  const T env = omx * omx * omx * (T(1) + xr * (T(3) + xr * (T(6) + xr * (T(10) + T(15) * xr))));
   T s1, c1;
   sincos_t<T>(T(3.14159265358979323846) * xr, &s1, &c1);
   const T pre = sqrt_t<T>(T(2) / rc) * ir * env;
@@ -169,7 +172,8 @@ k_geom_fwd(GeomArgs a, T* __restrict__ Y, T* __restrict__ ef, T* __restrict__ rv
 template <typename T, int L2>
 __global__ void __launch_bounds__(256)
 k_geom_bwd(int64_t ne, int64_t edge_begin, double r_cut, const T* __restrict__ rv,
-           const T* __restrict__ dY, int n_parts, const T* __restrict__ d_ef, T* __restrict__ g) {
+           const T* __restrict__ dY, int n_parts, const T* __restrict__ d_ef, const T* __restrict__ d_r,
+           T* __restrict__ g) {
   const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (t >= ne) return;
   constexpr int DSH = (L2 + 1) * (L2 + 1);
@@ -185,30 +189,34 @@ k_geom_bwd(int64_t ne, int64_t edge_begin, double r_cut, const T* __restrict__ r
   T q[3];
   harmonics_grad_dot<T, L2>(ux, uy, uz, w, q);
   const T uq = ux * q[0] + uy * q[1] + uz * q[2];
-  // radial part: sum_n d_ef_n * d(ef_n)/dr
-  const T rc = (T)r_cut;
-  const T xr = r / rc;
-  const T x2 = xr * xr, x4 = x2 * x2, x5 = x4 * xr;
-  const T env = T(1) - T(21) * x5 + T(35) * x5 * xr - T(15) * x5 * x2;
-  const T omx = T(1) - xr;
-  const T denv = T(-105) * x4 * omx * omx / rc;
-  T s1, c1;
-  sincos_t<T>(T(3.14159265358979323846) * xr, &s1, &c1);
-  const T pre = sqrt_t<T>(T(2) / rc);
-  const T k1 = T(3.14159265358979323846) / rc;
-  T sp = T(0), sn = s1, cp = T(1), cn = c1;
+  // radial part: sum_n d_ef_n * d(ef_n)/dr, or dL/dr given directly
   T acc = T(0);
+  if (d_r) {
+    acc = d_r[t];
+  } else {
+    const T rc = (T)r_cut;
+    const T xr = r / rc;
+    const T x2 = xr * xr, x4 = x2 * x2;
+    const T omx = T(1) - xr;
+    const T env = omx * omx * omx * (T(1) + xr * (T(3) + xr * (T(6) + xr * (T(10) + T(15) * xr))));
+    const T denv = T(-105) * x4 * omx * omx / rc;
+    T s1, c1;
+    sincos_t<T>(T(3.14159265358979323846) * xr, &s1, &c1);
+    const T pre = sqrt_t<T>(T(2) / rc);
+    const T k1 = T(3.14159265358979323846) / rc;
+    T sp = T(0), sn = s1, cp = T(1), cn = c1;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const T b = pre * sn * ir;
-    const T db = pre * (k1 * T(n + 1) * cn * ir - sn * ir * ir);
-    acc += d_ef[t * 8 + n] * (denv * b + env * db);
-    const T ns = T(2) * c1 * sn - sp;
-    const T nc = T(2) * c1 * cn - cp;
-    sp = sn;
-    sn = ns;
-    cp = cn;
-    cn = nc;
+    for (int n = 0; n < 8; ++n) {
+      const T b = pre * sn * ir;
+      const T db = pre * (k1 * T(n + 1) * cn * ir - sn * ir * ir);
+      acc += d_ef[t * 8 + n] * (denv * b + env * db);
+      const T ns = T(2) * c1 * sn - sp;
+      const T nc = T(2) * c1 * cn - cp;
+      sp = sn;
+      sn = ns;
+      cp = cn;
+      cn = nc;
+    }
   }
   const int64_t e = edge_begin + t;
   g[3 * e + 0] = (q[0] - uq * ux) * ir + acc * ux;
@@ -238,22 +246,23 @@ hipError_t geom_fwd_t(int L2, const GeomArgs& a, void* Y, void* ef, void* rv, hi
 
 template <typename T, int L2>
 hipError_t geom_bwd_impl(int64_t ne, int64_t edge_begin, double r_cut, const void* rv,
-                         const void* dY, int n_parts, const void* d_ef, void* g, hipStream_t s) {
+                         const void* dY, int n_parts, const void* d_ef, const void* d_r, void* g,
+                         hipStream_t s) {
   if (ne <= 0) return hipSuccess;
   k_geom_bwd<T, L2><<<(unsigned)((ne + 255) / 256), 256, 0, s>>>(
       ne, edge_begin, r_cut, static_cast<const T*>(rv), static_cast<const T*>(dY), n_parts,
-      static_cast<const T*>(d_ef), static_cast<T*>(g));
+      static_cast<const T*>(d_ef), static_cast<const T*>(d_r), static_cast<T*>(g));
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t geom_bwd_t(int L2, int64_t ne, int64_t eb, double rc, const void* rv, const void* dY,
-                      int n_parts, const void* d_ef, void* g, hipStream_t s) {
+                      int n_parts, const void* d_ef, const void* d_r, void* g, hipStream_t s) {
   switch (L2) {
-    case 0: return geom_bwd_impl<T, 0>(ne, eb, rc, rv, dY, n_parts, d_ef, g, s);
-    case 1: return geom_bwd_impl<T, 1>(ne, eb, rc, rv, dY, n_parts, d_ef, g, s);
-    case 2: return geom_bwd_impl<T, 2>(ne, eb, rc, rv, dY, n_parts, d_ef, g, s);
-    case 3: return geom_bwd_impl<T, 3>(ne, eb, rc, rv, dY, n_parts, d_ef, g, s);
+    case 0: return geom_bwd_impl<T, 0>(ne, eb, rc, rv, dY, n_parts, d_ef, d_r, g, s);
+    case 1: return geom_bwd_impl<T, 1>(ne, eb, rc, rv, dY, n_parts, d_ef, d_r, g, s);
+    case 2: return geom_bwd_impl<T, 2>(ne, eb, rc, rv, dY, n_parts, d_ef, d_r, g, s);
+    case 3: return geom_bwd_impl<T, 3>(ne, eb, rc, rv, dY, n_parts, d_ef, d_r, g, s);
   }
   return hipErrorInvalidValue;
 }
@@ -266,10 +275,10 @@ hipError_t launch_geom_fwd(int dtype, int L2, const GeomArgs& a, void* Y, void* 
 }
 
 hipError_t launch_geom_bwd(int dtype, int L2, int64_t ne, int64_t edge_begin, double r_cut,
-                           const void* rv, const void* dY, int n_parts, const void* d_ef, void* g,
+                           const void* rv, const void* dY, int n_parts, const void* d_ef, const void* d_r, void* g,
                            hipStream_t s) {
-  return dtype == 1 ? geom_bwd_t<double>(L2, ne, edge_begin, r_cut, rv, dY, n_parts, d_ef, g, s)
-                    : geom_bwd_t<float>(L2, ne, edge_begin, r_cut, rv, dY, n_parts, d_ef, g, s);
+  return dtype == 1 ? geom_bwd_t<double>(L2, ne, edge_begin, r_cut, rv, dY, n_parts, d_ef, d_r, g, s)
+                    : geom_bwd_t<float>(L2, ne, edge_begin, r_cut, rv, dY, n_parts, d_ef, d_r, g, s);
 }
 
 }  // namespace tpc

@@ -55,9 +55,11 @@ struct TPArgs {
 hipError_t launch_geom_fwd(int dtype, int L2, const GeomArgs& a, void* Y, void* ef, void* rv,
                            hipStream_t s);
 // dY holds n_parts partial slices [n_parts][ne][d_sh], summed in slice order.
+// The radial part comes from d_ef [ne][8] (dL/d(basis)), or, when d_ef is
+// null, from d_r [ne] (dL/dr directly, the table path).
 hipError_t launch_geom_bwd(int dtype, int L2, int64_t ne, int64_t edge_begin, double r_cut,
-                           const void* rv, const void* dY, int n_parts, const void* d_ef, void* g,
-                           hipStream_t s);
+                           const void* rv, const void* dY, int n_parts, const void* d_ef, const void* d_r,
+                           void* g, hipStream_t s);
 
 // The radial MLP's weights rewritten in MFMA operand order (element offsets
 // of each section in one buffer; every section starts on a 64-element
@@ -142,6 +144,21 @@ hipError_t launch_tp_dbl(int dtype, int L1, int L2, int L3, const TPArgs& a, hip
 // out[e][k] = sum over the n_parts slices of in[part][e][k], in slice order
 hipError_t launch_part_sum(int dtype, int n_parts, int64_t ne, int width, const void* in, void* out,
                            hipStream_t s);
+
+// Piecewise Chebyshev radial tables (radial_table.hip): elements of a table
+// of `pieces` pieces and degree d for pc columns; the fit writes float64
+// point values, the table and the certificate ratios [pieces][2].
+constexpr int kTableMaxDegree = 16;
+constexpr int kTableCheckPerPiece = 8;
+int64_t table_elems(int pieces, int degree, int pc);
+hipError_t launch_table_fit(int dtype, int NH, int H, int pc, int pieces, int degree, double r_cut,
+                            const void* const* w, double* f64_nodes, void* table, double* cert,
+                            hipStream_t s);
+hipError_t launch_table_fwd(int dtype, int64_t ne, int pc, int pieces, int degree, double r_cut,
+                            const void* rv, const void* table, void* R, hipStream_t s);
+// d_r[e] = dL/dr_e = sum_c dR[e][c] dR_c/dr (the radial part of the edge gradient)
+hipError_t launch_table_bwd(int dtype, int64_t ne, int pc, int pieces, int degree, double r_cut,
+                            const void* rv, const void* table, const void* dR, void* d_r, hipStream_t s);
 
 hipError_t launch_forces(int dtype, int64_t n, const int32_t* row_ptr, const int32_t* rev,
                          const void* g, void* forces, hipStream_t s);

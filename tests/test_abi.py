@@ -76,6 +76,8 @@ def _spec(**over):
     (dict(layer_dims=[8, 64, 64, 64, 999]), 1, "paths*channels"),
     (dict(layer_dims=[8, 48, 1280]), 2, "radial MLP"),
     (dict(layer_dims=[7, 64, 1280]), 1, "layer_dims[0]"),
+    (dict(radial_table_pieces=-1), 1, "radial_table_pieces"),
+    (dict(radial_table_pieces=16, radial_table_degree=0), 1, "radial_table_degree"),
     # float64 is built for node_lmax <= 1 only
     (dict(dtype="float64", node_lmax=2, layer_dims=[8, 64, 64, 64, 17 * 128]), 2, "no fused kernel"),
     (dict(dtype="float64", node_lmax=3, layer_dims=[8, 64, 64, 64, 23 * 128]), 2, "no fused kernel"),
@@ -159,3 +161,24 @@ def test_status_strings():
     lib = tpc.library()
     assert lib.tpc_status_string(3) == b"edge capacity too small"
     assert lib.tpc_status_string(99) == b"unknown status"
+
+
+def test_table_context_sizes_and_argument_checks():
+    """A table context reports its table size (pieces x (2 degree + 1) x P*C
+    values), needs no packed-weight workspace, and refuses a fit without a
+    table context, weights, certificate or large enough table."""
+    c = workloads.config(1)
+    ctx = tpc.Context(tpc.spec_for(c, table=(64, 8)))
+    assert ctx.sizes["table_bytes"] == 4 * 64 * 17 * ctx.r_width
+    assert ctx.sizes["fwd_workspace_bytes"] == 256
+    lib, h = _raw(ctx)
+    st = lib.tpc_radial_table_fit(h, None, None, 0, None, None, 0, None)
+    assert st == 1
+    m = lib.tpc_last_error().decode()
+    for needle in ("weights", "certificate", "table", "workspace"):
+        assert needle in m
+    plain = tpc.Context(tpc.spec_for(c))
+    lib, h = _raw(plain)
+    assert plain.sizes["table_bytes"] == 0
+    st = lib.tpc_radial_table_fit(h, None, None, 0, None, None, 0, None)
+    assert st == 1 and "no radial table" in lib.tpc_last_error().decode()
