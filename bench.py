@@ -50,6 +50,8 @@ KERNEL_SOURCES = {
     "geom_bwd": ["geom.hip"],
     "table_fwd": ["radial_table.hip"],
     "table_bwd": ["radial_table.hip"],
+    "radial_act": ["radial.hip"],
+    "tp_fwd_fused": ["tp_fused.hpp", "tp_fused.hip", "tp_impl.hpp", "tables.hpp", "tp_config.hpp"],
 }
 
 
@@ -65,6 +67,8 @@ KERNEL_SYMBOLS = {
     "geom_bwd": "k_geom_bwd<",
     "table_fwd": "k_table_fwd<",
     "table_bwd": "k_table_bwd<",
+    "radial_act": "k_radial_act<",
+    "tp_fwd_fused": "k_tp_fwd_fused<",
 }
 COPY_PROBE_BYTES = 1 << 30   # one plain device-to-device copy of this size calibrates the counters
 
@@ -88,9 +92,22 @@ def algorithmic(kernel, N, E, cfg, ctx):
     nnz = sum(int((t != 0).sum()) for t in tabs)
     m13 = sum(int((t != 0).any(axis=1).sum()) for t in tabs)
     csr = 4 * (N + 1) + 4 * E
+    hidden = 2 * (8 * H + (NH - 1) * H * H)
     if kernel == "tp_fwd":
         return (E * (T * PC + T * dsh) + N * T * C * (din + dout) + csr,
                 E * (2 * nnz + C * (2 * m13 + 2 * dout)))
+    if kernel == "tp_fwd_fused":
+        # reads the split activations (an intermediate of the radial split,
+        # counted here because this kernel is where they are read), Y, h and
+        # the CSR; writes out, and R when the backward needs it
+        act = ctx.sizes["act_bytes"]
+        r_out = T * PC if cfg.get("_store_R", True) else 0
+        tp = E * C * (2 * m13 + 2 * dout)
+        return (E * (act + T * dsh + r_out) + N * T * C * (din + dout) + csr,
+                tp + E * (2 * nnz * (C // 16)) + E * 2 * H * PC)
+    if kernel == "radial_act":
+        # reads ef, writes the split activations
+        return E * (8 * T + ctx.sizes["act_bytes"]), E * hidden
     if kernel == "tp_bwd_edge":
         # reads R, Y, h and G (once per atom); writes dR and dY.  The per-edge
         # dh contributions it also writes are an intermediate of the two-kernel
@@ -128,6 +145,11 @@ def group_rooflines(per_kernel, N, E, cfg, ctx):
     csr = 4 * (N + 1) + 4 * E
     groups = {
         "K8_tp_forward": (["tp_fwd"], E * (T * PC + T * dsh) + N * T * C * (din + dout) + csr),
+        # the fused forward: ef, Y, h and the CSR in, out (and R for the
+        # backward) out; the split activations are an intermediate
+        "K7K8_fused_forward": (["radial_act", "tp_fwd_fused"],
+                               E * (8 * T + T * dsh + (T * PC if cfg.get("_store_R", True) else 0))
+                               + N * T * C * (din + dout) + csr),
         "K9_tp_backward": (["tp_bwd_edge", "dh_gather"],
                            E * (2 * T * PC + 2 * T * dsh) + N * T * C * (2 * din + dout) + csr),
     }
@@ -135,23 +157,29 @@ def group_rooflines(per_kernel, N, E, cfg, ctx):
     for name, (ks, nbytes) in groups.items():
         if not all(k in per_kernel for k in ks):
             continue
-        sec = sum(per_kernel[k]["avg_ms"] for k in ks) * 1e-3
-        out[name] = dict(kernels=ks, algorithmic_bytes=nbytes, ms=sec * 1e3,
+        # the step's bytes over the group's time in the step (with chunks:
+        # every launch of every kernel of the group)
+        sec = sum(per_kernel[k]["ms_per_step"] for k in ks) * 1e-3
+        out[name] = dict(kernels=ks, algorithmic_bytes_per_step=nbytes, ms_per_step=sec * 1e3,
                          achieved_GBps=nbytes / sec / 1e9, frac=nbytes / sec / HBM_PEAK)
     return out
 
 
 def roofline_for(kernel, per_launch_s, N, E, cfg, ctx, workload="medium", launches=1):
+    """Roofline of one launch: ``per_launch_s`` its mean duration; the step's
+    algorithmic bytes and flops (all E edges) are split evenly over the
+    ``launches`` launches of a step (equal-edge receiver chunks)."""
     nbytes, flops = algorithmic(kernel, N, E, cfg, ctx)
     if nbytes is None:
         return None
+    nbytes, flops = nbytes / launches, flops / launches
     H, PC = cfg["hidden"][0], ctx.r_width
     if kernel in ("radial_fwd", "radial_bwd_dA") and str(ctx.dtype) == "torch.float32" and H % 32 == 0 and PC % 64 == 0:
         # the float32 last-layer products run as six bf16 products (three-part
         # operand split), the hidden layers on fp32 matrix cores; at those
         # rates the matrix work takes well under the time to stream R or dR,
         # so HBM bounds these kernels
-        last = E * 2 * H * PC
+        last = E * 2 * H * PC / launches
         ach = nbytes / per_launch_s
         r = dict(bound="hbm", achieved=ach / 1e9, peak=HBM_PEAK / 1e9, unit="GB/s",
                  frac=ach / HBM_PEAK, algorithmic_bytes_per_launch=nbytes,
@@ -167,8 +195,12 @@ def roofline_for(kernel, per_launch_s, N, E, cfg, ctx, workload="medium", launch
                  vector_alu_frac=(flops / per_launch_s) / VALU_F32_PEAK)
     r["kernel"] = kernel
     # the committed counters were taken on the default (separate-path) layout
-    t = None if cfg.get("sum_paths") else measured_traffic(kernel, workload)
-    r["traffic"] = None if t is None else t * launches
+    # the committed counters were taken on the default configuration: the
+    # separate-path layout and the default radial kernels
+    other = cfg.get("sum_paths") or (cfg.get("_radial_variant") and kernel.startswith(("radial", "table")))
+    t = None if other else measured_traffic(kernel, workload)
+    r["traffic"] = t
+    r["launches_per_step"] = launches
     return r
 
 
@@ -177,7 +209,7 @@ def traffic_path(workload):
 
 
 def measured_traffic(kernel, workload):
-    """HBM bytes per step of ``kernel`` from the committed counters of this
+    """HBM bytes per launch of ``kernel`` from the committed counters of this
     workload, when they were taken on the current kernel sources."""
     path = traffic_path(workload)
     if not os.path.exists(path):
@@ -388,6 +420,11 @@ def main(argv=None):
                     help="path-summed outputs (one block per output rank) on the same system")
     ap.add_argument("--radial-table", default=None, metavar="PIECES,DEGREE",
                     help="radial weights from certified piecewise Chebyshev tables (fitted before timing)")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time the neighbour build and conv_fwd only (no backward; with --fuse-radial no R "
+                         "buffer is written)")
+    ap.add_argument("--fuse-radial", action="store_true",
+                    help="the forward forms R inside the tensor-product kernel (spec.fuse_radial)")
     ap.add_argument("--fp32-mfma-only", action="store_true",
                     help="float32 radial products on float32 matrix cores only (no bf16 split)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -433,7 +470,12 @@ def main(argv=None):
     table = tuple(int(v) for v in a.radial_table.split(",")) if a.radial_table else None
     if table:
         cfg = dict(cfg, _table_degree=table[1])
-    ctx = tpc.Context(tpc.spec_for(cfg, fp32_mfma_only=a.fp32_mfma_only, table=table))
+    if table or a.fp32_mfma_only or a.fuse_radial:
+        cfg = dict(cfg, _radial_variant=True)
+    if a.forward_only:
+        cfg = dict(cfg, _store_R=False)   # the fused forward then writes no R
+    ctx = tpc.Context(tpc.spec_for(cfg, fp32_mfma_only=a.fp32_mfma_only, table=table,
+                                   fuse_radial=a.fuse_radial))
     pos = torch.from_numpy(d["pos"]).to(dev)
     species = torch.from_numpy(d["species"]).to(dev)
     h = torch.from_numpy(d["h"]).to(dev)
@@ -460,7 +502,8 @@ def main(argv=None):
     bounds = [(r0, r1, int(rp[r0]), int(rp[r1])) for r0, r1 in zip(cuts[:-1], cuts[1:]) if r1 > r0]
     max_e = max(e1 - e0 for _, _, e0, e1 in bounds)
     out = torch.empty((N, ctx.d_out, cfg["C"]), dtype=ctx.dtype, device=dev)
-    eb = ctx.alloc_edge_buffers(max_e, dev)
+    # a forward-only run of a fused context stores no R
+    eb = ctx.alloc_edge_buffers(max_e, dev, with_R=not a.forward_only)
     dh = torch.empty_like(h)
     dh_edge = torch.empty((E, ctx.d_in, cfg["C"]), dtype=ctx.dtype, device=dev)
     dR = torch.empty((max_e, ctx.r_width), dtype=ctx.dtype, device=dev)
@@ -475,6 +518,8 @@ def main(argv=None):
         for q, (r0, r1, e0, e1) in enumerate(bounds):
             ctx.conv_fwd(pos, cell, nl2, h, W, scale, out=out, eb=eb, rows=(r0, r1), edges=(e0, e1),
                          workspace=ws_f)
+            if a.forward_only:
+                continue
             last = q == len(bounds) - 1
             ctx.conv_bwd(nl2, h, W, scale, G, eb, dh=dh if last else None, dR=dR, g_edge=g_edge,
                          dh_edge=dh_edge, want_dh=last, forces=forces if last else None, want_forces=last,
@@ -503,7 +548,7 @@ def main(argv=None):
                   for n, (tot, cnt) in kt.items()}
 
     extras = {}
-    if not a.no_extras:
+    if not a.no_extras and not a.forward_only:
         # the virial (strain derivative) from the step's edge gradients, timed
         # on its own: it is not part of the step
         vir = torch.empty((3, 3), dtype=ctx.dtype, device=dev)
@@ -524,7 +569,7 @@ def main(argv=None):
 
     # one launch of each per pass (the weight packing runs once in each pass)
     fwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0)
-                 for n in ("geom_fwd", "radial_fwd", "table_fwd", "tp_fwd")) + \
+                 for n in ("geom_fwd", "radial_fwd", "radial_act", "table_fwd", "tp_fwd", "tp_fwd_fused")) + \
         per_kernel.get("radial_pack", {}).get("ms_per_step", 0.0) / 2
     bwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0)
                  for n in ("tp_bwd_edge", "radial_bwd_dA", "radial_bwd_mlp", "table_bwd", "geom_bwd", "dh_gather",
@@ -534,11 +579,12 @@ def main(argv=None):
     dominant = max((n for n in per_kernel if n in KERNEL_SOURCES), key=lambda n: per_kernel[n]["ms_per_step"])
     # algorithmic bytes of a step over the kernel's time in the step: with
     # equal-edge chunks this is the per-launch ratio of every chunk
-    roof = roofline_for(dominant, per_kernel[dominant]["ms_per_step"] * 1e-3, N, E, cfg, ctx, a.workload,
+    roof = roofline_for(dominant, per_kernel[dominant]["avg_ms"] * 1e-3, N, E, cfg, ctx, a.workload,
                         per_kernel[dominant]["launches_per_step"])
     kernels = {}
     for n, v in per_kernel.items():
-        r = roofline_for(n, v["ms_per_step"] * 1e-3, N, E, cfg, ctx, a.workload) if n in KERNEL_SOURCES else None
+        r = (roofline_for(n, v["avg_ms"] * 1e-3, N, E, cfg, ctx, a.workload, v["launches_per_step"])
+             if n in KERNEL_SOURCES else None)
         kernels[n] = dict(avg_ms=round(v["avg_ms"], 4), launches_per_step=v["launches_per_step"],
                           **({"bound": r["bound"], "frac": round(r["frac"], 4)} if r else {}))
 
@@ -567,11 +613,14 @@ def main(argv=None):
         "config": {"workload": f"{cfg['name']} ({geom}) N={N} E={E} C={cfg['C']} node_lmax={cfg['l1max']} "
                                f"sh_lmax={cfg['sh_lmax']} out_lmax={cfg['out_lmax']} "
                                f"mlp={'-'.join(map(str, cfg['layer_dims']))}: "
-                               "nbr_build + conv_fwd + conv_bwd (forces)"
+                               + ("nbr_build + conv_fwd (forward only)" if a.forward_only
+                                  else "nbr_build + conv_fwd + conv_bwd (forces)")
                                + (f" in {len(bounds)} receiver chunks" if len(bounds) > 1 else "")
                                + (", path-summed outputs" if cfg.get("sum_paths") else "")
                                + (f", radial tables {table[0]}x{table[1]}" if table else "")
-                               + (", float32 radial products on fp32 matrix cores" if a.fp32_mfma_only else ""),
+                               + (", float32 radial products on fp32 matrix cores" if a.fp32_mfma_only else "")
+                               + (", radial last layer fused into the forward tensor product"
+                                  if ctx.fused_radial else ""),
                    "n_atoms": N, "n_edges": E, "channels": cfg["C"], "paths": ctx.n_paths,
                    "chunks": len(bounds), "parallelism": "single GPU"},
         "roofline": roof,

@@ -131,6 +131,21 @@ typedef struct tpc_spec {
                                 convolution calls then take one weights
                                 pointer, the table */
   int radial_table_degree;   /* polynomial degree per piece, 1..16 */
+  int fuse_radial;           /* 0 (default): the radial network writes R and
+                                the tensor product reads it.  Nonzero, where
+                                the shapes allow it (float32, bf16-split
+                                products, hidden width 32 or 64, C a multiple
+                                of 16, no table): the forward forms R inside
+                                the tensor-product kernel from the last hidden
+                                activations (the fused folded forward of the
+                                FastMACE page "Rewrites and precision
+                                options", section "Convolution (OEq
+                                streaming)"), so a forward-only call needs no
+                                R buffer; tpc_info.fused_radial says whether
+                                it does.  It is slower than the two kernels
+                                on this GPU (its tensor product runs at two
+                                waves per SIMD) and is there for callers
+                                short of memory. */
 } tpc_spec;
 
 typedef struct tpc_info {
@@ -142,7 +157,7 @@ typedef struct tpc_info {
   /* Sizes of the buffers a caller allocates (bytes). */
   size_t edge_buffer_bytes;  /* per edge: Y, ef, rv and R of tpc_edge_buffers */
   size_t dR_bytes;           /* per edge: one row of dR */
-  size_t fwd_workspace_bytes;          /* tpc_conv_fwd workspace (any chunk) */
+  size_t fwd_workspace_bytes;          /* tpc_conv_fwd workspace: fixed part ... */
   size_t bwd_workspace_bytes_fixed;    /* tpc_conv_bwd workspace: fixed part ... */
   size_t bwd_workspace_bytes_per_edge; /* ... plus this per chunk edge (dR kept in
                                           the workspace when the caller passes
@@ -153,6 +168,15 @@ typedef struct tpc_info {
   size_t dh_edge_bytes;      /* per edge: one row of the dh_edge buffer of
                                 tpc_conv_bwd */
   size_t table_bytes;        /* the radial table (0 without one) */
+  size_t fwd_workspace_bytes_per_edge; /* ... plus this per chunk edge (a table
+                                          context sorts the chunk's edges by
+                                          piece; 0 otherwise), up to 256 bytes
+                                          of rounding; tpc_workspace_query
+                                          gives the exact figure */
+  int fused_radial;          /* 1: tpc_conv_fwd forms R inside the tensor-
+                                product kernel (see spec.fuse_radial) */
+  size_t act_bytes;          /* per edge: one row of tpc_edge_buffers.A (0
+                                when fused_radial is 0) */
 } tpc_info;
 
 /* Per-edge buffers.  conv_fwd writes them for the edges of the rows it
@@ -162,7 +186,15 @@ typedef struct tpc_edge_buffers {
   void* Y;    /* [E_chunk][d_sh]    harmonics of the edge direction */
   void* ef;   /* [E_chunk][8]       Bessel basis times envelope */
   void* rv;   /* [E_chunk][4]       edge vector (x, y, z) and its length */
-  void* R;    /* [E_chunk][P*C]     radial weights */
+  void* R;    /* [E_chunk][P*C]     radial weights; tpc_conv_bwd and
+                                   tpc_conv_double_bwd read them.  With
+                                   info.fused_radial the forward writes them
+                                   only when R is non-null (a forward-only
+                                   caller passes null and no R is stored) */
+  void* A;    /* [E_chunk][info.act_bytes] bytes: the radial network's last
+                 hidden activations in the library's own layout (written by
+                 tpc_conv_fwd when info.fused_radial; unused otherwise, may be
+                 null) */
 } tpc_edge_buffers;
 
 /* Create a context from a spec (host only; no device call).  Checks every
@@ -226,7 +258,9 @@ tpc_status tpc_nbr_build(const tpc_ctx* ctx, int64_t n_atoms, const double* pos,
  *             the last
  *   scale     s, the neighbour normalisation (1, or 1/avg_num_neighbors)
  *   out       [n_atoms][d_out][C], device; rows [row_begin,row_end) written
- *   eb        per-edge buffers written for the chunk (all four required)
+ *   eb        per-edge buffers written for the chunk: Y, ef and rv always;
+ *             R unless info.fused_radial (then optional); A when
+ *             info.fused_radial
  */
 tpc_status tpc_conv_fwd(const tpc_ctx* ctx, int64_t n_atoms, const double* pos,
                         const double* cell, const int32_t* row_ptr, const int32_t* src,

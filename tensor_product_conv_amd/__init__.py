@@ -46,7 +46,8 @@ class _Spec(ctypes.Structure):
                 ("poly_p", ctypes.c_int), ("n_species", ctypes.c_int), ("r_cut", ctypes.c_double),
                 ("n_layers", ctypes.c_int), ("layer_dims", ctypes.c_int * (TPC_MAX_LAYERS + 1)),
                 ("validate", ctypes.c_int), ("sum_paths", ctypes.c_int), ("fp32_mfma_only", ctypes.c_int),
-                ("radial_table_pieces", ctypes.c_int), ("radial_table_degree", ctypes.c_int)]
+                ("radial_table_pieces", ctypes.c_int), ("radial_table_degree", ctypes.c_int),
+                ("fuse_radial", ctypes.c_int)]
 
 
 class _Info(ctypes.Structure):
@@ -56,7 +57,9 @@ class _Info(ctypes.Structure):
                 ("edge_buffer_bytes", ctypes.c_size_t), ("dR_bytes", ctypes.c_size_t),
                 ("fwd_workspace_bytes", ctypes.c_size_t), ("bwd_workspace_bytes_fixed", ctypes.c_size_t),
                 ("bwd_workspace_bytes_per_edge", ctypes.c_size_t), ("dY_parts", ctypes.c_int),
-                ("dh_edge_bytes", ctypes.c_size_t), ("table_bytes", ctypes.c_size_t)]
+                ("dh_edge_bytes", ctypes.c_size_t), ("table_bytes", ctypes.c_size_t),
+                ("fwd_workspace_bytes_per_edge", ctypes.c_size_t),
+                ("fused_radial", ctypes.c_int), ("act_bytes", ctypes.c_size_t)]
 
 
 class _KernelTime(ctypes.Structure):
@@ -65,7 +68,7 @@ class _KernelTime(ctypes.Structure):
 
 class _EdgeBuffers(ctypes.Structure):
     _fields_ = [("Y", ctypes.c_void_p), ("ef", ctypes.c_void_p), ("rv", ctypes.c_void_p),
-                ("R", ctypes.c_void_p)]
+                ("R", ctypes.c_void_p), ("A", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -176,6 +179,7 @@ class Spec:
     fp32_mfma_only: bool = False
     radial_table_pieces: int = 0
     radial_table_degree: int = 0
+    fuse_radial: bool = False
 
     def to_c(self):
         s = _Spec()
@@ -192,6 +196,7 @@ class Spec:
         s.fp32_mfma_only = int(bool(self.fp32_mfma_only))
         s.radial_table_pieces = int(self.radial_table_pieces)
         s.radial_table_degree = int(self.radial_table_degree)
+        s.fuse_radial = int(bool(self.fuse_radial))
         return s
 
 
@@ -210,13 +215,14 @@ class EdgeBuffers:
     ef: object
     rv: object
     R: object
+    A: object = None       # uint8 [E, act_bytes] when the context fuses the radial last layer
     edge_begin: int = 0
     edge_end: int = 0
     row_begin: int = 0
     row_end: int = 0
 
     def to_c(self):
-        return _EdgeBuffers(_ptr(self.Y), _ptr(self.ef), _ptr(self.rv), _ptr(self.R))
+        return _EdgeBuffers(_ptr(self.Y), _ptr(self.ef), _ptr(self.rv), _ptr(self.R), _ptr(self.A))
 
 
 class Context:
@@ -235,7 +241,9 @@ class Context:
         self.paths = [tuple(info.paths[p]) for p in range(info.n_paths)]
         self.sizes = {k: getattr(info, k) for k in (
             "edge_buffer_bytes", "dR_bytes", "fwd_workspace_bytes", "bwd_workspace_bytes_fixed",
-            "bwd_workspace_bytes_per_edge", "dY_parts", "dh_edge_bytes", "table_bytes")}
+            "bwd_workspace_bytes_per_edge", "dY_parts", "dh_edge_bytes", "table_bytes", "act_bytes",
+            "fwd_workspace_bytes_per_edge")}
+        self.fused_radial = bool(info.fused_radial)
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -301,12 +309,17 @@ class Context:
         _check(st)
 
     # ---- forward ------------------------------------------------------------
-    def alloc_edge_buffers(self, n_edges, device):
+    def alloc_edge_buffers(self, n_edges, device, with_R=True):
+        """Per-edge buffers of a chunk of ``n_edges``; ``with_R=False`` leaves
+        out R when the context fuses the radial last layer (forward only)."""
         t = _torch()
+        act = self.sizes["act_bytes"]
         return EdgeBuffers(Y=t.empty((n_edges, self.d_sh), dtype=self.dtype, device=device),
                            ef=t.empty((n_edges, 8), dtype=self.dtype, device=device),
                            rv=t.empty((n_edges, 4), dtype=self.dtype, device=device),
-                           R=t.empty((n_edges, self.r_width), dtype=self.dtype, device=device))
+                           R=(t.empty((n_edges, self.r_width), dtype=self.dtype, device=device)
+                              if with_R or not self.fused_radial else None),
+                           A=t.empty((n_edges, act), dtype=t.uint8, device=device) if act else None)
 
     def conv_fwd(self, pos, cell, nl: NeighbourList, h, W, scale=1.0, out=None, eb=None,
                  rows=None, edges=None, workspace=None):
@@ -457,11 +470,12 @@ def conv_bwd(ctx: Context, *a, **k):
     return ctx.conv_bwd(*a, **k)
 
 
-def spec_for(cfg, validate=False, fp32_mfma_only=False, table=None):
+def spec_for(cfg, validate=False, fp32_mfma_only=False, table=None, fuse_radial=False):
     """Spec of a workload configuration dict (see ``workloads.config``);
     ``table`` = (pieces, degree) selects the radial tables."""
     return Spec(channels=cfg["C"], node_lmax=cfg["l1max"], sh_lmax=cfg["sh_lmax"],
                 out_lmax=cfg["out_lmax"], r_cut=cfg["r_cut"], layer_dims=list(cfg["layer_dims"]),
                 dtype=cfg["dtype"], validate=validate, sum_paths=bool(cfg.get("sum_paths", False)),
                 fp32_mfma_only=fp32_mfma_only,
-                radial_table_pieces=table[0] if table else 0, radial_table_degree=table[1] if table else 0)
+                radial_table_pieces=table[0] if table else 0, radial_table_degree=table[1] if table else 0,
+                fuse_radial=fuse_radial)

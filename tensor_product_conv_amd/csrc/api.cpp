@@ -27,6 +27,7 @@ struct tpc_ctx {
   int n_hidden;  // number of hidden layers
   size_t tsize;  // bytes per feature value
   bool table;    // radial weights from a piecewise Chebyshev table
+  bool fused;    // the forward forms R inside the tensor-product kernel
 };
 
 namespace {
@@ -200,7 +201,7 @@ NbrWs nbr_layout(int64_t n, int64_t nbin) {
 }
 
 struct BwdWs {
-  size_t dR, dY, d_ef, status, pack, dA, total, total_without_dR;
+  size_t dR, dY, d_ef, status, pack, dA, tsort, total, total_without_dR;
 };
 
 tpc::RadialPack pack_layout(const tpc_ctx* c) {
@@ -209,16 +210,19 @@ tpc::RadialPack pack_layout(const tpc_ctx* c) {
 }
 
 struct FwdWs {
-  size_t status, pack, total;
+  size_t status, pack, tsort, total;
 };
 
-FwdWs fwd_layout(const tpc_ctx* c) {
+// ne: edges of the chunk (a table context sorts them by piece)
+FwdWs fwd_layout(const tpc_ctx* c, int64_t ne) {
   FwdWs w{};
   size_t off = 0;
   w.status = off;
   off += align_up(sizeof(int32_t) * 8);
   w.pack = off;
   if (!c->table) off += align_up(c->tsize * (size_t)pack_layout(c).total);
+  w.tsort = off;
+  if (c->table) off += align_up(sizeof(int32_t) * (size_t)tpc::table_sort_ints(c->spec.radial_table_pieces, ne));
   w.total = off;
   return w;
 }
@@ -277,6 +281,8 @@ BwdWs bwd_layout(const tpc_ctx* c, int64_t ne) {
   if (!c->table) off += align_up(T * (size_t)pack_layout(c).total);
   w.dA = off;
   if (!c->table) off += align_up(T * (size_t)tpc::radial_dA_elems(c->hidden, ne));
+  w.tsort = off;
+  if (c->table) off += align_up(sizeof(int32_t) * (size_t)tpc::table_sort_ints(c->spec.radial_table_pieces, ne));
   w.total_without_dR = off;
   w.dR = off;
   off += align_up(T * (size_t)ne * c->tab.np * c->spec.channels);
@@ -370,6 +376,22 @@ tpc_status tpc_timing_collect(tpc_kernel_time* out, int max, int* n) {
   return TPC_OK;
 }
 
+namespace {
+
+// Whether the forward fuses the radial last layer into the tensor product:
+// asked for (spec.fuse_radial), float32 with the bf16-split products, hidden width 32 or 64, 16-channel
+// slices, no table, and the slice's weights (P x 64 lanes x H/32 x 24 bf16)
+// plus the waves' staging rows within the 160 KiB of LDS.
+bool fused_radial_ok(const tpc_spec& s, const tpc::Table& tab, int H) {
+  if (!s.fuse_radial || s.dtype != TPC_F32 || s.fp32_mfma_only || s.radial_table_pieces > 0) return false;
+  if ((H != 32 && H != 64) || s.channels % 16 != 0 || tab.np <= 0) return false;
+  if ((tab.np * s.channels) % 32 != 0) return false;
+  const size_t lds = (size_t)tab.np * 64 * (H / 32) * 24 * 2 + 8 * 256 * 4;
+  return lds <= 160 * 1024;
+}
+
+}  // namespace
+
 tpc_status tpc_ctx_create(const tpc_spec* spec, tpc_ctx** out) {
   Errors E;
   if (!spec || !out) {
@@ -426,6 +448,7 @@ tpc_status tpc_ctx_create(const tpc_spec* spec, tpc_ctx** out) {
   c->n_hidden = NH;
   c->tsize = s.dtype == TPC_F64 ? 8 : 4;
   c->table = s.radial_table_pieces > 0;
+  c->fused = fused_radial_ok(s, tab, H);
   *out = c;
   return TPC_OK;
 }
@@ -448,14 +471,17 @@ tpc_status tpc_ctx_info(const tpc_ctx* c, tpc_info* info) {
   const size_t T = c->tsize;
   info->edge_buffer_bytes = T * (size_t)(c->tab.dsh + 8 + 4 + c->tab.np * c->spec.channels);
   info->dR_bytes = T * (size_t)c->tab.np * c->spec.channels;
-  info->fwd_workspace_bytes = fwd_layout(c).total;
+  info->fwd_workspace_bytes = fwd_layout(c, 0).total;
   info->bwd_workspace_bytes_per_edge =
       T * (size_t)(c->tab.dsh * dy_parts(c) + 8 + (c->table ? 0 : c->hidden)) +
-      T * (size_t)c->tab.np * c->spec.channels;
+      T * (size_t)c->tab.np * c->spec.channels + (c->table ? sizeof(int32_t) : 0);
+  info->fwd_workspace_bytes_per_edge = c->table ? sizeof(int32_t) : 0;
   info->bwd_workspace_bytes_fixed = bwd_layout(c, 0).total;
   info->dY_parts = dy_parts(c);
   info->dh_edge_bytes = T * (size_t)c->tab.din * c->spec.channels;
   info->table_bytes = table_bytes(c);
+  info->fused_radial = c->fused ? 1 : 0;
+  info->act_bytes = c->fused ? (size_t)(c->hidden / 32) * 192 : 0;
   for (int p = 0; p < c->tab.np; ++p) {
     info->paths[p][0] = c->tab.path[p].l1;
     info->paths[p][1] = c->tab.path[p].l2;
@@ -506,7 +532,7 @@ tpc_status tpc_workspace_query(const tpc_ctx* c, int op, int64_t n_atoms, int64_
     if (E.status != TPC_OK) return E.finish();
     *bytes = nbr_layout(n_atoms, (int64_t)g.nb[0] * g.nb[1] * g.nb[2]).total;
   } else if (op == TPC_OP_FWD) {
-    *bytes = fwd_layout(c).total;
+    *bytes = fwd_layout(c, n_edges).total;
   } else if (op == TPC_OP_BWD) {
     *bytes = bwd_layout(c, n_edges).total;
   } else if (op == TPC_OP_VIRIAL) {
@@ -708,10 +734,15 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
     need_ptr(eb->Y, "eb.Y", va, E);
     need_ptr(eb->ef, "eb.ef", va, E);
     need_ptr(eb->rv, "eb.rv", va, E);
-    need_ptr(eb->R, "eb.R", va, E);
+    if (c->fused) {
+      need_ptr(eb->A, "eb.A", va, E);
+      if (eb->R && !aligned(eb->R, va)) E.add(TPC_ERR_INVALID, "eb.R must be %zu-byte aligned", va);
+    } else {
+      need_ptr(eb->R, "eb.R", va, E);
+    }
   }
   check_weights(c, weights, E);
-  const FwdWs FL = fwd_layout(c);
+  const FwdWs FL = fwd_layout(c, edge_end - edge_begin);
   if (edge_end > edge_begin || c->spec.validate) {
     if (!ws) E.add(TPC_ERR_INVALID, "workspace must be non-null");
     else if (ws_bytes < FL.total)
@@ -754,15 +785,20 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
     if (c->table) {
       TPC_LAUNCH("table_fwd", s,
                  tpc::launch_table_fwd(dt, ne, c->tab.np * c->spec.channels, c->spec.radial_table_pieces,
-                                       c->spec.radial_table_degree, c->spec.r_cut, eb->rv, weights[0], eb->R, s),
+                                       c->spec.radial_table_degree, c->spec.r_cut, eb->rv, weights[0],
+                                       static_cast<char*>(ws) + FL.tsort, eb->R, s),
                  "conv_fwd: radial table");
     } else {
       const tpc::RadialPack PL = pack_layout(c);
       void* pk = static_cast<char*>(ws) + FL.pack;
       TPC_LAUNCH("radial_pack", s, tpc::launch_radial_pack(dt, PL, weights, pk, s),
                  "conv_fwd: radial weight packing");
-      TPC_LAUNCH("radial_fwd", s, tpc::launch_radial_fwd(dt, PL, ne, eb->ef, pk, eb->R, s),
-                 "conv_fwd: radial MLP");
+      if (c->fused)
+        TPC_LAUNCH("radial_act", s, tpc::launch_radial_act(PL, ne, eb->ef, pk, eb->A, s),
+                   "conv_fwd: radial hidden layers");
+      else
+        TPC_LAUNCH("radial_fwd", s, tpc::launch_radial_fwd(dt, PL, ne, eb->ef, pk, eb->R, s),
+                   "conv_fwd: radial MLP");
     }
   }
   tpc::TPArgs ta{};
@@ -779,8 +815,22 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
   ta.R = eb ? eb->R : nullptr;
   ta.n_chunk_edges = edge_end - edge_begin;
   ta.out = out;
-  TPC_LAUNCH("tp_fwd", s, tpc::launch_tp_fwd(dt, c->spec.node_lmax, c->spec.sh_lmax, c->spec.out_lmax, ta, s),
-             "conv_fwd: tensor product");
+  // a chunk without edges has no packed weights (the workspace may be null):
+  // the unfused kernel writes its rows' zeros without reading any edge data
+  if (c->fused && ne > 0) {
+    const tpc::RadialPack PL = pack_layout(c);
+    ta.act = eb ? eb->A : nullptr;
+    ta.wfs = static_cast<const float*>(static_cast<const void*>(static_cast<char*>(ws) + FL.pack)) + PL.fs;
+    ta.H = c->hidden;
+    ta.R_out = eb ? eb->R : nullptr;
+    TPC_LAUNCH("tp_fwd_fused", s,
+               tpc::launch_tp_fused(c->spec.node_lmax, c->spec.sh_lmax, c->spec.out_lmax, ta, s),
+               "conv_fwd: tensor product with the radial last layer");
+  } else {
+    TPC_LAUNCH("tp_fwd", s,
+               tpc::launch_tp_fwd(dt, c->spec.node_lmax, c->spec.sh_lmax, c->spec.out_lmax, ta, s),
+               "conv_fwd: tensor product");
+  }
   g_last_error.clear();
   return TPC_OK;
 }
@@ -799,7 +849,7 @@ tpc_status tpc_conv_fwd_noalloc(const tpc_ctx* c, int64_t n, const double* pos, 
   size_t cap = 0;
   const hipError_t e = tpc::scratch_for_current_device(&scratch, &cap);
   if (e != hipSuccess) return device_error(e, "conv_fwd_noalloc: device scratch address");
-  const size_t need = fwd_layout(c).total;
+  const size_t need = fwd_layout(c, edge_end > edge_begin ? edge_end - edge_begin : 0).total;
   if (need > cap) {
     E.add(TPC_ERR_UNSUPPORTED, "this spec's forward needs %zu bytes of scratch; the fixed device scratch holds %zu",
           need, cap);
@@ -899,7 +949,7 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
       TPC_LAUNCH("table_bwd", s,
                  tpc::launch_table_bwd(dt, ne, c->tab.np * c->spec.channels, c->spec.radial_table_pieces,
                                        c->spec.radial_table_degree, c->spec.r_cut, eb->rv, weights[0], dRp,
-                                       d_ef, s),
+                                       w + L.tsort, d_ef, s),
                  "conv_bwd: radial table");
       TPC_LAUNCH("geom_bwd", s,
                  tpc::launch_geom_bwd(dt, L2, ne, edge_begin, c->spec.r_cut, eb->rv, dY, dy_parts(c), nullptr,

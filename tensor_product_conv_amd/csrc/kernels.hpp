@@ -50,6 +50,11 @@ struct TPArgs {
   void* g_hat;     // [N][d_out][C], rows [row_begin, row_end)
   void* x_hat;     // [N][d_in][C], rows [row_begin, row_end)
   void* w_hat;     // [E_chunk][P*C]
+  // forward with the fused radial last layer
+  const void* act;  // [E_chunk][H / 32][4][3][8] bf16: split last hidden activations
+  const void* wfs;  // the packed split last-layer weights (radial pack section fs)
+  int H;            // hidden width of the radial network
+  void* R_out;      // nullable: R [E_chunk][P*C] stored for a backward that reads it
 };
 
 hipError_t launch_geom_fwd(int dtype, int L2, const GeomArgs& a, void* Y, void* ef, void* rv,
@@ -119,6 +124,10 @@ hipError_t launch_radial_pack(int dtype, const RadialPack& L, const void* const*
                               hipStream_t s);
 hipError_t launch_radial_fwd(int dtype, const RadialPack& L, int64_t ne, const void* ef,
                              const void* pk, void* R, hipStream_t s);
+// Last hidden activations, split for the fused forward (float32, H = 32 or 64):
+// act [ne][H / 32][4][3][8] bf16.
+hipError_t launch_radial_act(const RadialPack& L, int64_t ne, const void* ef, const void* pk, void* act,
+                             hipStream_t s);
 hipError_t launch_radial_bwd_dA(int dtype, const RadialPack& L, int64_t ne, const void* dR,
                                 const void* pk, void* dA3, hipStream_t s);
 hipError_t launch_radial_bwd_mlp(int dtype, const RadialPack& L, int64_t ne, const void* ef,
@@ -127,6 +136,10 @@ hipError_t launch_radial_bwd_mlp(int dtype, const RadialPack& L, int64_t ne, con
 // Which (node_lmax, sh_lmax, out_lmax, channels) the fused kernels are built for.
 bool tp_supported(int dtype, int L1, int L2, int L3, int C);
 hipError_t launch_tp_fwd(int dtype, int L1, int L2, int L3, const TPArgs& a, hipStream_t s);
+// Forward with the radial last layer fused in (float32, C a multiple of 16,
+// H = 32 or 64): reads a.act and a.wfs instead of R; writes R too when a.R_out
+// is non-null.
+hipError_t launch_tp_fused(int L1, int L2, int L3, const TPArgs& a, hipStream_t s);
 // dR, the partial dY slices and the per-edge dh contributions of rows
 // [row_begin, row_end)
 hipError_t launch_tp_bwd(int dtype, int L1, int L2, int L3, const TPArgs& a, hipStream_t s);
@@ -154,11 +167,15 @@ int64_t table_elems(int pieces, int degree, int pc);
 hipError_t launch_table_fit(int dtype, int NH, int H, int pc, int pieces, int degree, double r_cut,
                             const void* const* w, double* f64_nodes, void* table, double* cert,
                             hipStream_t s);
+// Work buffer of the runtime table kernels: int32 [pieces + 1 + ne] (piece
+// counts, then the chunk's edges sorted by piece).
+int64_t table_sort_ints(int pieces, int64_t ne);
 hipError_t launch_table_fwd(int dtype, int64_t ne, int pc, int pieces, int degree, double r_cut,
-                            const void* rv, const void* table, void* R, hipStream_t s);
+                            const void* rv, const void* table, void* work, void* R, hipStream_t s);
 // d_r[e] = dL/dr_e = sum_c dR[e][c] dR_c/dr (the radial part of the edge gradient)
 hipError_t launch_table_bwd(int dtype, int64_t ne, int pc, int pieces, int degree, double r_cut,
-                            const void* rv, const void* table, const void* dR, void* d_r, hipStream_t s);
+                            const void* rv, const void* table, const void* dR, void* work, void* d_r,
+                            hipStream_t s);
 
 hipError_t launch_forces(int dtype, int64_t n, const int32_t* row_ptr, const int32_t* rev,
                          const void* g, void* forces, hipStream_t s);

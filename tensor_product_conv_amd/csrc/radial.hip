@@ -608,6 +608,63 @@ k_radial_fwd(int64_t ne, int pc, const T* __restrict__ ef, const T* __restrict__
   }
 }
 
+// The last hidden activations only (float32, H a multiple of 32), for the
+// forward that fuses the last layer into the tensor product: each activation
+// is split into three bf16 parts and stored in that kernel's A-operand order,
+//   act[e][kb][g][part][j] = part `part` of a[e][32 kb + 16 (j / 4) + 4 g + j % 4]
+// (the reduction order of the packed last-layer weights, section fs), so a
+// lane of that kernel reads its operand as three 16-byte vectors.  The lane
+// that computed an edge's activations holds exactly the features of k-slot g.
+template <int H, int NH, int S>
+__global__ void __launch_bounds__(256)
+k_radial_act(int64_t ne, const float* __restrict__ ef, const float* __restrict__ pk, RadialPack L,
+             __bf16* __restrict__ act_out) {
+  constexpr int NB = H / 16, S4 = 4 * NB, KB = H / 32;
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, el = lane % 16;
+  const int64_t e0 = (blockIdx.x * (int64_t)(blockDim.x / kWave) + threadIdx.x / kWave) * (16 * S);
+  if (e0 >= ne) return;
+  float act[S][NB][4];
+  layer0<float, H, S>(e0, ne, lane, ef, pk + L.f0, act);
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) act[st][nb][r] = silu<float>(act[st][nb][r]);
+#pragma unroll
+  for (int layer = 1; layer < NH; ++layer) {
+    float z[S][NB][4];
+    hidden<float, H, S>(lane, pk + L.fh + (int64_t)(layer - 1) * NB * kWave * S4, act, z);
+#pragma unroll
+    for (int st = 0; st < S; ++st)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) act[st][nb][r] = silu<float>(z[st][nb][r]);
+  }
+#pragma unroll
+  for (int st = 0; st < S; ++st) {
+    const int64_t e = e0 + st * 16 + el;
+    if (e >= ne) continue;
+    bf16x8* dst = reinterpret_cast<bf16x8*>(act_out + e * (KB * 96)) + g * 3;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      bf16x8 v[3];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        __bf16 p1, p2, p3;
+        split3(act[st][2 * kb + j / 4][j % 4], p1, p2, p3);
+        v[0][j] = p1;
+        v[1][j] = p2;
+        v[2][j] = p3;
+      }
+#pragma unroll
+      for (int part = 0; part < 3; ++part) dst[kb * 12 + part] = v[part];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // backward, part 1: dA[e][k] = sum_n dR[e][n] W_L[k][n].  Reduction step
 // (t, r), k-slot g covers n = 16t + 4g + r, so a lane reads four consecutive
@@ -1035,6 +1092,24 @@ hipError_t launch_radial_fwd(int dtype, const RadialPack& L, int64_t ne, const v
                              const void* pk, void* R, hipStream_t s) {
   if (ne <= 0) return hipSuccess;
   return dtype == 1 ? fwd_dispatch<double>(L, ne, ef, pk, R, s) : fwd_dispatch<float>(L, ne, ef, pk, R, s);
+}
+
+hipError_t launch_radial_act(const RadialPack& L, int64_t ne, const void* ef, const void* pk, void* act,
+                             hipStream_t s) {
+  if (ne <= 0) return hipSuccess;
+  const int64_t per_block = 4 * 16 * kFwdStrips;
+  const unsigned blocks = (unsigned)((ne + per_block - 1) / per_block);
+  const float* e = static_cast<const float*>(ef);
+  const float* p = static_cast<const float*>(pk);
+  __bf16* o = static_cast<__bf16*>(act);
+#define TPC_CASE(HH, NN)                                                                   \
+  if (L.H == HH && L.NH == NN) {                                                           \
+    k_radial_act<HH, NN, kFwdStrips><<<blocks, 256, 0, s>>>(ne, e, p, L, o);                \
+    return hipGetLastError();                                                              \
+  }
+  TPC_CASE(32, 1) TPC_CASE(32, 2) TPC_CASE(32, 3) TPC_CASE(64, 1) TPC_CASE(64, 2) TPC_CASE(64, 3)
+#undef TPC_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_radial_bwd_dA(int dtype, const RadialPack& L, int64_t ne, const void* dR,

@@ -22,12 +22,14 @@
 // runtime kernels do, at each piece's start and at points between its
 // nodes, and divides its largest error on the piece by the largest float
 // rounding scale, on the piece, of the computation it replaces.
-// Runtime: k_table_fwd writes R from the table (Clenshaw), k_table_bwd
-// forms dL/dr = sum_c dR[c] dR_c/dr for the geometry backward.
+// Runtime: k_table_fwd_sorted writes R from the table (Clenshaw), and
+// k_table_bwd_sorted forms dL/dr = sum_c dR[c] dR_c/dr for the geometry
+// backward, both over edges bucketed by piece (see below).
 #include <cmath>
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "nbr.hpp"
 
 namespace tpc {
 
@@ -242,38 +244,231 @@ k_table_cert(RadialWeights<T> W, int NH, int H, int pc, int pieces, int n, doubl
   }
 }
 
-// R[e][c] from the table: a block of 256 threads per (edge, 256-column
-// slice); the edge length is rv[e][3].
+// ---------------------------------------------------------------------------
+// Runtime evaluation over edges grouped by piece.  Evaluated edge by edge,
+// every edge would read (degree + 1) coefficient rows of P*C columns from L2,
+// about (degree + 1) times the bytes of the R row it writes.  Instead the
+// edges of a chunk are bucketed by piece (a counting sort: k_table_count,
+// k_table_offsets, k_table_place), and a block walks a contiguous range of
+// the sorted order with its columns' coefficients of the current piece in
+// registers, reloading them only when the piece changes.  Each R row (and
+// each dL/dr) depends on its own edge only, so the order the atomics give
+// the edges within a bucket changes no value.
+
+constexpr int kTabThreads = 512;  // threads per block
+constexpr int kTabCols = 6;       // columns per thread: P*C <= 3072
+constexpr int kTabChunk = 256;    // sorted positions per block
+
 template <typename T>
-__global__ void __launch_bounds__(256)
-k_table_fwd(int64_t ne, int pc, int pieces, int n, T r_cut, const T* __restrict__ rv,
-            const T* __restrict__ table, T* __restrict__ R) {
-  const int64_t e = blockIdx.y;
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= ne || c >= pc) return;
-  T v, d;
-  table_eval<T>(table, pieces, n, pc, r_cut, rv[e * 4 + 3], c, &v, &d);
-  __builtin_nontemporal_store(v, R + e * pc + c);
+__device__ __forceinline__ int table_piece(T r, T r_cut, int pieces) {
+  const T h = r_cut / (T)pieces;
+  int q = (int)(r / h);
+  return q < 0 ? 0 : (q >= pieces ? pieces - 1 : q);
 }
 
-// dL/dr[e] = sum_c dR[e][c] dR_c/dr(r_e): one wave per edge, lanes over the
-// columns, then a fixed-order wave sum.
 template <typename T>
-__global__ void __launch_bounds__(256)
-k_table_bwd(int64_t ne, int pc, int pieces, int n, T r_cut, const T* __restrict__ rv,
-            const T* __restrict__ table, const T* __restrict__ dR, T* __restrict__ d_r) {
-  const int lane = threadIdx.x % 64;
-  const int64_t e = blockIdx.x * (int64_t)(blockDim.x / 64) + threadIdx.x / 64;
-  if (e >= ne) return;
-  const T r = rv[e * 4 + 3];
-  T acc = T(0);
-  for (int c = lane; c < pc; c += 64) {
-    T v, d;
-    table_eval<T>(table, pieces, n, pc, r_cut, r, c, &v, &d);
-    acc += __builtin_nontemporal_load(dR + e * pc + c) * d;
+__device__ __forceinline__ T table_x(T r, T r_cut, int pieces, int q) {
+  const T h = r_cut / (T)pieces;
+  const T x = T(2) * (r - (T)q * h) / h - T(1);
+  return x < T(-1) ? T(-1) : (x > T(1) ? T(1) : x);
+}
+
+// Clenshaw sum of M coefficients a[0..M-1] at x, in table_eval's order.
+template <typename T, int M>
+__device__ __forceinline__ T clenshaw(const T (&a)[M], T x) {
+  if constexpr (M == 0) {
+    return T(0);
+  } else {
+    T b1 = T(0), b2 = T(0);
+#pragma unroll
+    for (int k = M - 1; k >= 1; --k) {
+      const T b0 = a[k] + T(2) * x * b1 - b2;
+      b2 = b1;
+      b1 = b0;
+    }
+    return a[0] + x * b1 - b2;
   }
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) d_r[e] = acc;
+}
+
+// The counting sort works per block of kSortChunk edges: counts in LDS,
+// then one global atomic per piece the block touches (a global atomic per
+// edge would serialise on the few piece counters).
+constexpr int kSortChunk = 4096;
+constexpr int kSortThreads = 256;
+constexpr int kMaxPieces = 4096;
+
+template <typename T>
+__global__ void __launch_bounds__(kSortThreads)
+k_table_count(int64_t ne, int pieces, T r_cut, const T* __restrict__ rv, int* __restrict__ counts) {
+  __shared__ int hist[kMaxPieces];
+  const int64_t e0 = blockIdx.x * (int64_t)kSortChunk;
+  for (int q = threadIdx.x; q < pieces; q += kSortThreads) hist[q] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < kSortChunk; i += kSortThreads) {
+    const int64_t e = e0 + i;
+    if (e < ne) atomicAdd(&hist[table_piece<T>(rv[e * 4 + 3], r_cut, pieces)], 1);
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < pieces; q += kSortThreads)
+    if (hist[q]) atomicAdd(&counts[q], hist[q]);
+}
+
+// counts -> start positions (exclusive scan; the pieces are few)
+__global__ void k_table_offsets(int pieces, int* __restrict__ counts) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int run = 0;
+  for (int q = 0; q < pieces; ++q) {
+    const int n = counts[q];
+    counts[q] = run;
+    run += n;
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kSortThreads)
+k_table_place(int64_t ne, int pieces, T r_cut, const T* __restrict__ rv, int* __restrict__ cursor,
+              int* __restrict__ order) {
+  __shared__ int hist[kMaxPieces];
+  const int64_t e0 = blockIdx.x * (int64_t)kSortChunk;
+  for (int q = threadIdx.x; q < pieces; q += kSortThreads) hist[q] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < kSortChunk; i += kSortThreads) {
+    const int64_t e = e0 + i;
+    if (e < ne) atomicAdd(&hist[table_piece<T>(rv[e * 4 + 3], r_cut, pieces)], 1);
+  }
+  __syncthreads();
+  // reserve the block's range of each piece; hist[q] becomes its next slot
+  for (int q = threadIdx.x; q < pieces; q += kSortThreads)
+    if (hist[q]) hist[q] = atomicAdd(&cursor[q], hist[q]);
+  __syncthreads();
+  for (int i = threadIdx.x; i < kSortChunk; i += kSortThreads) {
+    const int64_t e = e0 + i;
+    if (e < ne) order[atomicAdd(&hist[table_piece<T>(rv[e * 4 + 3], r_cut, pieces)], 1)] = (int)e;
+  }
+}
+
+// R[e][c] over sorted positions: N = degree + 1 value coefficients per column.
+template <typename T, int N>
+__global__ void __launch_bounds__(kTabThreads)
+k_table_fwd_sorted(int64_t ne, int pc, int pieces, T r_cut, const T* __restrict__ rv,
+                   const T* __restrict__ table, const int* __restrict__ order, T* __restrict__ R) {
+  __shared__ int se[kTabChunk];
+  __shared__ T sr[kTabChunk];
+  const int64_t p0 = blockIdx.x * (int64_t)kTabChunk;
+  const int np = (int)(p0 + kTabChunk < ne ? kTabChunk : ne - p0);
+  const int t = threadIdx.x;
+  // the block's edges and lengths first, so the loop below carries no
+  // dependent global loads
+  if (t < np) {
+    const int e = order[p0 + t];
+    se[t] = e;
+    sr[t] = rv[(int64_t)e * 4 + 3];
+  }
+  __syncthreads();
+  T cf[kTabCols][N];
+  int cur = -1;
+  for (int i = 0; i < np; ++i) {
+    const int e = se[i];
+    const T r = sr[i];
+    const int q = uniform(table_piece<T>(r, r_cut, pieces));
+    if (q != cur) {
+      const T* tq = table + (int64_t)q * (2 * N - 1) * pc;
+#pragma unroll
+      for (int j = 0; j < kTabCols; ++j) {
+        const int c = t + kTabThreads * j;
+#pragma unroll
+        for (int k = 0; k < N; ++k) cf[j][k] = c < pc ? tq[(int64_t)k * pc + c] : T(0);
+      }
+      cur = q;
+    }
+    const T x = table_x<T>(r, r_cut, pieces, q);
+    T* re = R + (int64_t)e * pc;
+#pragma unroll
+    for (int j = 0; j < kTabCols; ++j) {
+      const int c = t + kTabThreads * j;
+      if (c < pc) __builtin_nontemporal_store(clenshaw<T, N>(cf[j], x), re + c);
+    }
+  }
+}
+
+// dL/dr[e] = sum_c dR[e][c] dR_c/dr over sorted positions, GR edges per
+// reduction: the group's dR values load first (every load in flight at
+// once), then per edge the Clenshaw sums and per-thread partials, a wave sum,
+// and the block's waves added in a fixed order.
+template <typename T, int N>
+__global__ void __launch_bounds__(kTabThreads)
+k_table_bwd_sorted(int64_t ne, int pc, int pieces, T r_cut, const T* __restrict__ rv,
+                   const T* __restrict__ table, const T* __restrict__ dR, const int* __restrict__ order,
+                   T* __restrict__ d_r) {
+  constexpr int D = N - 1;  // derivative coefficients per column
+  constexpr int W = kTabThreads / 64;
+  constexpr int GR = sizeof(T) == 8 ? 4 : 16;  // edges per reduction
+  __shared__ T part[W][GR];
+  __shared__ int se[kTabChunk];
+  __shared__ T sr[kTabChunk];
+  const int64_t p0 = blockIdx.x * (int64_t)kTabChunk;
+  const int np = (int)(p0 + kTabChunk < ne ? kTabChunk : ne - p0);
+  const int t = threadIdx.x, lane = t % 64, wv = t / 64;
+  if (t < np) {
+    const int e = order[p0 + t];
+    se[t] = e;
+    sr[t] = rv[(int64_t)e * 4 + 3];
+  }
+  __syncthreads();
+  T cf[kTabCols][D > 0 ? D : 1];
+  int cur = -1;
+  for (int g0 = 0; g0 < np; g0 += GR) {
+    T dv[GR][kTabCols];
+#pragma unroll
+    for (int i = 0; i < GR; ++i) {
+      const int e = se[g0 + i < np ? g0 + i : np - 1];
+      const T* de = dR + (int64_t)e * pc;
+#pragma unroll
+      for (int j = 0; j < kTabCols; ++j) {
+        const int c = t + kTabThreads * j;
+        dv[i][j] = (c < pc && g0 + i < np) ? __builtin_nontemporal_load(de + c) : T(0);
+      }
+    }
+    T acc[GR];
+#pragma unroll
+    for (int i = 0; i < GR; ++i) {
+      acc[i] = T(0);
+      if (g0 + i < np) {
+        const T r = sr[g0 + i];
+        const int q = uniform(table_piece<T>(r, r_cut, pieces));
+        if (q != cur) {
+          const T* tq = table + ((int64_t)q * (2 * N - 1) + N) * pc;
+#pragma unroll
+          for (int j = 0; j < kTabCols; ++j) {
+            const int c = t + kTabThreads * j;
+#pragma unroll
+            for (int k = 0; k < D; ++k) cf[j][k] = c < pc ? tq[(int64_t)k * pc + c] : T(0);
+          }
+          cur = q;
+        }
+        const T x = table_x<T>(r, r_cut, pieces, q);
+        T sacc = T(0);
+#pragma unroll
+        for (int j = 0; j < kTabCols; ++j)
+          if constexpr (D > 0) sacc += dv[i][j] * clenshaw<T, D>(cf[j], x);
+        acc[i] = sacc;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GR; ++i) {
+      T v = acc[i];
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+      if (lane == 0) part[wv][i] = v;
+    }
+    __syncthreads();
+    if (t < GR && g0 + t < np) {
+      T v = T(0);
+#pragma unroll
+      for (int w = 0; w < W; ++w) v += part[w][t];
+      d_r[se[g0 + t]] = v;
+    }
+    __syncthreads();
+  }
 }
 
 }  // namespace
@@ -306,32 +501,88 @@ hipError_t launch_table_fit(int dtype, int NH, int H, int pc, int pieces, int de
   return hipGetLastError();
 }
 
-hipError_t launch_table_fwd(int dtype, int64_t ne, int pc, int pieces, int degree, double r_cut,
-                            const void* rv, const void* table, void* R, hipStream_t s) {
-  if (ne <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((pc + 255) / 256), (unsigned)ne);
-  if (dtype == 1)
-    k_table_fwd<double><<<grid, 256, 0, s>>>(ne, pc, pieces, degree + 1, r_cut, static_cast<const double*>(rv),
-                                             static_cast<const double*>(table), static_cast<double*>(R));
-  else
-    k_table_fwd<float><<<grid, 256, 0, s>>>(ne, pc, pieces, degree + 1, (float)r_cut, static_cast<const float*>(rv),
-                                            static_cast<const float*>(table), static_cast<float*>(R));
+int64_t table_sort_ints(int pieces, int64_t ne) { return (int64_t)pieces + 1 + ne; }
+
+namespace {
+
+template <typename T>
+hipError_t table_sort(int64_t ne, int pieces, double r_cut, const T* rv, int* work, hipStream_t s) {
+  int* counts = work;
+  int* order = work + pieces + 1;
+  hipError_t e = launch_fill_i32(counts, pieces + 1, 0, s);
+  if (e != hipSuccess) return e;
+  if (pieces > kMaxPieces) return hipErrorInvalidValue;
+  const unsigned blocks = (unsigned)((ne + kSortChunk - 1) / kSortChunk);
+  k_table_count<T><<<blocks, kSortThreads, 0, s>>>(ne, pieces, (T)r_cut, rv, counts);
+  k_table_offsets<<<1, 64, 0, s>>>(pieces, counts);
+  k_table_place<T><<<blocks, kSortThreads, 0, s>>>(ne, pieces, (T)r_cut, rv, counts, order);
   return hipGetLastError();
 }
 
-hipError_t launch_table_bwd(int dtype, int64_t ne, int pc, int pieces, int degree, double r_cut,
-                            const void* rv, const void* table, const void* dR, void* d_r, hipStream_t s) {
+#define TPC_TABLE_N(X) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16) X(17)
+
+template <typename T>
+hipError_t table_fwd_t(int64_t ne, int pc, int pieces, int n, double r_cut, const T* rv, const T* table,
+                       int* work, T* R, hipStream_t s) {
+  hipError_t e = table_sort<T>(ne, pieces, r_cut, rv, work, s);
+  if (e != hipSuccess) return e;
+  const unsigned blocks = (unsigned)((ne + kTabChunk - 1) / kTabChunk);
+  const int* order = work + pieces + 1;
+#define TPC_CASE(NN)                                                                                 \
+  if (n == NN) {                                                                                     \
+    k_table_fwd_sorted<T, NN><<<blocks, kTabThreads, 0, s>>>(ne, pc, pieces, (T)r_cut, rv, table, order, R); \
+    return hipGetLastError();                                                                        \
+  }
+  TPC_TABLE_N(TPC_CASE)
+#undef TPC_CASE
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t table_bwd_t(int64_t ne, int pc, int pieces, int n, double r_cut, const T* rv, const T* table,
+                       const T* dR, int* work, T* d_r, hipStream_t s) {
+  hipError_t e = table_sort<T>(ne, pieces, r_cut, rv, work, s);
+  if (e != hipSuccess) return e;
+  const unsigned blocks = (unsigned)((ne + kTabChunk - 1) / kTabChunk);
+  const int* order = work + pieces + 1;
+#define TPC_CASE(NN)                                                                                      \
+  if (n == NN) {                                                                                          \
+    k_table_bwd_sorted<T, NN><<<blocks, kTabThreads, 0, s>>>(ne, pc, pieces, (T)r_cut, rv, table, dR, order, \
+                                                              d_r);                                         \
+    return hipGetLastError();                                                                             \
+  }
+  TPC_TABLE_N(TPC_CASE)
+#undef TPC_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_table_fwd(int dtype, int64_t ne, int pc, int pieces, int degree, double r_cut,
+                            const void* rv, const void* table, void* work, void* R, hipStream_t s) {
   if (ne <= 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((ne + 3) / 4);
+  if (pc > kTabThreads * kTabCols) return hipErrorInvalidValue;
+  int* w = static_cast<int*>(work);
   if (dtype == 1)
-    k_table_bwd<double><<<blocks, 256, 0, s>>>(ne, pc, pieces, degree + 1, r_cut, static_cast<const double*>(rv),
-                                               static_cast<const double*>(table), static_cast<const double*>(dR),
-                                               static_cast<double*>(d_r));
-  else
-    k_table_bwd<float><<<blocks, 256, 0, s>>>(ne, pc, pieces, degree + 1, (float)r_cut,
-                                              static_cast<const float*>(rv), static_cast<const float*>(table),
-                                              static_cast<const float*>(dR), static_cast<float*>(d_r));
-  return hipGetLastError();
+    return table_fwd_t<double>(ne, pc, pieces, degree + 1, r_cut, static_cast<const double*>(rv),
+                               static_cast<const double*>(table), w, static_cast<double*>(R), s);
+  return table_fwd_t<float>(ne, pc, pieces, degree + 1, r_cut, static_cast<const float*>(rv),
+                            static_cast<const float*>(table), w, static_cast<float*>(R), s);
+}
+
+hipError_t launch_table_bwd(int dtype, int64_t ne, int pc, int pieces, int degree, double r_cut,
+                            const void* rv, const void* table, const void* dR, void* work, void* d_r,
+                            hipStream_t s) {
+  if (ne <= 0) return hipSuccess;
+  if (pc > kTabThreads * kTabCols) return hipErrorInvalidValue;
+  int* w = static_cast<int*>(work);
+  if (dtype == 1)
+    return table_bwd_t<double>(ne, pc, pieces, degree + 1, r_cut, static_cast<const double*>(rv),
+                               static_cast<const double*>(table), static_cast<const double*>(dR), w,
+                               static_cast<double*>(d_r), s);
+  return table_bwd_t<float>(ne, pc, pieces, degree + 1, r_cut, static_cast<const float*>(rv),
+                            static_cast<const float*>(table), static_cast<const float*>(dR), w,
+                            static_cast<float*>(d_r), s);
 }
 
 }  // namespace tpc

@@ -52,5 +52,10 @@ template <typename T, int L1, int L2, int L3>
 hipError_t tp_bwd_cfg(const TPArgs& a, hipStream_t s);
 template <typename T, int L1, int L2, int L3>
 hipError_t tp_dbl_cfg(const TPArgs& a, hipStream_t s);
+template <typename T, int L1, int L2, int L3>
+hipError_t tp_fused_cfg(const TPArgs& a, hipStream_t s);
+
+// Blocks of the fused forward (one per CU).
+constexpr int kFusedBlocks = 256;
 
 }  // namespace tpc

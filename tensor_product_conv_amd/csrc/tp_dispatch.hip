@@ -31,6 +31,14 @@ hipError_t launch_tp_fwd(int dtype, int L1, int L2, int L3, const TPArgs& a, hip
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_tp_fused(int L1, int L2, int L3, const TPArgs& a, hipStream_t s) {
+#define TPC_X(I, T, A, B, D) \
+  if (dtype_id<T>() == 0 && L1 == A && L2 == B && L3 == D) return tp_fused_cfg<T, A, B, D>(a, s);
+  TPC_TP_CONFIGS(TPC_X)
+#undef TPC_X
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_tp_bwd(int dtype, int L1, int L2, int L3, const TPArgs& a, hipStream_t s) {
 #define TPC_X(I, T, A, B, D) \
   if (dtype == dtype_id<T>() && L1 == A && L2 == B && L3 == D) return tp_bwd_cfg<T, A, B, D>(a, s);

@@ -170,7 +170,10 @@ def test_table_context_sizes_and_argument_checks():
     c = workloads.config(1)
     ctx = tpc.Context(tpc.spec_for(c, table=(64, 8)))
     assert ctx.sizes["table_bytes"] == 4 * 64 * 17 * ctx.r_width
-    assert ctx.sizes["fwd_workspace_bytes"] == 256
+    # status word and piece counts; the sorted edge order adds 4 bytes per edge
+    assert ctx.sizes["fwd_workspace_bytes"] == 256 + 512   # 65 counts round up to 512 bytes
+    assert ctx.sizes["fwd_workspace_bytes_per_edge"] == 4
+    assert ctx.workspace_bytes(tpc.OP_FWD, 0, 1000) == 256 + 4352
     lib, h = _raw(ctx)
     st = lib.tpc_radial_table_fit(h, None, None, 0, None, None, 0, None)
     assert st == 1
@@ -182,3 +185,32 @@ def test_table_context_sizes_and_argument_checks():
     assert plain.sizes["table_bytes"] == 0
     st = lib.tpc_radial_table_fit(h, None, None, 0, None, None, 0, None)
     assert st == 1 and "no radial table" in lib.tpc_last_error().decode()
+
+
+def test_fused_radial_selection_and_edge_buffer_checks():
+    """spec.fuse_radial takes the fused forward where the shapes allow it
+    (float32, bf16-split products, hidden width 32 or 64, C a multiple of 16,
+    no table) and reports the activation row size (H / 32 x 192 bytes); a
+    fused forward needs eb.A and no longer needs eb.R."""
+    c = workloads.config(1)
+    plain = tpc.Context(tpc.spec_for(c))
+    assert not plain.fused_radial and plain.sizes["act_bytes"] == 0
+    fused = tpc.Context(tpc.spec_for(c, fuse_radial=True))
+    assert fused.fused_radial and fused.sizes["act_bytes"] == 2 * 192
+    assert tpc.Context(tpc.spec_for(workloads.config(6), fuse_radial=True)).sizes["act_bytes"] == 192
+    # shapes the fused kernel does not take keep the two kernels
+    for k, extra in ((5, {}), (0, {}), (1, dict(fp32_mfma_only=True)), (1, dict(table=(64, 8)))):
+        assert not tpc.Context(tpc.spec_for(workloads.config(k), fuse_radial=True, **extra)).fused_radial
+    lib, h = _raw(fused)
+    eb = tpc._EdgeBuffers()
+    cell = (ctypes.c_double * 9)(*np.eye(3).reshape(-1).tolist())
+    st = lib.tpc_conv_fwd(h, 10, None, cell, None, None, None, 0, 10, 0, 5, None, None, 1.0, None,
+                          ctypes.byref(eb), None, 0, None)
+    assert st == 1
+    m = lib.tpc_last_error().decode()
+    assert "eb.A" in m and "eb.R" not in m
+    lib, h = _raw(plain)
+    st = lib.tpc_conv_fwd(h, 10, None, cell, None, None, None, 0, 10, 0, 5, None, None, 1.0, None,
+                          ctypes.byref(eb), None, 0, None)
+    m = lib.tpc_last_error().decode()
+    assert "eb.R" in m and "eb.A" not in m
