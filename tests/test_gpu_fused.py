@@ -8,13 +8,18 @@ import numpy as np
 import pytest
 
 import tensor_product_conv_amd as tpc
+import workloads
 from _gpu import TOL, Case, np_csr, rel, run_chunked, say, torch
 
 pytestmark = pytest.mark.gpu
 
 
 def _fused_case(k, with_grad=True):
-    case = Case(k, with_grad=with_grad)
+    # "10h64": config 10's dense system (node l <= 3, C = 64) with two hidden
+    # layers of 64, the large system's fused instantiation (P = 23 slices of
+    # 6 KB in LDS)
+    data = workloads.variant(10, 64, 3, 3, 3, [64, 64], "float32", 1064) if k == "10h64" else None
+    case = Case(10 if k == "10h64" else k, with_grad=with_grad, data=data)
     case.ctx = tpc.Context(tpc.spec_for(case.cfg, fuse_radial=True))
     assert case.ctx.fused_radial and case.ctx.sizes["act_bytes"] > 0
     return case
@@ -29,9 +34,10 @@ def _oracle(case, nl):
 
 # 1 small; 6, 7 hidden width 32 at 64 and 32 channels (one k-block of the
 # split products, 4 and 2 channel slices); 8 path-summed outputs; 9 rows of
-# 114-176 edges (up to 11 batches of 16 per row, ragged last batches)
+# 114-176 edges (up to 11 batches of 16 per row, ragged last batches); 10
+# node l <= 3 (P = 23, the largest weight slice in LDS)
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("k", [1, 6, 7, 8, 9])
+@pytest.mark.parametrize("k", [1, 6, 7, 8, 9, 10, "10h64"])
 def test_forward_without_R_matches_the_oracle(k):
     case = _fused_case(k, with_grad=False)
     ctx = case.ctx
@@ -56,7 +62,7 @@ def test_forward_without_R_matches_the_oracle(k):
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("k", [1, 8, 9])
+@pytest.mark.parametrize("k", [1, 8, 9, 10, "10h64"])
 def test_backward_on_the_fused_forward(k):
     case = _fused_case(k)
     nl = case.nbr()
