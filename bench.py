@@ -505,7 +505,7 @@ def main(argv=None):
     # a forward-only run of a fused context stores no R
     eb = ctx.alloc_edge_buffers(max_e, dev, with_R=not a.forward_only)
     dh = torch.empty_like(h)
-    dh_edge = torch.empty((E, ctx.d_in, cfg["C"]), dtype=ctx.dtype, device=dev)
+    dh_edge = torch.empty((max_e, ctx.d_in, cfg["C"]), dtype=ctx.dtype, device=dev)
     dR = torch.empty((max_e, ctx.r_width), dtype=ctx.dtype, device=dev)
     g_edge = torch.empty((E, 3), dtype=ctx.dtype, device=dev)
     forces = torch.empty((N, 3), dtype=ctx.dtype, device=dev)
@@ -521,9 +521,8 @@ def main(argv=None):
             if a.forward_only:
                 continue
             last = q == len(bounds) - 1
-            ctx.conv_bwd(nl2, h, W, scale, G, eb, dh=dh if last else None, dR=dR, g_edge=g_edge,
-                         dh_edge=dh_edge, want_dh=last, forces=forces if last else None, want_forces=last,
-                         workspace=ws_b)
+            ctx.conv_bwd(nl2, h, W, scale, G, eb, dh=dh, dR=dR, g_edge=g_edge, dh_edge=dh_edge,
+                         forces=forces if last else None, want_forces=last, workspace=ws_b)
 
     for _ in range(a.warmup):
         step()

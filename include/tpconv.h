@@ -165,8 +165,8 @@ typedef struct tpc_info {
                                           tpc_workspace_query gives the exact
                                           figure */
   int dY_parts;              /* partial dY slices the backward keeps per edge */
-  size_t dh_edge_bytes;      /* per edge: one row of the dh_edge buffer of
-                                tpc_conv_bwd */
+  size_t dh_edge_bytes;      /* per chunk edge: one row of the dh_edge
+                                buffer of tpc_conv_bwd */
   size_t table_bytes;        /* the radial table (0 without one) */
   size_t fwd_workspace_bytes_per_edge; /* ... plus this per chunk edge (a table
                                           context sorts the chunk's edges by
@@ -291,7 +291,7 @@ tpc_status tpc_conv_fwd_noalloc(const tpc_ctx* ctx, int64_t n_atoms, const doubl
                                 const tpc_edge_buffers* eb, void* stream);
 
 /* Backward of L = sum(G * out) for receivers [row_begin, row_end).
- *   n_edges   total edges of the list (g_edge, dh_edge and rev span all of them)
+ *   n_edges   total edges of the list (g_edge and rev span all of them)
  *   rev       [n_edges] int32 from tpc_nbr_build
  *   grad_out  G [n_atoms][d_out][C], device
  *   eb        per-edge buffers of the same chunk, as written by tpc_conv_fwd
@@ -299,19 +299,28 @@ tpc_status tpc_conv_fwd_noalloc(const tpc_ctx* ctx, int64_t n_atoms, const doubl
  *             dL/dR, the inner product of G with the unweighted product
  *             (FlashCart section 3, "Symbolic derivatives")
  *   g_edge    [n_edges][3] device, out: dL/d(edge vector), absolute edge index
- *   dh_edge   [n_edges][d_in][C] device, out: each edge's contribution to dL/dh
- *             of its sender, stored at the reverse edge's slot (so the
- *             contributions to atom j fill row j of the list)
- *   dh        [n_atoms][d_in][C] device, nullable: dL/dh = s * row sums of
- *             dh_edge, for every atom
+ *   dh_edge   [E_chunk][d_in][C] device, scratch of the call: each chunk
+ *             edge's contribution to dL/dh of its sender, at the edge's own
+ *             slot (reused by the next chunk's call)
+ *   dh        [n_atoms][d_in][C] device, nullable: dL/dh for every atom, the
+ *             sum over the entries of row j of the reverse edges'
+ *             contributions, times s.  Pass it on every chunk's call (or on
+ *             none), chunks in ascending row order covering [0, n_atoms):
+ *             each call continues every atom's sum with the entries of its
+ *             row whose sender lies in the chunk (the call with row_begin 0
+ *             starts the sums; between calls dh holds the unscaled partial
+ *             sums; the call with row_end n_atoms stores s * sum).  Each row
+ *             must be sorted by sender, as tpc_nbr_build leaves it; the
+ *             result then equals the unchunked call's bit for bit.
  *   forces    [n_atoms][3] device, nullable: F = -dL/dx from g_edge of every
  *             edge
- * dh and forces read the per-edge outputs of every edge, so pass them only on
- * the call that finishes the last chunk (all chunks' per-edge outputs written
- * earlier on this stream); an unchunked call passes everything at once.
- * With spec.validate the rows, sender indices and the reverse index are
- * checked first (TPC_ERR_PRECONDITION for an unsorted or non-symmetric list).
- * No atomics: every sum runs in a fixed order.
+ * forces reads g_edge of every edge, so pass it only on the call that
+ * finishes the last chunk (all chunks' g_edge written earlier on this
+ * stream); an unchunked call passes everything at once.
+ * With spec.validate the chunk's rows, sender indices and reverse index are
+ * checked first (TPC_ERR_PRECONDITION for an unsorted or non-symmetric list);
+ * a reverse index that leaves the chunk adds nothing to dh rather than being
+ * read.  No atomics: every sum runs in a fixed order.
  */
 tpc_status tpc_conv_bwd(const tpc_ctx* ctx, int64_t n_atoms, int64_t n_edges,
                         const int32_t* row_ptr, const int32_t* src, const int32_t* rev,

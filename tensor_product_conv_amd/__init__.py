@@ -11,7 +11,7 @@ library is missing or a call fails, an exception is raised.
                                layer_dims=[8, 64, 64, 64, 17 * 128]))
     nl = ctx.nbr_build(pos, cell)                    # receiver-sorted CSR
     out, saved = ctx.conv_fwd(pos, cell, nl, h, W, scale)
-    dh, dR, forces = ctx.conv_bwd(nl, h, W, scale, G, saved)
+    dh, dR, forces, g_edge = ctx.conv_bwd(nl, h, W, scale, G, saved)
 """
 from __future__ import annotations
 
@@ -349,10 +349,13 @@ class Context:
                  forces=None, workspace=None):
         """Backward of L = sum(G * out) for the chunk in ``eb``.
 
-        Returns (dh, dR, forces, g_edge).  dh and forces are sums over every
-        edge, so a chunked caller asks for them (want_dh / want_forces) only on
-        the last chunk, after every chunk's per-edge outputs (g_edge and
-        dh_edge, shared full-size buffers) are written.
+        Returns (dh, dR, forces, g_edge).  A chunked caller passes the same
+        dh on every chunk, chunks in ascending row order: each call continues
+        every atom's running sum with the chunk's terms (the first chunk
+        starts it, the last scales it), and dh_edge is chunk-sized scratch
+        that the calls may share.  forces sums g_edge over every edge, so it
+        is asked for (want_forces) only on the last chunk, after every chunk's
+        g_edge (one shared full-size buffer) is written.
         """
         t = _torch()
         N = h.shape[0]
@@ -366,8 +369,7 @@ class Context:
         if g_edge is None:
             g_edge = t.empty((nl.n_edges, 3), dtype=self.dtype, device=h.device)
         if dh_edge is None:
-            dh_edge = t.empty((nl.n_edges, self.d_in, self.spec.channels), dtype=self.dtype,
-                              device=h.device)
+            dh_edge = t.empty((ne, self.d_in, self.spec.channels), dtype=self.dtype, device=h.device)
         if want_forces and forces is None:
             forces = t.empty((N, 3), dtype=self.dtype, device=h.device)
         if not want_forces:

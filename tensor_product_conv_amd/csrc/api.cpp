@@ -264,8 +264,8 @@ VirialWs virial_layout(int64_t n) {
   return w;
 }
 
-int dy_parts(const tpc_ctx* c) { return tpc::tp_bwd_parts(c->spec.channels); }
-int yh_parts(const tpc_ctx* c) { return tpc::tp_dbl_parts(c->spec.dtype, c->spec.node_lmax, c->spec.channels); }
+int dy_parts(const tpc_ctx* c) { return tpc::tp_bwd_parts(c->spec.dtype, c->spec.node_lmax, c->spec.channels); }
+int yh_parts(const tpc_ctx* c) { return dy_parts(c); }
 
 BwdWs bwd_layout(const tpc_ctx* c, int64_t ne) {
   BwdWs w{};
@@ -883,11 +883,15 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
     need_ptr(src, "src", 4, E);
     need_ptr(rev, "rev", 4, E);
   }
-  if (n_edges > 0) {
-    need_ptr(g_edge, "g_edge", 8, E);
-    need_ptr(dh_edge, "dh_edge", va, E);
+  if (n_edges > 0) need_ptr(g_edge, "g_edge", 8, E);
+  if (edge_end > edge_begin) need_ptr(dh_edge, "dh_edge", va, E);
+  if (dh) {
+    need_ptr(dh, "dh", va, E);
+    if (n_edges > 0) {
+      need_ptr(src, "src", 4, E);
+      need_ptr(rev, "rev", 4, E);
+    }
   }
-  if (dh) need_ptr(dh, "dh", va, E);
   if (forces) {
     need_ptr(forces, "forces", 8, E);
     if (n_edges > 0) need_ptr(rev, "rev", 4, E);
@@ -971,10 +975,23 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
                  "conv_bwd: geometry");
     }
   }
-  if (dh)
-    TPC_LAUNCH("dh_gather", s,
-               tpc::launch_dh_gather(dt, n, c->tab.din * c->spec.channels, row_ptr, scale, dh_edge, dh, s),
-               "conv_bwd: dh row sums");
+  if (dh) {
+    tpc::DhGather g;
+    g.n = n;
+    g.din_c = c->tab.din * c->spec.channels;
+    g.row_ptr = row_ptr;
+    g.src = src;
+    g.rev = rev;
+    g.row_begin = row_begin;
+    g.row_end = row_end;
+    g.edge_begin = edge_begin;
+    g.n_chunk_edges = ne;
+    g.first = row_begin == 0;
+    g.last = row_end == n;
+    g.t_chunk = dh_edge;
+    g.dh = dh;
+    TPC_LAUNCH("dh_gather", s, tpc::launch_dh_gather(dt, g, scale, s), "conv_bwd: dh row sums");
+  }
   if (forces)
     TPC_LAUNCH("forces", s, tpc::launch_forces(dt, n, row_ptr, rev, g_edge, forces, s), "conv_bwd: forces");
   g_last_error.clear();

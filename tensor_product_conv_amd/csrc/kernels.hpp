@@ -39,9 +39,9 @@ struct TPArgs {
   void* out;       // forward: out [N][d_out][C]
   void* dR;        // backward edge kernel: [E][P*C]
   void* dY;        // backward: partial dY [parts][E][d_sh], parts = tp_bwd_parts
-                   // (double backward: partial y_hat, parts = tp_dbl_parts)
-  void* dh_edge;   // backward: [n_edges][d_in][C] per-edge dh contributions,
-                   // absolute edge index (stored at the reverse edge's slot)
+                   // (double backward: partial y_hat, parts = tp_bwd_parts)
+  void* dh_edge;   // backward: [E_chunk][d_in][C] per-edge dh contributions
+                   // of the chunk's edges, at each edge's own slot
   // double backward: cotangents of the VJP outputs and its results
   const int32_t* rev;  // reverse-edge index [n_edges]
   const void* uh;  // [N][d_in][C]
@@ -143,13 +143,26 @@ hipError_t launch_tp_fused(int L1, int L2, int L3, const TPArgs& a, hipStream_t 
 // dR, the partial dY slices and the per-edge dh contributions of rows
 // [row_begin, row_end)
 hipError_t launch_tp_bwd(int dtype, int L1, int L2, int L3, const TPArgs& a, hipStream_t s);
-// number of partial dY slices launch_tp_bwd writes (one per 64-channel wave)
-int tp_bwd_parts(int C);
-// number of partial y_hat slices launch_tp_dbl writes (one per wave of a row)
-int tp_dbl_parts(int dtype, int L1, int C);
-// dh[j] = scale * sum_{e in row j} dh_edge[e] for every atom
-hipError_t launch_dh_gather(int dtype, int64_t n, int din_c, const int32_t* row_ptr, double scale,
-                            const void* dh_edge, void* dh, hipStream_t s);
+// number of partial dY slices launch_tp_bwd writes, and of partial y_hat
+// slices launch_tp_dbl writes (one per wave of a row)
+int tp_bwd_parts(int dtype, int L1, int C);
+// One receiver chunk's step of dh: for every atom j, the running sum dh[j]
+// continues over the entries e of row j whose sender lies in
+// [row_begin, row_end), adding t_chunk[rev[e] - edge_begin] (launch_tp_bwd's
+// per-edge contributions of the chunk).  first starts the sums from zero,
+// last stores scale * sum.
+struct DhGather {
+  int64_t n = 0;
+  int din_c = 0;
+  const int32_t* row_ptr = nullptr;
+  const int32_t* src = nullptr;
+  const int32_t* rev = nullptr;
+  int64_t row_begin = 0, row_end = 0, edge_begin = 0, n_chunk_edges = 0;
+  bool first = true, last = true;
+  const void* t_chunk = nullptr;
+  void* dh = nullptr;
+};
+hipError_t launch_dh_gather(int dtype, const DhGather& g, double scale, hipStream_t s);
 // VJP-of-VJP of rows [row_begin, row_end): g_hat, x_hat of the rows, w_hat
 // and tp_bwd_parts partial slices of y_hat (in TPArgs::dY) of the chunk's
 // edges; separate (not path-summed) outputs only

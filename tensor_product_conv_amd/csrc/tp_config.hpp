@@ -32,19 +32,18 @@ struct TpCfg;
 TPC_TP_CONFIGS(TPC_CFG_TRAIT)
 #undef TPC_CFG_TRAIT
 
-// Waves per row and 64-channel slice in the double backward: whole l1
-// classes per wave.  Float64 splits further (its registers are twice as
-// wide).
+// Waves per row and 64-channel slice in the backward and the double
+// backward: whole l1 classes per wave.  Float64 splits further (its
+// registers are twice as wide).
 constexpr int bwd_groups(bool f64, int L1) {
   if (f64) return L1 + 1;
   return L1 <= 1 ? 1 : L1;
 }
 // 64-channel slices per row (1 for C <= 64)
 constexpr int channel_slices(int C) { return C <= 64 ? 1 : C / 64; }
-// Partial dY slices the backward writes (one per 64-channel wave of a row).
-constexpr int bwd_parts(int C) { return channel_slices(C); }
-// Partial y_hat slices the double backward writes (one per wave of a row).
-constexpr int dbl_parts(bool f64, int L1, int C) { return bwd_groups(f64, L1) * channel_slices(C); }
+// Partial dY (backward) and y_hat (double backward) slices: one per wave of
+// a row.
+constexpr int bwd_parts(bool f64, int L1, int C) { return bwd_groups(f64, L1) * channel_slices(C); }
 
 template <typename T, int L1, int L2, int L3>
 hipError_t tp_fwd_cfg(const TPArgs& a, hipStream_t s);

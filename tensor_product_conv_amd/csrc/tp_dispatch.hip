@@ -20,8 +20,7 @@ bool tp_supported(int dtype, int L1, int L2, int L3, int C) {
   return false;
 }
 
-int tp_bwd_parts(int C) { return bwd_parts(C); }
-int tp_dbl_parts(int dtype, int L1, int C) { return dbl_parts(dtype == 1, L1, C); }
+int tp_bwd_parts(int dtype, int L1, int C) { return bwd_parts(dtype == 1, L1, C); }
 
 hipError_t launch_tp_fwd(int dtype, int L1, int L2, int L3, const TPArgs& a, hipStream_t s) {
 #define TPC_X(I, T, A, B, D) \
@@ -56,27 +55,23 @@ hipError_t launch_tp_dbl(int dtype, int L1, int L2, int L3, const TPArgs& a, hip
 }
 
 template <typename T, int V>
-hipError_t dh_gather_impl(int64_t n, int din_c, const int32_t* row_ptr, double scale,
-                          const void* dh_edge, void* dh, hipStream_t s) {
-  const int64_t total = n * (din_c / V);
-  const unsigned blocks = (unsigned)((total + 255) / 256);
-  k_dh_gather<T, V><<<blocks, 256, 0, s>>>(n, din_c, row_ptr, (T)scale, static_cast<const T*>(dh_edge),
-                                           static_cast<T*>(dh));
+hipError_t dh_gather_impl(const DhGather& g, double scale, hipStream_t s) {
+  const int64_t waves = g.n * ((g.din_c + 64 * V - 1) / (64 * V));
+  const unsigned blocks = (unsigned)((waves + kGatherWaves - 1) / kGatherWaves);
+  k_dh_gather_chunk<T, V><<<blocks, 64 * kGatherWaves, 0, s>>>(
+      g.n, g.din_c, g.row_ptr, g.src, g.rev, g.row_begin, g.row_end, g.edge_begin, g.n_chunk_edges, g.first,
+      g.last, (T)scale, static_cast<const T*>(g.t_chunk), static_cast<T*>(g.dh));
   return hipGetLastError();
 }
 
-hipError_t launch_dh_gather(int dtype, int64_t n, int din_c, const int32_t* row_ptr, double scale,
-                            const void* dh_edge, void* dh, hipStream_t s) {
-  if (n * din_c <= 0) return hipSuccess;
+hipError_t launch_dh_gather(int dtype, const DhGather& g, double scale, hipStream_t s) {
+  if (g.n * g.din_c <= 0) return hipSuccess;
   // 16-byte vectors when every row of din_c values starts 16-byte aligned
   const size_t tsz = dtype == 1 ? 8 : 4;
-  const bool vec = (din_c * tsz) % 16 == 0 && reinterpret_cast<uintptr_t>(dh_edge) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(dh) % 16 == 0;
-  if (dtype == 1)
-    return vec ? dh_gather_impl<double, 2>(n, din_c, row_ptr, scale, dh_edge, dh, s)
-               : dh_gather_impl<double, 1>(n, din_c, row_ptr, scale, dh_edge, dh, s);
-  return vec ? dh_gather_impl<float, 4>(n, din_c, row_ptr, scale, dh_edge, dh, s)
-             : dh_gather_impl<float, 1>(n, din_c, row_ptr, scale, dh_edge, dh, s);
+  const bool vec = (g.din_c * tsz) % 16 == 0 && reinterpret_cast<uintptr_t>(g.t_chunk) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(g.dh) % 16 == 0;
+  if (dtype == 1) return vec ? dh_gather_impl<double, 2>(g, scale, s) : dh_gather_impl<double, 1>(g, scale, s);
+  return vec ? dh_gather_impl<float, 4>(g, scale, s) : dh_gather_impl<float, 1>(g, scale, s);
 }
 
 }  // namespace tpc

@@ -129,36 +129,6 @@ __device__ __forceinline__ void edge_loop(int e_lo, int e_hi, Load&& load, Compu
   if (e < e_hi) compute(e, A);
 }
 
-template <int NW>
-__device__ __forceinline__ int channels(int C) {
-  if constexpr (NW > 0) {
-    return 64 * NW;
-  } else {
-    return C;
-  }
-}
-
-struct RowWave {
-  int row;   // receiver (or atom) index
-  int c0;    // this lane's channel
-  bool on;   // c0 < C
-  bool ok;   // the wave has a row to process
-};
-
-template <int NW>
-__device__ __forceinline__ RowWave row_wave(int64_t row_begin, int64_t row_end, int C) {
-  const int lane = threadIdx.x % kTPWave;
-  const int wpr = NW > 0 ? NW : 1;  // waves per row
-  const int64_t w = xcd_block() * kTPWavesPerBlock + threadIdx.x / kTPWave;
-  RowWave r;
-  const int64_t row = row_begin + w / wpr;
-  r.ok = row < row_end;
-  r.row = uniform((int)(r.ok ? row : row_begin));
-  r.c0 = (int)(w % wpr) * kTPWave + lane;
-  r.on = r.c0 < C;
-  return r;
-}
-
 // ---------------------------------------------------------------------------
 // Forward.  NG * NWC waves share a receiver row: NWC channel slices of
 // 64 * CPL channels, and in each slice NG waves that own compile-time subsets
@@ -431,40 +401,44 @@ __device__ __forceinline__ T wave_reduce_scatter16(const T (&v)[16]) {
   return d;
 }
 
-// Backward, edge side.  One wave per receiver row and 64 channels (NW waves
-// per row, one channel per lane), G[i] held in registers for the whole row.
-// Per edge and path, with K[m1][m2] = sum_m3 C^p[m1,m2,m3] G[i,(p,m3)]:
+// Backward, edge side.  NG * NWC waves share a receiver row: NWC slices of
+// 64 channels (one channel per lane; one masked wave for C < 64), and in each
+// slice NG waves that own whole l1 classes of the paths (kBwdGroups), so each
+// reads only its rows of h, R and G and writes disjoint rows of the dh
+// contributions.  G[i] rows of the group's paths stay in registers for the
+// whole row.  Per edge and path, with K[m1][m2] = sum_m3 C^p[m1,m2,m3]
+// G[i,(p,m3)]:
 //   W[m1] = sum_m2 Y[m2] K[m1][m2]    Q[m2] = sum_m1 h[j,m1] K[m1][m2]
-//   dR    = s * sum_m1 h[j,m1] W[m1]  dY[m2] += R Q[m2]   (channel reduction)
+//   dR    = s * sum_m1 h[j,m1] W[m1]  dY[m2] += R Q[m2]   (channel reduction,
+//                                      one partial slice per wave)
 //   t[m1] += R W[m1]                  (the edge's contribution to dh of its
-//                                      sender j, stored at the reverse edge's
-//                                      slot so dh of j is a contiguous row sum)
-template <typename T, int L1, int L2, int L3, bool SUM, int NW>
-__global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
-k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src,
-              const int32_t* __restrict__ rev, int64_t row_begin, int64_t row_end,
-              int64_t edge_begin, int64_t n_chunk_edges, int C, T scale, const T* __restrict__ h,
-              const T* __restrict__ Y, const T* __restrict__ R, const T* __restrict__ G,
-              T* __restrict__ dR, T* __restrict__ dYp, T* __restrict__ dh_edge) {
-  constexpr int NP = kTable<L1, L2, L3, SUM>.np, DIN = kTable<L1, L2, L3, SUM>.din;
-  constexpr int DSH = kTable<L1, L2, L3, SUM>.dsh, DOUT = kTable<L1, L2, L3, SUM>.dout;
+//                                      sender j, stored at the edge's own slot
+//                                      of the chunk; k_dh_gather_chunk sums
+//                                      them along row j through the reverse
+//                                      index)
+#define TBL kTable<L1, L2, L3, SUM>
+#define BGR kBwdGroups<L1, L2, L3, SUM, NG>
+template <typename T, int L1, int L2, int L3, bool SUM, bool MASKED, int NG, int G>
+__device__ __forceinline__ void tp_bwd_edge_group(const int32_t* __restrict__ src, int i, int e_lo, int e_hi,
+                                                  int64_t edge_begin, int64_t n_chunk_edges, int CC, uint32_t c0,
+                                                  bool on, int part, T scale, const T* __restrict__ h,
+                                                  const T* __restrict__ Y, const T* __restrict__ R,
+                                                  const T* __restrict__ G_, T* __restrict__ dR,
+                                                  T* __restrict__ dYp, T* __restrict__ dh_edge) {
+  constexpr int NP = TBL.np, DIN = TBL.din, DSH = TBL.dsh, DOUT = TBL.dout;
   static_assert(DSH <= 16, "harmonics beyond l = 3");
-  const RowWave rw = row_wave<NW>(row_begin, row_end, C);
-  if (!rw.ok) return;
-  const int i = rw.row;
-  const int CC = channels<NW>(C);
+  static_assert(BGR.ok, "every wave group owns an l1 class");
+  constexpr int NWM = MASKED ? 0 : 1;   // ldc/stc: masked lanes past C
   const int PC = NP * CC;
-  const uint32_t c0 = (uint32_t)rw.c0;
-  const int e_lo = uniform(row_ptr[i]), e_hi = uniform(row_ptr[i + 1]);
-  if (e_lo == e_hi) return;
   const int lane = threadIdx.x % kTPWave;
-  const int part = rw.c0 / kTPWave;   // which 64-channel slice (partial dY buffer)
 
   T gi[DOUT];
   {
-    const T* __restrict__ gr = G + (int64_t)i * DOUT * CC;
-#pragma unroll
-    for (int o = 0; o < DOUT; ++o) gi[o] = ldc<NW>(gr, o * CC + c0, rw.on);
+    const T* __restrict__ gr = G_ + (int64_t)i * DOUT * CC;
+    static_for<DOUT>([&](auto oc) {
+      constexpr int o = decltype(oc)::value;
+      if constexpr (bwd_group_reads_row(TBL, BGR, G, o)) gi[o] = ldc<NWM>(gr, o * CC + c0, on);
+    });
   }
 
   // The edge's harmonics travel with the prefetch as one vector load (lane k
@@ -475,18 +449,21 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
     T h[DIN];
     T r[NP];
     T y;
-    int er;  // reverse edge
   };
   const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
-  auto load_j = [&](int e, int j, int er, Buf& b) __attribute__((always_inline)) {
+  auto load_j = [&](int e, int j, Buf& b) __attribute__((always_inline)) {
     const T* __restrict__ hj = h + (int64_t)j * DIN * CC;
     const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
-#pragma unroll
-    for (int m = 0; m < DIN; ++m) b.h[m] = ldc<NW>(hj, m * CC + c0, rw.on);
-#pragma unroll
-    for (int p = 0; p < NP; ++p) b.r[p] = ldc_nt<NW>(re, p * CC + c0, rw.on);
+    static_for<DIN>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int l1 = m >= 9 ? 3 : m >= 4 ? 2 : m >= 1 ? 1 : 0;
+      if constexpr (bwd_group_owns_l1(TBL, BGR, G, l1)) b.h[m] = ldc<NWM>(hj, m * CC + c0, on);
+    });
+    static_for<NP>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      if constexpr (BGR.group[p] == G) b.r[p] = ldc_nt<NWM>(re, p * CC + c0, on);
+    });
     b.y = Y[((int64_t)e - edge_begin) * DSH + ylane];
-    b.er = er;
   };
   auto compute = [&](int e, const Buf& b) __attribute__((always_inline)) {
     const int64_t el = (int64_t)e - edge_begin;
@@ -502,50 +479,55 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
     for (int m = 0; m < DIN; ++m) t[m] = T(0);
     static_for<NP>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
-      constexpr Path P = kTable<L1, L2, L3, SUM>.path[p];
-      constexpr int n1 = 2 * P.l1 + 1, n2 = 2 * P.l2 + 1;
-      T K[n1][n2];
+      if constexpr (BGR.group[p] == G) {
+        constexpr Path P = TBL.path[p];
+        constexpr int n1 = 2 * P.l1 + 1, n2 = 2 * P.l2 + 1;
+        T K[n1][n2];
 #pragma unroll
-      for (int a = 0; a < n1; ++a)
+        for (int a = 0; a < n1; ++a)
 #pragma unroll
-        for (int c = 0; c < n2; ++c) K[a][c] = T(0);
-      static_for<2 * P.l3 + 1>([&](auto m3c) {
-        constexpr int m3 = decltype(m3c)::value;
-        constexpr int row = kTable<L1, L2, L3, SUM>.out_row(p, m3);
-        static_for<n1>([&](auto m1c) {
-          constexpr int m1 = decltype(m1c)::value;
-          static_for<n2>([&](auto m2c) {
-            constexpr int m2 = decltype(m2c)::value;
-            constexpr double cv = kTable<L1, L2, L3, SUM>.cg[p][m1][m2][m3];
-            if constexpr (cv != 0.0) K[m1][m2] += T(cv) * gi[row];
+          for (int c = 0; c < n2; ++c) K[a][c] = T(0);
+        static_for<2 * P.l3 + 1>([&](auto m3c) {
+          constexpr int m3 = decltype(m3c)::value;
+          constexpr int row = TBL.out_row(p, m3);
+          static_for<n1>([&](auto m1c) {
+            constexpr int m1 = decltype(m1c)::value;
+            static_for<n2>([&](auto m2c) {
+              constexpr int m2 = decltype(m2c)::value;
+              constexpr double cv = TBL.cg[p][m1][m2][m3];
+              if constexpr (cv != 0.0) K[m1][m2] += T(cv) * gi[row];
+            });
           });
         });
-      });
-      T dr = T(0);
-      static_for<n1>([&](auto m1c) {
-        constexpr int m1 = decltype(m1c)::value;
-        T w = T(0);
-        static_for<n2>([&](auto m2c) {
-          constexpr int m2 = decltype(m2c)::value;
-          if constexpr (kTable<L1, L2, L3, SUM>.m12nz(p, m1, m2)) w += ye[P.l2 * P.l2 + m2] * K[m1][m2];
-        });
-        dr += b.h[P.l1 * P.l1 + m1] * w;
-        t[P.l1 * P.l1 + m1] += b.r[p] * w;
-      });
-      static_for<n2>([&](auto m2c) {
-        constexpr int m2 = decltype(m2c)::value;
-        T q = T(0);
+        T dr = T(0);
         static_for<n1>([&](auto m1c) {
           constexpr int m1 = decltype(m1c)::value;
-          if constexpr (kTable<L1, L2, L3, SUM>.m12nz(p, m1, m2)) q += b.h[P.l1 * P.l1 + m1] * K[m1][m2];
+          T w = T(0);
+          static_for<n2>([&](auto m2c) {
+            constexpr int m2 = decltype(m2c)::value;
+            if constexpr (TBL.m12nz(p, m1, m2)) w += ye[P.l2 * P.l2 + m2] * K[m1][m2];
+          });
+          dr += b.h[P.l1 * P.l1 + m1] * w;
+          t[P.l1 * P.l1 + m1] += b.r[p] * w;
         });
-        dy[P.l2 * P.l2 + m2] += b.r[p] * q;
-      });
-      stc_nt<NW>(dre, p * CC + c0, rw.on, scale * dr);
+        static_for<n2>([&](auto m2c) {
+          constexpr int m2 = decltype(m2c)::value;
+          T q = T(0);
+          static_for<n1>([&](auto m1c) {
+            constexpr int m1 = decltype(m1c)::value;
+            if constexpr (TBL.m12nz(p, m1, m2)) q += b.h[P.l1 * P.l1 + m1] * K[m1][m2];
+          });
+          dy[P.l2 * P.l2 + m2] += b.r[p] * q;
+        });
+        stc_nt<NWM>(dre, p * CC + c0, on, scale * dr);
+      }
     });
-    T* __restrict__ te = dh_edge + (int64_t)b.er * DIN * CC;
-#pragma unroll
-    for (int m = 0; m < DIN; ++m) stc_nt<NW>(te, m * CC + c0, rw.on, t[m]);
+    T* __restrict__ te = dh_edge + el * DIN * CC;
+    static_for<DIN>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int l1 = m >= 9 ? 3 : m >= 4 ? 2 : m >= 1 ? 1 : 0;
+      if constexpr (bwd_group_owns_l1(TBL, BGR, G, l1)) stc_nt<NWM>(te, m * CC + c0, on, t[m]);
+    });
     // every lane of a quad holds the same total, so with 16 harmonics all
     // lanes store (identical values per address) and the store needs no
     // branch, which keeps the wait for the next edge's loads exact
@@ -554,48 +536,123 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
       dYp[((int64_t)part * n_chunk_edges + el) * DSH + (lane >> 2)] = scale * tot;
   };
   if (e_hi - e_lo > 64 * kIdxWindows) {
-    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, uniform(src[e]), uniform(rev[e]), b); },
+    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, uniform(src[e]), b); },
                    compute);
   } else {
-    RowIdx<kIdxWindows> si, ri;
+    RowIdx<kIdxWindows> si;
     si.init(src, e_lo, e_hi, lane);
-    ri.init(rev, e_lo, e_hi, lane);
     edge_loop<Buf>(e_lo, e_hi,
-                   [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, si.get(e - e_lo), ri.get(e - e_lo), b); }, compute);
+                   [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, si.get(e - e_lo), b); }, compute);
   }
+}
+#undef TBL
+#undef BGR
+
+// Wave w of the grid: row w / (NG * NWC), then group and channel slice;
+// partial dY slice (channel slice) * NG + group.
+template <typename T, int L1, int L2, int L3, bool SUM, bool MASKED, int NG, int NWC>
+__global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
+k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, int64_t row_begin,
+              int64_t row_end, int64_t edge_begin, int64_t n_chunk_edges, int C, T scale, const T* __restrict__ h,
+              const T* __restrict__ Y, const T* __restrict__ R, const T* __restrict__ G_, T* __restrict__ dR,
+              T* __restrict__ dYp, T* __restrict__ dh_edge) {
+  const int lane = threadIdx.x % kTPWave;
+  const int64_t w = xcd_block() * kTPWavesPerBlock + threadIdx.x / kTPWave;
+  const int64_t row = row_begin + w / (NG * NWC);
+  if (row >= row_end) return;
+  const int i = uniform((int)row);
+  const int rem = uniform((int)(w % (NG * NWC)));
+  const int g = rem % NG, cw = rem / NG;
+  const int CC = MASKED ? C : 64 * NWC;
+  const uint32_t c0 = (uint32_t)(cw * 64 + lane);
+  const bool on = (int)c0 < C;
+  const int e_lo = uniform(row_ptr[i]), e_hi = uniform(row_ptr[i + 1]);
+  if (e_lo == e_hi) return;
+  const int part = cw * NG + g;
+  static_for<NG>([&](auto gc) {
+    constexpr int G = decltype(gc)::value;
+    if (g == G)
+      tp_bwd_edge_group<T, L1, L2, L3, SUM, MASKED, NG, G>(src, i, e_lo, e_hi, edge_begin, n_chunk_edges, CC, c0,
+                                                           on, part, scale, h, Y, R, G_, dR, dYp, dh_edge);
+  });
 }
 
 // ---------------------------------------------------------------------------
-// dh[j] = s * sum over the edges e of row j of dh_edge[e]: each slot holds the
-// contribution of the reverse edge (whose sender is j), so the sum runs over a
-// contiguous range in CSR order (deterministic, no atomics).  One thread per
-// (atom, group of V consecutive feature values); every value is summed over
-// the row's edges in CSR order, V at a time, with eight edges' loads in
-// flight (non-temporal: each value is read once).
+// dh of every atom j, one receiver chunk at a time.  The backward of the
+// chunk's edges leaves each edge's contribution to dh of its sender at the
+// edge's own slot of the chunk (t_chunk).  Atom j gathers them along its own
+// row through the symmetric list: the entries e' of row j whose sender lies
+// in the chunk's rows [row_begin, row_end) have their reverse edges in the
+// chunk, at t_chunk[rev(e') - edge_begin].  Row j is sorted by sender, so
+// those entries form one contiguous run, and the runs of successive chunks
+// follow each other in row order: continuing the running sum chunk after
+// chunk adds every term in the same CSR order as a single pass over the
+// whole list, so chunked and unchunked results agree bit for bit, and the
+// intermediate only spans one chunk's edges.  dh holds the unscaled sum
+// between chunks (first: start from zero; last: store s * sum).
+//
+// One wave per (atom, slab of 64 V feature values), V consecutive values per
+// lane, eight terms' loads in flight.  The wave's atom is uniform, so the row
+// bounds and reverse indices are scalar loads, and the run is found with one
+// coalesced load of up to 64 senders per step and two ballots (the number of
+// entries below row_begin and below row_end).  A reverse index outside the
+// chunk (a list that is not symmetric or not sender-sorted) contributes
+// nothing rather than reading outside t_chunk.  Deterministic, no atomics.
+constexpr int kGatherWaves = 4;
 template <typename T, int V>
-__global__ void __launch_bounds__(256)
-k_dh_gather(int64_t n, int din_c, const int32_t* __restrict__ row_ptr, T scale,
-            const T* __restrict__ dh_edge, T* __restrict__ dh) {
+__global__ void __launch_bounds__(64 * kGatherWaves)
+k_dh_gather_chunk(int64_t n, int din_c, const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src,
+                  const int32_t* __restrict__ rev, int64_t row_begin, int64_t row_end, int64_t edge_begin,
+                  int64_t n_chunk_edges, bool first, bool last, T scale, const T* __restrict__ t_chunk,
+                  T* __restrict__ dh) {
   typedef T vec __attribute__((ext_vector_type(V)));
-  const int groups = din_c / V;
-  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (t >= n * groups) return;
-  const int64_t j = t / groups;
-  const int q = (int)(t - j * groups) * V;
-  vec acc = vec(T(0));
-  const int lo = row_ptr[j], hi = row_ptr[j + 1];
-  const T* __restrict__ p = dh_edge + q;
+  const int lane = threadIdx.x % 64;
+  const int slabs = (din_c + 64 * V - 1) / (64 * V);
+  const int64_t w = (int64_t)blockIdx.x * kGatherWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  if (w >= n * slabs) return;
+  const int64_t j = w / slabs;
+  const int q = (int)(w - j * slabs) * 64 * V + lane * V;
+  const int r0 = row_ptr[j], r1 = row_ptr[j + 1];
+  int lo = r0, hi = r1;
+  if (n_chunk_edges <= 0) {
+    hi = lo;
+  } else if (row_begin > 0 || row_end < n) {
+    int below_begin = 0, below_end = 0;
+    for (int b = r0; b < r1; b += 64) {
+      const int e = b + lane;
+      const int v = e < r1 ? src[e] : 0x7fffffff;
+      below_begin += __popcll(__ballot(v < row_begin));
+      below_end += __popcll(__ballot(v < row_end));
+    }
+    lo = r0 + below_begin;
+    hi = r0 + below_end;
+  }
+  if (q >= din_c) return;
+  T* __restrict__ dj = dh + j * din_c + q;
+  vec acc = first ? vec(T(0)) : *reinterpret_cast<const vec*>(dj);
+  const T* __restrict__ p = t_chunk + q;
+  auto term = [&](int e) __attribute__((always_inline)) {
+    const int64_t r = (int64_t)rev[e] - edge_begin;
+    return (uint64_t)r < (uint64_t)n_chunk_edges ? r : int64_t(-1);
+  };
   int e = lo;
   for (; e + 8 <= hi; e += 8) {
+    int64_t r[8];
     vec a[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      a[k] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(p + (int64_t)(e + k) * din_c));
+    for (int k = 0; k < 8; ++k) r[k] = term(e + k);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc += a[k];
+    for (int k = 0; k < 8; ++k)
+      a[k] = __builtin_nontemporal_load(reinterpret_cast<const vec*>(p + (r[k] < 0 ? 0 : r[k]) * din_c));
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (r[k] >= 0) acc += a[k];
   }
-  for (; e < hi; ++e) acc += *reinterpret_cast<const vec*>(p + (int64_t)e * din_c);
-  *reinterpret_cast<vec*>(dh + j * din_c + q) = scale * acc;
+  for (; e < hi; ++e) {
+    const int64_t r = term(e);
+    if (r >= 0) acc += *reinterpret_cast<const vec*>(p + r * din_c);
+  }
+  *reinterpret_cast<vec*>(dj) = last ? scale * acc : acc;
 }
 
 // ---------------------------------------------------------------------------
