@@ -11,15 +11,16 @@ namespace tpc {
 
 // Waves of a row: C = 128 takes two 64-channel waves, each over every path
 // (sender features and radial weights are then read once per edge); C = 64
-// splits the paths over two waves when the output block is large (by whole
-// l1 classes where that balances, so each wave reads only its rows of h);
-// C < 64 masks the lanes past C.
+// splits the paths over two waves when the output block is large, three at
+// node l <= 3 (by whole l1 classes where that balances, so each wave reads
+// only its rows of h; three waves hold about 130 registers each, four waves
+// per SIMD); C < 64 masks the lanes past C.
 template <typename T, int L1, int L2, int L3, bool SUM>
 hipError_t fwd_launch(const TPArgs& a, hipStream_t s) {
   const int64_t rows = a.row_end - a.row_begin;
   constexpr int DOUT = kTable<L1, L2, L3, SUM>.dout;
   const bool masked = a.C < 64;
-  const int ng = DOUT >= 64 ? 2 : 1;
+  const int ng = DOUT >= 96 ? 3 : DOUT >= 64 ? 2 : 1;
   const T sc = (T)a.scale;
   const T* h = static_cast<const T*>(a.h);
   const T* Y = static_cast<const T*>(a.Y);
@@ -35,7 +36,9 @@ hipError_t fwd_launch(const TPArgs& a, hipStream_t s) {
   } else if (a.C == 128) {
     TPC_GO(1, false, 2);
   } else {
-    if (ng == 2) TPC_GO(2, false, 1); else TPC_GO(1, false, 1);
+    if (ng == 3) TPC_GO(3, false, 1);
+    else if (ng == 2) TPC_GO(2, false, 1);
+    else TPC_GO(1, false, 1);
   }
 #undef TPC_GO
   return hipGetLastError();
