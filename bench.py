@@ -59,14 +59,14 @@ KERNEL_SOURCES = {
 KERNEL_SYMBOLS = {
     "tp_fwd": "k_tp_fwd<",
     "tp_bwd_edge": "k_tp_bwd_edge<",
-    "dh_gather": "k_dh_gather<",
+    "dh_gather": "k_dh_gather_chunk<",
     "radial_fwd": "k_radial_fwd<",
     "radial_bwd_dA": "k_radial_bwd_dA",   # also the bf16-split k_radial_bwd_dA_x6
     "radial_bwd_mlp": "k_radial_bwd_mlp<",
     "geom_fwd": "k_geom_fwd<",
     "geom_bwd": "k_geom_bwd<",
-    "table_fwd": "k_table_fwd<",
-    "table_bwd": "k_table_bwd<",
+    "table_fwd": "k_table_fwd_sorted<",
+    "table_bwd": "k_table_bwd_sorted<",
     "radial_act": "k_radial_act<",
     "tp_fwd_fused": "k_tp_fwd_fused<",
 }
@@ -184,6 +184,27 @@ def roofline_for(kernel, per_launch_s, N, E, cfg, ctx, workload="medium", launch
         r = dict(bound="hbm", achieved=ach / 1e9, peak=HBM_PEAK / 1e9, unit="GB/s",
                  frac=ach / HBM_PEAK, algorithmic_bytes_per_launch=nbytes,
                  matrix_frac=((flops - last) / MFMA_F32_PEAK + 6 * last / MFMA_BF16_PEAK) / per_launch_s)
+    elif kernel == "tp_fwd_fused":
+        # three bounds: the bytes it moves, the tensor product on the vector
+        # ALUs, and the radial last layer on the matrix cores as six bf16
+        # products (executed bf16 flops against the bf16 peak).  The largest
+        # ideal time names the bound; at the medium system it is the vector
+        # ALUs (the kernel runs well below all three: latency-bound).
+        mat = E * 2 * H * PC / launches
+        vec = flops - mat
+        t_hbm, t_vec, t_mat = nbytes / HBM_PEAK, vec / VALU_F32_PEAK, 6 * mat / MFMA_BF16_PEAK
+        fr = dict(hbm_frac=t_hbm / per_launch_s, vector_alu_frac=t_vec / per_launch_s,
+                  matrix_frac=t_mat / per_launch_s)
+        if t_mat >= max(t_hbm, t_vec):
+            r = dict(bound="mfma", achieved=6 * mat / per_launch_s / 1e12, peak=MFMA_BF16_PEAK / 1e12,
+                     unit="TFLOP/s", frac=fr["matrix_frac"], executed_bf16_flops_per_launch=6 * mat)
+        elif t_vec >= t_hbm:
+            r = dict(bound="alu", achieved=vec / per_launch_s / 1e12, peak=VALU_F32_PEAK / 1e12,
+                     unit="TFLOP/s", frac=fr["vector_alu_frac"], vector_flops_per_launch=vec)
+        else:
+            r = dict(bound="hbm", achieved=nbytes / per_launch_s / 1e9, peak=HBM_PEAK / 1e9, unit="GB/s",
+                     frac=fr["hbm_frac"])
+        r.update(fr, algorithmic_bytes_per_launch=nbytes, algorithmic_matrix_flops_per_launch=mat)
     elif kernel.startswith("radial"):
         ach = flops / per_launch_s
         r = dict(bound="mfma", achieved=ach / 1e12, peak=MFMA_F32_PEAK / 1e12, unit="TFLOP/s",
@@ -194,7 +215,6 @@ def roofline_for(kernel, per_launch_s, N, E, cfg, ctx, workload="medium", launch
                  frac=ach / HBM_PEAK, algorithmic_bytes_per_launch=nbytes,
                  vector_alu_frac=(flops / per_launch_s) / VALU_F32_PEAK)
     r["kernel"] = kernel
-    # the committed counters were taken on the default (separate-path) layout
     # the committed counters were taken on the default configuration: the
     # separate-path layout and the default radial kernels
     other = cfg.get("sum_paths") or (cfg.get("_radial_variant") and kernel.startswith(("radial", "table")))

@@ -101,3 +101,25 @@ def test_profile_summary_reads_kernel_traces(tmp_path, capsys):
     text = capsys.readouterr().out
     assert "| `k_tp_fwd<float, 2>` | 2 | 5.600 | 11.20 |" in text
     assert "k_bin" not in text          # under 0.1 ms in total
+
+
+def test_fused_forward_roofline_names_its_largest_bound():
+    c = workloads.config(3)
+    ctx = tpc.Context(tpc.spec_for(c, fuse_radial=True))
+    N, E = 32768, 2_934_240
+    H, PC = c["hidden"][0], ctx.r_width
+    fwd_only = dict(c, _store_R=False)
+    r = bench.roofline_for("tp_fwd_fused", 6e-3, N, E, fwd_only, ctx)
+    # without R stores the vector ALUs take longest at their peak: the bound is
+    # "alu", measured on the vector flops alone (the matrix flops of the radial
+    # last layer are not counted against the vector peak)
+    assert r["bound"] == "alu" and r["unit"] == "TFLOP/s"
+    nbytes, flops = bench.algorithmic("tp_fwd_fused", N, E, fwd_only, ctx)
+    vec = flops - E * 2 * H * PC
+    assert r["frac"] == pytest.approx(vec / 6e-3 / bench.VALU_F32_PEAK)
+    assert r["matrix_frac"] == pytest.approx(6 * E * 2 * H * PC / bench.MFMA_BF16_PEAK / 6e-3)
+    assert r["hbm_frac"] == pytest.approx(nbytes / bench.HBM_PEAK / 6e-3)
+    # storing R for the backward adds 8.7 KB per edge: HBM becomes the bound
+    r2 = bench.roofline_for("tp_fwd_fused", 15e-3, N, E, dict(c, _store_R=True), ctx)
+    assert r2["bound"] == "hbm" and r2["unit"] == "GB/s"
+    assert max(r2["hbm_frac"], r2["vector_alu_frac"], r2["matrix_frac"]) == r2["frac"]
