@@ -94,7 +94,8 @@ def test_large_parity_sampled_chunked():
     case = Case(4)
     nl = case.nbr()
     rows, edges = _samples(case, 40, 12)
-    res = run_chunked(case, nl, chunks=3, keep_edges=edges)
+    # the 4 receiver chunks bench.py times
+    res = run_chunked(case, nl, chunks=4, keep_edges=edges)
     _sampled_check(case, nl, res, rows, _spread(rows, 24), edges)
 
 
@@ -105,6 +106,39 @@ def test_chunked_equals_unchunked():
     b = run_chunked(case, nl, chunks=5)
     for key in ("out", "dh", "forces", "g_edge"):
         assert torch().equal(a[key], b[key]), key
+
+
+def test_chunked_dh_over_chunks_without_edges():
+    """dh continues over every chunk's call: chunks that hold no edges (an
+    isolated atom) still carry the running sums through, and the chunk of the
+    last row scales them; the result equals the single call bit for bit."""
+    t = torch()
+    case = Case(0)
+    ctx = case.ctx
+    pos = t.tensor([[1.0, 1.0, 1.0], [1.5, 1.0, 1.0], [7.0, 7.0, 7.0], [1.0, 1.8, 1.0]], dtype=t.float64,
+                   device="cuda")
+    cell = np.eye(3) * 20.0
+    nl = ctx.nbr_build(pos, cell)
+    rp = nl.row_ptr.cpu().tolist()
+    assert rp[3] == rp[2]    # atom 2 has no neighbours
+    h = case.h[:4].contiguous()
+    G = case.G[:4].contiguous()
+    out, eb = ctx.conv_fwd(pos, cell, nl, h, case.W, 0.5)
+    dh_ref, _, F_ref, _ = ctx.conv_bwd(nl, h, case.W, 0.5, G, eb)
+    dh = t.full_like(h, float("nan"))       # every entry must be written
+    g_edge = t.empty((nl.n_edges, 3), dtype=ctx.dtype, device="cuda")
+    for a, b in [(0, 1), (1, 2), (2, 3), (3, 4)]:
+        e0, e1 = rp[a], rp[b]
+        ebc = ctx.alloc_edge_buffers(max(e1 - e0, 1), "cuda")
+        ctx.conv_fwd(pos, cell, nl, h, case.W, 0.5, out=t.empty_like(out), eb=ebc, rows=(a, b), edges=(e0, e1))
+        _, _, F, _ = ctx.conv_bwd(nl, h, case.W, 0.5, G, ebc, dh=dh, g_edge=g_edge, want_forces=b == 4)
+    t.cuda.synchronize()
+    assert t.equal(dh, dh_ref) and t.equal(F, F_ref)
+    prob = conv.Problem(case.layout, pos.cpu().numpy(), cell, *np_csr(nl)[:3], case.d["h"][:4], case.d["W"],
+                        case.cfg["r_cut"], 0.5, case.d["G"][:4])
+    b = prob.backward()
+    assert rel(dh.cpu().numpy(), b["dh"]) < 1e-10
+    assert rel(F.cpu().numpy(), b["F"]) < 1e-10
 
 
 def test_bitwise_deterministic():
