@@ -881,8 +881,11 @@ k_radial_bwd_dA_x6(int64_t ne, int pc, const float* __restrict__ dR, const __bf1
 }
 
 // backward, part 2: recompute the hidden layers, then d(ef) from dA3.
+// Float32 asks for two waves per SIMD (at most 256 registers): left free, the
+// compiler gave the two-hidden-layer network 260 (accumulator copies) and so
+// one wave per SIMD; bounded, it takes 156 with no spills.
 template <typename T, int H, int NH, int S>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, sizeof(T) == 4 ? 2 : 1)
 k_radial_bwd_mlp(int64_t ne, const T* __restrict__ ef, const T* __restrict__ dA3,
                  const T* __restrict__ pk, RadialPack L, T* __restrict__ d_ef) {
   constexpr int NB = H / 16, S4 = 4 * NB;
