@@ -423,7 +423,7 @@ __device__ __forceinline__ void tp_bwd_edge_group(const int32_t* __restrict__ sr
                                                   int64_t edge_begin, int64_t n_chunk_edges, int CC, uint32_t c0,
                                                   bool on, int part, T scale, const T* __restrict__ h,
                                                   const T* __restrict__ Y, const T* __restrict__ R,
-                                                  const T* __restrict__ G_, T* __restrict__ dR,
+                                                  const T* __restrict__ Gr, T* __restrict__ dR,
                                                   T* __restrict__ dYp, T* __restrict__ dh_edge) {
   constexpr int NP = TBL.np, DIN = TBL.din, DSH = TBL.dsh, DOUT = TBL.dout;
   static_assert(DSH <= 16, "harmonics beyond l = 3");
@@ -434,7 +434,7 @@ __device__ __forceinline__ void tp_bwd_edge_group(const int32_t* __restrict__ sr
 
   T gi[DOUT];
   {
-    const T* __restrict__ gr = G_ + (int64_t)i * DOUT * CC;
+    const T* __restrict__ gr = Gr + (int64_t)i * DOUT * CC;
     static_for<DOUT>([&](auto oc) {
       constexpr int o = decltype(oc)::value;
       if constexpr (bwd_group_reads_row(TBL, BGR, G, o)) gi[o] = ldc<NWM>(gr, o * CC + c0, on);
@@ -554,7 +554,7 @@ template <typename T, int L1, int L2, int L3, bool SUM, bool MASKED, int NG, int
 __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
 k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, int64_t row_begin,
               int64_t row_end, int64_t edge_begin, int64_t n_chunk_edges, int C, T scale, const T* __restrict__ h,
-              const T* __restrict__ Y, const T* __restrict__ R, const T* __restrict__ G_, T* __restrict__ dR,
+              const T* __restrict__ Y, const T* __restrict__ R, const T* __restrict__ Gr, T* __restrict__ dR,
               T* __restrict__ dYp, T* __restrict__ dh_edge) {
   const int lane = threadIdx.x % kTPWave;
   const int64_t w = xcd_block() * kTPWavesPerBlock + threadIdx.x / kTPWave;
@@ -573,7 +573,7 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
     constexpr int G = decltype(gc)::value;
     if (g == G)
       tp_bwd_edge_group<T, L1, L2, L3, SUM, MASKED, NG, G>(src, i, e_lo, e_hi, edge_begin, n_chunk_edges, CC, c0,
-                                                           on, part, scale, h, Y, R, G_, dR, dYp, dh_edge);
+                                                           on, part, scale, h, Y, R, Gr, dR, dYp, dh_edge);
   });
 }
 
