@@ -99,3 +99,17 @@ def test_fused_forward_is_deterministic_and_chunk_invariant():
                      eb=ctx.alloc_edge_buffers(e1 - e0, "cuda", with_R=False))
     torch().cuda.synchronize()
     assert torch().equal(out_a, out_c)
+
+
+@pytest.mark.timeout(300)
+def test_fused_step_medium_sampled():
+    """The medium water system through the fused forward (R stored) and the
+    backward, in the launch configuration of the fused benchmark line: out,
+    dR and g_edge on sampled rows and edges, dh and forces on sampled atoms,
+    against the oracle."""
+    from test_gpu_conv import _sampled_check, _samples, _spread
+    case = _fused_case(3)
+    nl = case.nbr()
+    rows, edges = _samples(case, 64, 21)
+    res = run_chunked(case, nl, chunks=1, keep_edges=edges)
+    _sampled_check(case, nl, res, rows, _spread(rows, 24), edges)
