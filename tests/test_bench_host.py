@@ -123,3 +123,13 @@ def test_fused_forward_roofline_names_its_largest_bound():
     r2 = bench.roofline_for("tp_fwd_fused", 15e-3, N, E, dict(c, _store_R=True), ctx)
     assert r2["bound"] == "hbm" and r2["unit"] == "GB/s"
     assert max(r2["hbm_frac"], r2["vector_alu_frac"], r2["matrix_frac"]) == r2["frac"]
+
+
+def test_more_than_one_gpu_is_refused_before_any_work(capsys, monkeypatch):
+    # one GPU only: --gpus above 1 (or a launcher's WORLD_SIZE) ends at once
+    # with a message and a non-zero status, before torch or the library load
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU only" in capsys.readouterr().out
+    monkeypatch.setenv("WORLD_SIZE", "4")
+    assert bench.main([]) == 2
+    assert "WORLD_SIZE=4" in capsys.readouterr().out
