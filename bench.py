@@ -447,6 +447,10 @@ def main(argv=None):
                     help="the forward forms R inside the tensor-product kernel (spec.fuse_radial)")
     ap.add_argument("--fp32-mfma-only", action="store_true",
                     help="float32 radial products on float32 matrix cores only (no bf16 split)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step with its convolution calls replayed from one captured HIP graph "
+                         "(the neighbour build, which waits for its edge count, stays eager) even with "
+                         "--no-extras; the default run reports it among the extras")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, copy %d bytes device to device three times "
@@ -533,8 +537,10 @@ def main(argv=None):
     ws_f = ctx._workspace(ctx.workspace_bytes(tpc.OP_FWD, N, max_e), dev)
     ws_b = ctx._workspace(ctx.workspace_bytes(tpc.OP_BWD, N, max_e), dev)
 
-    def step():
-        nl2 = ctx.nbr_build(pos, cell, species, edge_cap=E, into=nl, workspace=ws_n)
+    def step_nbr():
+        return ctx.nbr_build(pos, cell, species, edge_cap=E, into=nl, workspace=ws_n)
+
+    def step_conv(nl2):
         for q, (r0, r1, e0, e1) in enumerate(bounds):
             ctx.conv_fwd(pos, cell, nl2, h, W, scale, out=out, eb=eb, rows=(r0, r1), edges=(e0, e1),
                          workspace=ws_f)
@@ -543,6 +549,9 @@ def main(argv=None):
             last = q == len(bounds) - 1
             ctx.conv_bwd(nl2, h, W, scale, G, eb, dh=dh, dR=dR, g_edge=g_edge, dh_edge=dh_edge,
                          forces=forces if last else None, want_forces=last, workspace=ws_b)
+
+    def step():
+        step_conv(step_nbr())
 
     for _ in range(a.warmup):
         step()
@@ -585,6 +594,13 @@ def main(argv=None):
         del ws_v
         if chunks == 1 and not cfg.get("sum_paths") and not table:
             extras["double_backward"] = time_double_backward(tpc, ctx, nl, h, G, eb, scale, N, E, cfg, a.steps)
+
+    if a.graph or not a.no_extras:
+        try:
+            extras["graph_replay"] = time_graph_replay(torch, step_nbr, step_conv, a.steps, E)
+        except RuntimeError as exc:   # reported, not fatal: the eager step above is the measurement
+            torch.cuda.synchronize()
+            extras["graph_replay"] = {"error": str(exc)[:200]}
 
     # one launch of each per pass (the weight packing runs once in each pass)
     fwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0)
@@ -655,6 +671,37 @@ def main(argv=None):
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def time_graph_replay(torch, step_nbr, step_conv, steps, E):
+    """The step with its convolution calls captured once in a HIP graph and
+    replayed: the same kernels on the same buffers, launched by one graph
+    launch instead of one host call each.  The neighbour build stays eager
+    (it waits for its edge count)."""
+    nl = step_nbr()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step_conv(nl)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step_conv(nl)
+    for _ in range(2):
+        step_nbr()
+        g.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step_nbr()
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    del g
+    return {"ms_per_step": ms, "edges_per_s": E / (ms * 1e-3)}
 
 
 def time_double_backward(tpc, ctx, nl, h, G, eb, scale, N, E, cfg, steps):
