@@ -8,7 +8,7 @@ forces).  The default workload is the medium water system (32,768 atoms,
 C = 128, node irreps 0e+1o+2e, harmonics l <= 3, outputs l <= 3, radial MLP
 8-64-64-64-2176, about 2.93 M directed edges).  The small system (4,096
 atoms, C = 128) and the large fcc system (262,144 atoms, C = 64, about
-19.8 M edges, processed in 4 receiver chunks) are the other lines.  Inputs
+19.8 M edges, processed in 2 receiver chunks) are the other lines.  Inputs
 are resident in HBM before timing starts.  The metric is directed edges per
 second through the step.
 
@@ -165,7 +165,7 @@ def group_rooflines(per_kernel, N, E, cfg, ctx):
     return out
 
 
-def roofline_for(kernel, per_launch_s, N, E, cfg, ctx, workload="medium", launches=1):
+def roofline_for(kernel, per_launch_s, N, E, cfg, ctx, workload="medium", launches=1, chunks=None):
     """Roofline of one launch: ``per_launch_s`` its mean duration; the step's
     algorithmic bytes and flops (all E edges) are split evenly over the
     ``launches`` launches of a step (equal-edge receiver chunks)."""
@@ -218,7 +218,7 @@ def roofline_for(kernel, per_launch_s, N, E, cfg, ctx, workload="medium", launch
     # the committed counters were taken on the default configuration: the
     # separate-path layout and the default radial kernels
     other = cfg.get("sum_paths") or (cfg.get("_radial_variant") and kernel.startswith(("radial", "table")))
-    t = None if other else measured_traffic(kernel, workload)
+    t = None if other else measured_traffic(kernel, workload, chunks)
     r["traffic"] = t
     r["launches_per_step"] = launches
     return r
@@ -228,14 +228,17 @@ def traffic_path(workload):
     return os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, workload, chunks=None):
     """HBM bytes per launch of ``kernel`` from the committed counters of this
-    workload, when they were taken on the current kernel sources."""
+    workload, when they were taken on the current kernel sources and (when
+    ``chunks`` is given) with the same number of receiver chunks."""
     path = traffic_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
+    if chunks is not None and t.get("_chunks") != chunks:
+        return None
     rec = t.get(kernel)
     if not rec or rec.get("source_hash") != source_hash(kernel):
         return None
@@ -327,12 +330,13 @@ def _per_dispatch(rows, counter):
     return acc
 
 
-def traffic_from(fetch_dir, write_dir, out_path):
+def traffic_from(fetch_dir, write_dir, out_path, chunks=None):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, both in KiB
     per dispatch) of ``bench.py --copy-probe`` into HBM bytes per launch of
     each kernel, each counter scaled by what it reads for a plain copy of
-    COPY_PROBE_BYTES (read once, written once)."""
-    out = {}
+    COPY_PROBE_BYTES (read once, written once).  ``chunks``: the receiver
+    chunks the counted runs used (per-launch bytes depend on it)."""
+    out = {"_chunks": chunks}
     per = {}
     for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         disp = _per_dispatch(_counter_rows(d), counter)
@@ -422,7 +426,9 @@ def cpu_baseline(case_data, budget_s=10.0, sample_rows=None):
 
 
 WORKLOADS = {"small": 1, "medium": 3, "large": 4}
-DEFAULT_CHUNKS = {"small": 1, "medium": 1, "large": 4}
+# the large system in the fewest receiver chunks whose per-edge buffers (R,
+# dR and the dh contributions: 16 KB per edge) fit beside the rest in 288 GB
+DEFAULT_CHUNKS = {"small": 1, "medium": 1, "large": 2}
 
 
 def main(argv=None):
@@ -465,7 +471,8 @@ def main(argv=None):
     if a.profile_summary:
         return profile_summary(a.profile_summary[0], a.profile_summary[1:])
     if a.traffic_from:
-        return traffic_from(a.traffic_from[0], a.traffic_from[1], traffic_path(a.workload))
+        return traffic_from(a.traffic_from[0], a.traffic_from[1], traffic_path(a.workload),
+                            a.chunks or DEFAULT_CHUNKS[a.workload])
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE={world}); "
@@ -615,10 +622,10 @@ def main(argv=None):
     # algorithmic bytes of a step over the kernel's time in the step: with
     # equal-edge chunks this is the per-launch ratio of every chunk
     roof = roofline_for(dominant, per_kernel[dominant]["avg_ms"] * 1e-3, N, E, cfg, ctx, a.workload,
-                        per_kernel[dominant]["launches_per_step"])
+                        per_kernel[dominant]["launches_per_step"], chunks)
     kernels = {}
     for n, v in per_kernel.items():
-        r = (roofline_for(n, v["avg_ms"] * 1e-3, N, E, cfg, ctx, a.workload, v["launches_per_step"])
+        r = (roofline_for(n, v["avg_ms"] * 1e-3, N, E, cfg, ctx, a.workload, v["launches_per_step"], chunks)
              if n in KERNEL_SOURCES else None)
         kernels[n] = dict(avg_ms=round(v["avg_ms"], 4), launches_per_step=v["launches_per_step"],
                           **({"bound": r["bound"], "frac": round(r["frac"], 4)} if r else {}))

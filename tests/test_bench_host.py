@@ -83,6 +83,10 @@ def test_traffic_calibration_from_counter_databases(tmp_path, monkeypatch):
     # the committed counters apply only while the kernel sources are unchanged
     monkeypatch.setattr(bench, "traffic_path", lambda w: str(out))
     assert bench.measured_traffic("tp_fwd", "medium") == pytest.approx(rec["hbm_bytes_per_launch"])
+    # counters taken in other receiver chunks do not apply either
+    assert bench.traffic_from(str(tmp_path / "f"), str(tmp_path / "w"), str(out), chunks=2) == 0
+    assert bench.measured_traffic("tp_fwd", "medium", chunks=2) == pytest.approx(rec["hbm_bytes_per_launch"])
+    assert bench.measured_traffic("tp_fwd", "medium", chunks=4) is None
     monkeypatch.setattr(bench, "source_hash", lambda k: "changed")
     assert bench.measured_traffic("tp_fwd", "medium") is None
 

@@ -94,8 +94,8 @@ def test_large_parity_sampled_chunked():
     case = Case(4)
     nl = case.nbr()
     rows, edges = _samples(case, 40, 12)
-    # the 4 receiver chunks bench.py times
-    res = run_chunked(case, nl, chunks=4, keep_edges=edges)
+    # the 2 receiver chunks bench.py times
+    res = run_chunked(case, nl, chunks=2, keep_edges=edges)
     _sampled_check(case, nl, res, rows, _spread(rows, 24), edges)
 
 
