@@ -120,7 +120,11 @@ def algorithmic(kernel, N, E, cfg, ctx):
         return (E * T * C * din + N * T * C * din + 4 * (N + 1), E * C * din)
     hidden = 2 * (8 * H + (NH - 1) * H * H)
     if kernel == "radial_fwd":
-        return E * (8 * T + T * PC), E * (hidden + 2 * H * PC)
+        # one row of R per distinct edge length: with rows shared by edge
+        # pairs, half the edges of a symmetric list (plus the pairs cut by a
+        # chunk boundary)
+        rows = cfg.get("_R_rows", E)
+        return rows * (8 * T + T * PC), rows * (hidden + 2 * H * PC)
     if kernel == "radial_bwd_dA":
         # reads dR, writes dA (H per edge)
         return E * (T * PC + T * H), E * 2 * H * PC
@@ -451,6 +455,9 @@ def main(argv=None):
                          "buffer is written)")
     ap.add_argument("--fuse-radial", action="store_true",
                     help="the forward forms R inside the tensor-product kernel (spec.fuse_radial)")
+    ap.add_argument("--per-edge-radial", action="store_true",
+                    help="one row of R per edge (spec.pair_radial off; by default an edge and its "
+                         "reverse share one row)")
     ap.add_argument("--fp32-mfma-only", action="store_true",
                     help="float32 radial products on float32 matrix cores only (no bf16 split)")
     ap.add_argument("--graph", action="store_true",
@@ -501,12 +508,12 @@ def main(argv=None):
     table = tuple(int(v) for v in a.radial_table.split(",")) if a.radial_table else None
     if table:
         cfg = dict(cfg, _table_degree=table[1])
-    if table or a.fp32_mfma_only or a.fuse_radial:
+    if table or a.fp32_mfma_only or a.fuse_radial or a.per_edge_radial:
         cfg = dict(cfg, _radial_variant=True)
     if a.forward_only:
         cfg = dict(cfg, _store_R=False)   # the fused forward then writes no R
     ctx = tpc.Context(tpc.spec_for(cfg, fp32_mfma_only=a.fp32_mfma_only, table=table,
-                                   fuse_radial=a.fuse_radial))
+                                   fuse_radial=a.fuse_radial, pair_radial=not a.per_edge_radial))
     pos = torch.from_numpy(d["pos"]).to(dev)
     species = torch.from_numpy(d["species"]).to(dev)
     h = torch.from_numpy(d["h"]).to(dev)
@@ -532,6 +539,17 @@ def main(argv=None):
     cuts = [0] + [int(np.searchsorted(rp, E * q // chunks)) for q in range(1, chunks)] + [N]
     bounds = [(r0, r1, int(rp[r0]), int(rp[r1])) for r0, r1 in zip(cuts[:-1], cuts[1:]) if r1 > r0]
     max_e = max(e1 - e0 for _, _, e0, e1 in bounds)
+    if ctx.pair_radial:
+        # rows of R the network writes: one per pair inside a chunk, one per
+        # edge whose reverse lies in another chunk (the library's own count
+        # is checked against this after the timed steps)
+        rev = nl.rev.cpu().numpy().astype(np.int64)
+        owners = 0
+        for _, _, e0, e1 in bounds:
+            idx = np.arange(e1 - e0)
+            r = rev[e0:e1] - e0
+            owners += int(((r < 0) | (r >= e1 - e0) | (idx < r)).sum())
+        cfg = dict(cfg, _R_rows=owners)
     out = torch.empty((N, ctx.d_out, cfg["C"]), dtype=ctx.dtype, device=dev)
     # a forward-only run of a fused context stores no R
     eb = ctx.alloc_edge_buffers(max_e, dev, with_R=not a.forward_only)
@@ -581,6 +599,12 @@ def main(argv=None):
 
     per_kernel = {n: dict(avg_ms=tot / cnt, launches_per_step=cnt / a.steps, ms_per_step=tot / a.steps)
                   for n, (tot, cnt) in kt.items()}
+    if ctx.pair_radial:
+        e0, e1 = bounds[-1][2], bounds[-1][3]
+        got = int(eb.Rrow[e1 - e0].item())
+        idx = np.arange(e1 - e0)
+        r = rev[e0:e1] - e0
+        assert got == int(((r < 0) | (r >= e1 - e0) | (idx < r)).sum()), "shared R row count"
 
     extras = {}
     if not a.no_extras and not a.forward_only:
@@ -611,7 +635,8 @@ def main(argv=None):
 
     # one launch of each per pass (the weight packing runs once in each pass)
     fwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0)
-                 for n in ("geom_fwd", "radial_fwd", "radial_act", "table_fwd", "tp_fwd", "tp_fwd_fused")) + \
+                 for n in ("geom_fwd", "pair_rows", "radial_fwd", "radial_act", "table_fwd", "tp_fwd",
+                           "tp_fwd_fused")) + \
         per_kernel.get("radial_pack", {}).get("ms_per_step", 0.0) / 2
     bwd_ms = sum(per_kernel.get(n, {}).get("ms_per_step", 0.0)
                  for n in ("tp_bwd_edge", "radial_bwd_dA", "radial_bwd_mlp", "table_bwd", "geom_bwd", "dh_gather",
@@ -662,7 +687,9 @@ def main(argv=None):
                                + (f", radial tables {table[0]}x{table[1]}" if table else "")
                                + (", float32 radial products on fp32 matrix cores" if a.fp32_mfma_only else "")
                                + (", radial last layer fused into the forward tensor product"
-                                  if ctx.fused_radial else ""),
+                                  if ctx.fused_radial else "")
+                               + (f", R rows shared by edge pairs ({cfg['_R_rows']} rows)"
+                                  if ctx.pair_radial else ""),
                    "n_atoms": N, "n_edges": E, "channels": cfg["C"], "paths": ctx.n_paths,
                    "chunks": len(bounds), "parallelism": "single GPU"},
         "roofline": roof,

@@ -146,6 +146,19 @@ typedef struct tpc_spec {
                                 on this GPU (its tensor product runs at two
                                 waves per SIMD) and is there for callers
                                 short of memory. */
+  int pair_radial;           /* 0 (default): one row of R per edge.  Nonzero,
+                                with the radial network unfused and no table:
+                                an edge and its reverse share one row of R.
+                                The radial weights depend on the edge length
+                                only (FlashCart section 2, distance-dependent
+                                path weights; FastMACE "Rewrites and
+                                precision options", "Radial network"), and
+                                the reverse of an edge has the negated vector
+                                and the same length bit for bit, so the
+                                network runs once per pair of the chunk and
+                                writes half the rows.  tpc_conv_fwd then
+                                needs rev and eb.Rrow; tpc_info.pair_radial
+                                says whether the mode is in effect. */
 } tpc_spec;
 
 typedef struct tpc_info {
@@ -170,13 +183,20 @@ typedef struct tpc_info {
   size_t table_bytes;        /* the radial table (0 without one) */
   size_t fwd_workspace_bytes_per_edge; /* ... plus this per chunk edge (a table
                                           context sorts the chunk's edges by
-                                          piece; 0 otherwise), up to 256 bytes
-                                          of rounding; tpc_workspace_query
-                                          gives the exact figure */
+                                          piece, a pair_radial context keeps
+                                          each row's basis values; 0
+                                          otherwise), up to 512 bytes of
+                                          rounding and, with pair_radial, 8
+                                          bytes per 4,096 edges of scan sums;
+                                          tpc_workspace_query gives the exact
+                                          figure */
   int fused_radial;          /* 1: tpc_conv_fwd forms R inside the tensor-
                                 product kernel (see spec.fuse_radial) */
   size_t act_bytes;          /* per edge: one row of tpc_edge_buffers.A (0
                                 when fused_radial is 0) */
+  int pair_radial;           /* 1: an edge and its reverse share one row of R
+                                (see spec.pair_radial); tpc_edge_buffers.Rrow
+                                is then required */
 } tpc_info;
 
 /* Per-edge buffers.  conv_fwd writes them for the edges of the rows it
@@ -190,11 +210,23 @@ typedef struct tpc_edge_buffers {
                                    tpc_conv_double_bwd read them.  With
                                    info.fused_radial the forward writes them
                                    only when R is non-null (a forward-only
-                                   caller passes null and no R is stored) */
+                                   caller passes null and no R is stored).
+                                   With info.pair_radial, row Rrow[k] holds
+                                   the weights of edge edge_begin + k, and
+                                   only the first Rrow[E_chunk] rows are
+                                   written */
   void* A;    /* [E_chunk][info.act_bytes] bytes: the radial network's last
                  hidden activations in the library's own layout (written by
                  tpc_conv_fwd when info.fused_radial; unused otherwise, may be
                  null) */
+  int32_t* Rrow; /* [E_chunk + 1] int32 with info.pair_radial (unused
+                    otherwise, may be null): written by tpc_conv_fwd, read by
+                    tpc_conv_bwd and tpc_conv_double_bwd.  Rrow[k] is the row
+                    of R that edge edge_begin + k reads; Rrow[E_chunk] the
+                    number of rows written.  An edge whose reverse lies in the
+                    chunk shares the row of the lower-indexed of the two; an
+                    edge whose reverse lies outside keeps a row of its own.
+                    Rows are numbered in chunk order (deterministic). */
 } tpc_edge_buffers;
 
 /* Create a context from a spec (host only; no device call).  Checks every
@@ -252,6 +284,13 @@ tpc_status tpc_nbr_build(const tpc_ctx* ctx, int64_t n_atoms, const double* pos,
  *             receiver-sorted: FastMACE's receiver-streaming kernels give wrong
  *             results on unsorted edges, so with spec.validate the CSR is
  *             checked and TPC_ERR_PRECONDITION returned)
+ *   rev       [n_edges] int32 from tpc_nbr_build, device: read with
+ *             info.pair_radial (entries [edge_begin, edge_end)), else unused
+ *             and may be null.  The forward trusts it: a reverse index that
+ *             is not an involution gives wrong rows of R but no access
+ *             outside R (tpc_conv_bwd with spec.validate checks it).  A chunk
+ *             holds at most 2^24 edges in this mode (else
+ *             TPC_ERR_UNSUPPORTED).
  *   h         [n_atoms][d_in][C], device
  *   weights   host array of n_layers device pointers, W_k [dims[k-1]][dims[k]]
  *             row-major, already scaled; no biases; SiLU after every layer but
@@ -260,11 +299,15 @@ tpc_status tpc_nbr_build(const tpc_ctx* ctx, int64_t n_atoms, const double* pos,
  *   out       [n_atoms][d_out][C], device; rows [row_begin,row_end) written
  *   eb        per-edge buffers written for the chunk: Y, ef and rv always;
  *             R unless info.fused_radial (then optional); A when
- *             info.fused_radial
+ *             info.fused_radial; Rrow when info.pair_radial
+ *   workspace with info.pair_radial it also holds the rows' basis values
+ *             (info.fwd_workspace_bytes_per_edge per chunk edge), so the
+ *             forward that allocates nothing below refuses pair contexts
+ *             whose chunk needs more than its fixed scratch
  */
 tpc_status tpc_conv_fwd(const tpc_ctx* ctx, int64_t n_atoms, const double* pos,
                         const double* cell, const int32_t* row_ptr, const int32_t* src,
-                        const int32_t* shift, int64_t row_begin, int64_t row_end,
+                        const int32_t* shift, const int32_t* rev, int64_t row_begin, int64_t row_end,
                         int64_t edge_begin, int64_t edge_end, const void* h,
                         const void* const* weights, double scale, void* out,
                         const tpc_edge_buffers* eb, void* workspace, size_t workspace_bytes,
@@ -285,7 +328,7 @@ tpc_status tpc_conv_fwd(const tpc_ctx* ctx, int64_t n_atoms, const double* pos,
  * tpc_conv_fwd. */
 tpc_status tpc_conv_fwd_noalloc(const tpc_ctx* ctx, int64_t n_atoms, const double* pos,
                                 const double* cell, const int32_t* row_ptr, const int32_t* src,
-                                const int32_t* shift, int64_t row_begin, int64_t row_end,
+                                const int32_t* shift, const int32_t* rev, int64_t row_begin, int64_t row_end,
                                 int64_t edge_begin, int64_t edge_end, const void* h,
                                 const void* const* weights, double scale, void* out,
                                 const tpc_edge_buffers* eb, void* stream);

@@ -47,7 +47,7 @@ class _Spec(ctypes.Structure):
                 ("n_layers", ctypes.c_int), ("layer_dims", ctypes.c_int * (TPC_MAX_LAYERS + 1)),
                 ("validate", ctypes.c_int), ("sum_paths", ctypes.c_int), ("fp32_mfma_only", ctypes.c_int),
                 ("radial_table_pieces", ctypes.c_int), ("radial_table_degree", ctypes.c_int),
-                ("fuse_radial", ctypes.c_int)]
+                ("fuse_radial", ctypes.c_int), ("pair_radial", ctypes.c_int)]
 
 
 class _Info(ctypes.Structure):
@@ -59,7 +59,8 @@ class _Info(ctypes.Structure):
                 ("bwd_workspace_bytes_per_edge", ctypes.c_size_t), ("dY_parts", ctypes.c_int),
                 ("dh_edge_bytes", ctypes.c_size_t), ("table_bytes", ctypes.c_size_t),
                 ("fwd_workspace_bytes_per_edge", ctypes.c_size_t),
-                ("fused_radial", ctypes.c_int), ("act_bytes", ctypes.c_size_t)]
+                ("fused_radial", ctypes.c_int), ("act_bytes", ctypes.c_size_t),
+                ("pair_radial", ctypes.c_int)]
 
 
 class _KernelTime(ctypes.Structure):
@@ -68,7 +69,7 @@ class _KernelTime(ctypes.Structure):
 
 class _EdgeBuffers(ctypes.Structure):
     _fields_ = [("Y", ctypes.c_void_p), ("ef", ctypes.c_void_p), ("rv", ctypes.c_void_p),
-                ("R", ctypes.c_void_p), ("A", ctypes.c_void_p)]
+                ("R", ctypes.c_void_p), ("A", ctypes.c_void_p), ("Rrow", ctypes.c_void_p)]
 
 
 _LIB = None
@@ -94,7 +95,7 @@ def library():
                                         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_size_t)]
     lib.tpc_nbr_build.argtypes = [_VP, _I64, _VP, ctypes.POINTER(ctypes.c_double), _VP, _I64,
                                   _VP, _VP, _VP, _VP, ctypes.POINTER(_I64), _VP, ctypes.c_size_t, _VP]
-    lib.tpc_conv_fwd.argtypes = [_VP, _I64, _VP, ctypes.POINTER(ctypes.c_double), _VP, _VP, _VP,
+    lib.tpc_conv_fwd.argtypes = [_VP, _I64, _VP, ctypes.POINTER(ctypes.c_double), _VP, _VP, _VP, _VP,
                                  _I64, _I64, _I64, _I64, _VP, ctypes.POINTER(_VP), ctypes.c_double,
                                  _VP, ctypes.POINTER(_EdgeBuffers), _VP, ctypes.c_size_t, _VP]
     lib.tpc_conv_bwd.argtypes = [_VP, _I64, _I64, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _VP,
@@ -180,6 +181,7 @@ class Spec:
     radial_table_pieces: int = 0
     radial_table_degree: int = 0
     fuse_radial: bool = False
+    pair_radial: bool = False
 
     def to_c(self):
         s = _Spec()
@@ -197,6 +199,7 @@ class Spec:
         s.radial_table_pieces = int(self.radial_table_pieces)
         s.radial_table_degree = int(self.radial_table_degree)
         s.fuse_radial = int(bool(self.fuse_radial))
+        s.pair_radial = int(bool(self.pair_radial))
         return s
 
 
@@ -216,13 +219,23 @@ class EdgeBuffers:
     rv: object
     R: object
     A: object = None       # uint8 [E, act_bytes] when the context fuses the radial last layer
+    Rrow: object = None    # int32 [E + 1] when an edge and its reverse share a row of R
     edge_begin: int = 0
     edge_end: int = 0
     row_begin: int = 0
     row_end: int = 0
 
     def to_c(self):
-        return _EdgeBuffers(_ptr(self.Y), _ptr(self.ef), _ptr(self.rv), _ptr(self.R), _ptr(self.A))
+        return _EdgeBuffers(_ptr(self.Y), _ptr(self.ef), _ptr(self.rv), _ptr(self.R), _ptr(self.A),
+                            _ptr(self.Rrow))
+
+    def R_per_edge(self):
+        """R with one row per edge of the chunk (rows gathered through Rrow
+        when an edge and its reverse share one)."""
+        if self.Rrow is None or self.R is None:
+            return self.R
+        ne = self.edge_end - self.edge_begin
+        return self.R.index_select(0, self.Rrow[:ne].long())
 
 
 class Context:
@@ -244,6 +257,7 @@ class Context:
             "bwd_workspace_bytes_per_edge", "dY_parts", "dh_edge_bytes", "table_bytes", "act_bytes",
             "fwd_workspace_bytes_per_edge")}
         self.fused_radial = bool(info.fused_radial)
+        self.pair_radial = bool(info.pair_radial)
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -319,7 +333,9 @@ class Context:
                            rv=t.empty((n_edges, 4), dtype=self.dtype, device=device),
                            R=(t.empty((n_edges, self.r_width), dtype=self.dtype, device=device)
                               if with_R or not self.fused_radial else None),
-                           A=t.empty((n_edges, act), dtype=t.uint8, device=device) if act else None)
+                           A=t.empty((n_edges, act), dtype=t.uint8, device=device) if act else None,
+                           Rrow=(t.empty(n_edges + 1, dtype=t.int32, device=device)
+                                 if self.pair_radial else None))
 
     def conv_fwd(self, pos, cell, nl: NeighbourList, h, W, scale=1.0, out=None, eb=None,
                  rows=None, edges=None, workspace=None):
@@ -338,7 +354,7 @@ class Context:
         ws = workspace if workspace is not None else \
             self._workspace(self.workspace_bytes(OP_FWD, N, ee - eb_), h.device)
         _check(library().tpc_conv_fwd(self._h, N, _ptr(pos), _cell_arg(cell), _ptr(nl.row_ptr),
-                                      _ptr(nl.src), _ptr(nl.shift), rb, re_, eb_, ee, _ptr(h), wp,
+                                      _ptr(nl.src), _ptr(nl.shift), _ptr(nl.rev), rb, re_, eb_, ee, _ptr(h), wp,
                                       float(scale), _ptr(out), ctypes.byref(ebc), _ptr(ws), ws.numel(),
                                       _stream()))
         return out, eb
@@ -472,7 +488,7 @@ def conv_bwd(ctx: Context, *a, **k):
     return ctx.conv_bwd(*a, **k)
 
 
-def spec_for(cfg, validate=False, fp32_mfma_only=False, table=None, fuse_radial=False):
+def spec_for(cfg, validate=False, fp32_mfma_only=False, table=None, fuse_radial=False, pair_radial=False):
     """Spec of a workload configuration dict (see ``workloads.config``);
     ``table`` = (pieces, degree) selects the radial tables."""
     return Spec(channels=cfg["C"], node_lmax=cfg["l1max"], sh_lmax=cfg["sh_lmax"],
@@ -480,4 +496,4 @@ def spec_for(cfg, validate=False, fp32_mfma_only=False, table=None, fuse_radial=
                 dtype=cfg["dtype"], validate=validate, sum_paths=bool(cfg.get("sum_paths", False)),
                 fp32_mfma_only=fp32_mfma_only,
                 radial_table_pieces=table[0] if table else 0, radial_table_degree=table[1] if table else 0,
-                fuse_radial=fuse_radial)
+                fuse_radial=fuse_radial, pair_radial=pair_radial)

@@ -26,7 +26,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtpconv.so")
 
 PLAIN_SOURCES = ["api.cpp", "nbr.hip", "scan.hip", "geom.hip", "radial.hip", "tp_dispatch.hip",
-                 "forces.hip", "noalloc.hip", "radial_table.hip"]
+                 "forces.hip", "noalloc.hip", "radial_table.hip", "pair.hip"]
 PER_CONFIG_SOURCES = ["tp_fwd.hip", "tp_bwd.hip", "tp_dbl.hip", "tp_fused.hip"]
 HEADERS = ["common.hpp", "kernels.hpp", "nbr.hpp", "tables.hpp", "tp_impl.hpp", "tp_config.hpp", "tp_fused.hpp"]
 

@@ -28,6 +28,7 @@ struct tpc_ctx {
   size_t tsize;  // bytes per feature value
   bool table;    // radial weights from a piecewise Chebyshev table
   bool fused;    // the forward forms R inside the tensor-product kernel
+  bool pair;     // an edge and its reverse share one row of R
 };
 
 namespace {
@@ -210,7 +211,7 @@ tpc::RadialPack pack_layout(const tpc_ctx* c) {
 }
 
 struct FwdWs {
-  size_t status, pack, tsort, total;
+  size_t status, pack, tsort, pair_part, ef_rows, total;
 };
 
 // ne: edges of the chunk (a table context sorts them by piece)
@@ -223,9 +224,17 @@ FwdWs fwd_layout(const tpc_ctx* c, int64_t ne) {
   if (!c->table) off += align_up(c->tsize * (size_t)pack_layout(c).total);
   w.tsort = off;
   if (c->table) off += align_up(sizeof(int32_t) * (size_t)tpc::table_sort_ints(c->spec.radial_table_pieces, ne));
+  // shared R rows: the scan's partial sums and the rows' basis values
+  w.pair_part = off;
+  if (c->pair) off += align_up(sizeof(int64_t) * (size_t)tpc::pair_partials_len(ne));
+  w.ef_rows = off;
+  if (c->pair) off += align_up(c->tsize * 8 * (size_t)ne);
   w.total = off;
   return w;
 }
+
+// Largest chunk whose shared-row map one scan can number (16 M edges).
+constexpr int64_t kPairMaxChunk = (int64_t)4096 * 4096;
 
 struct TableWs {
   size_t nodes, cert, total;
@@ -449,6 +458,7 @@ tpc_status tpc_ctx_create(const tpc_spec* spec, tpc_ctx** out) {
   c->tsize = s.dtype == TPC_F64 ? 8 : 4;
   c->table = s.radial_table_pieces > 0;
   c->fused = fused_radial_ok(s, tab, H);
+  c->pair = s.pair_radial != 0 && !c->fused && !c->table;
   *out = c;
   return TPC_OK;
 }
@@ -475,13 +485,14 @@ tpc_status tpc_ctx_info(const tpc_ctx* c, tpc_info* info) {
   info->bwd_workspace_bytes_per_edge =
       T * (size_t)(c->tab.dsh * dy_parts(c) + 8 + (c->table ? 0 : c->hidden)) +
       T * (size_t)c->tab.np * c->spec.channels + (c->table ? sizeof(int32_t) : 0);
-  info->fwd_workspace_bytes_per_edge = c->table ? sizeof(int32_t) : 0;
+  info->fwd_workspace_bytes_per_edge = c->table ? sizeof(int32_t) : c->pair ? c->tsize * 8 : 0;
   info->bwd_workspace_bytes_fixed = bwd_layout(c, 0).total;
   info->dY_parts = dy_parts(c);
   info->dh_edge_bytes = T * (size_t)c->tab.din * c->spec.channels;
   info->table_bytes = table_bytes(c);
   info->fused_radial = c->fused ? 1 : 0;
   info->act_bytes = c->fused ? (size_t)(c->hidden / 32) * 192 : 0;
+  info->pair_radial = c->pair ? 1 : 0;
   for (int p = 0; p < c->tab.np; ++p) {
     info->paths[p][0] = c->tab.path[p].l1;
     info->paths[p][1] = c->tab.path[p].l2;
@@ -706,7 +717,7 @@ tpc_status run_csr_check(int64_t n, int64_t n_edges, const int32_t* row_ptr, con
 
 tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const double* cell,
                         const int32_t* row_ptr, const int32_t* src, const int32_t* shift,
-                        int64_t row_begin, int64_t row_end, int64_t edge_begin, int64_t edge_end,
+                        const int32_t* rev, int64_t row_begin, int64_t row_end, int64_t edge_begin, int64_t edge_end,
                         const void* h, const void* const* weights, double scale, void* out,
                         const tpc_edge_buffers* eb, void* ws, size_t ws_bytes, void* stream) {
   Errors E;
@@ -739,6 +750,13 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
       if (eb->R && !aligned(eb->R, va)) E.add(TPC_ERR_INVALID, "eb.R must be %zu-byte aligned", va);
     } else {
       need_ptr(eb->R, "eb.R", va, E);
+    }
+    if (c->pair) {
+      need_ptr(rev, "rev", 4, E);
+      need_ptr(eb->Rrow, "eb.Rrow", 4, E);
+      if (edge_end - edge_begin > kPairMaxChunk)
+        E.add(TPC_ERR_UNSUPPORTED, "shared R rows (spec.pair_radial) take chunks of at most %lld edges",
+              (long long)kPairMaxChunk);
     }
   }
   check_weights(c, weights, E);
@@ -796,8 +814,19 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
       if (c->fused)
         TPC_LAUNCH("radial_act", s, tpc::launch_radial_act(PL, ne, eb->ef, pk, eb->A, s),
                    "conv_fwd: radial hidden layers");
-      else
-        TPC_LAUNCH("radial_fwd", s, tpc::launch_radial_fwd(dt, PL, ne, eb->ef, pk, eb->R, s),
+      else if (c->pair) {
+        // one row of R per edge pair of the chunk: number the rows, gather
+        // their basis values, and run the network on the rows only
+        void* ef_rows = static_cast<char*>(ws) + FL.ef_rows;
+        TPC_LAUNCH("pair_rows", s,
+                   tpc::launch_pair_rows(dt, rev, edge_begin, ne, eb->Rrow,
+                                         reinterpret_cast<int32_t*>(static_cast<char*>(ws) + FL.pair_part),
+                                         eb->ef, ef_rows, s),
+                   "conv_fwd: shared R rows");
+        TPC_LAUNCH("radial_fwd", s, tpc::launch_radial_fwd(dt, PL, ne, eb->Rrow + ne, ef_rows, pk, eb->R, s),
+                   "conv_fwd: radial MLP");
+      } else
+        TPC_LAUNCH("radial_fwd", s, tpc::launch_radial_fwd(dt, PL, ne, nullptr, eb->ef, pk, eb->R, s),
                    "conv_fwd: radial MLP");
     }
   }
@@ -813,6 +842,7 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
   ta.h = h;
   ta.Y = eb ? eb->Y : nullptr;
   ta.R = eb ? eb->R : nullptr;
+  ta.Rrow = eb && c->pair ? eb->Rrow : nullptr;
   ta.n_chunk_edges = edge_end - edge_begin;
   ta.out = out;
   // a chunk without edges has no packed weights (the workspace may be null):
@@ -837,7 +867,7 @@ tpc_status tpc_conv_fwd(const tpc_ctx* c, int64_t n, const double* pos, const do
 
 tpc_status tpc_conv_fwd_noalloc(const tpc_ctx* c, int64_t n, const double* pos, const double* cell,
                                 const int32_t* row_ptr, const int32_t* src, const int32_t* shift,
-                                int64_t row_begin, int64_t row_end, int64_t edge_begin, int64_t edge_end,
+                                const int32_t* rev, int64_t row_begin, int64_t row_end, int64_t edge_begin, int64_t edge_end,
                                 const void* h, const void* const* weights, double scale, void* out,
                                 const tpc_edge_buffers* eb, void* stream) {
   Errors E;
@@ -855,7 +885,7 @@ tpc_status tpc_conv_fwd_noalloc(const tpc_ctx* c, int64_t n, const double* pos, 
           need, cap);
     return E.finish();
   }
-  return tpc_conv_fwd(c, n, pos, cell, row_ptr, src, shift, row_begin, row_end, edge_begin, edge_end, h,
+  return tpc_conv_fwd(c, n, pos, cell, row_ptr, src, shift, rev, row_begin, row_end, edge_begin, edge_end, h,
                       weights, scale, out, eb, scratch, cap, stream);
 }
 
@@ -904,6 +934,7 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
     need_ptr(eb->ef, "eb.ef", va, E);
     need_ptr(eb->rv, "eb.rv", va, E);
     need_ptr(eb->R, "eb.R", va, E);
+    if (c->pair) need_ptr(eb->Rrow, "eb.Rrow", 4, E);
   }
   check_weights(c, weights, E);
   const int64_t ne = edge_end - edge_begin;
@@ -940,6 +971,7 @@ tpc_status tpc_conv_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, const int3
   ta.h = h;
   ta.Y = eb->Y;
   ta.R = eb->R;
+  ta.Rrow = c->pair ? eb->Rrow : nullptr;
   ta.n_chunk_edges = ne;
   ta.G = grad_out;
   ta.rev = rev;
@@ -1036,6 +1068,7 @@ tpc_status tpc_conv_double_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, con
   } else if (edge_end > edge_begin) {
     need_ptr(eb->Y, "eb.Y", va, E);
     need_ptr(eb->R, "eb.R", va, E);
+    if (c->pair) need_ptr(eb->Rrow, "eb.Rrow", 4, E);
   }
   const int64_t ne = edge_end - edge_begin;
   const DblWs L = dbl_layout(c, ne > 0 ? ne : 0);
@@ -1066,6 +1099,7 @@ tpc_status tpc_conv_double_bwd(const tpc_ctx* c, int64_t n, int64_t n_edges, con
   ta.h = h;
   ta.Y = eb->Y;
   ta.R = eb->R;
+  ta.Rrow = c->pair ? eb->Rrow : nullptr;
   ta.G = grad_out;
   ta.uh = u_dh;
   ta.uY = u_dY;

@@ -34,7 +34,9 @@ struct TPArgs {
   double scale;    // neighbour normalisation s
   const void* h;   // [N][d_in][C]
   const void* Y;   // [E][d_sh]
-  const void* R;   // [E][P*C]
+  const void* R;   // [E][P*C], or [rows][P*C] read through Rrow
+  const int32_t* Rrow;  // nullable: chunk-relative R row of each edge (shared
+                        // rows of edge pairs); null: row (edge - edge_begin)
   const void* G;   // [N][d_out][C]  (backward)
   void* out;       // forward: out [N][d_out][C]
   void* dR;        // backward edge kernel: [E][P*C]
@@ -122,8 +124,17 @@ inline int64_t radial_dA_elems(int H, int64_t ne) { return (ne + 15) / 16 * 16 *
 bool radial_supported(int H, int NH);
 hipError_t launch_radial_pack(int dtype, const RadialPack& L, const void* const* w, void* pk,
                               hipStream_t s);
-hipError_t launch_radial_fwd(int dtype, const RadialPack& L, int64_t ne, const void* ef,
-                             const void* pk, void* R, hipStream_t s);
+// ne_dev (nullable): the number of rows, read on the device when it is only
+// known there (at most ne, which sizes the grid).
+hipError_t launch_radial_fwd(int dtype, const RadialPack& L, int64_t ne, const int32_t* ne_dev,
+                             const void* ef, const void* pk, void* R, hipStream_t s);
+// Shared R rows of the chunk's edge pairs: rrow [ne + 1] (chunk-relative row
+// of each edge's R, rrow[ne] = number of rows), partials [pair_partials_len]
+// scratch, and each row's basis values copied from ef [ne][8] to
+// ef_rows [ne][8] (nullable: the map only).
+hipError_t launch_pair_rows(int dtype, const int32_t* rev, int64_t edge_begin, int64_t ne, int32_t* rrow,
+                            int32_t* partials, const void* ef, void* ef_rows, hipStream_t s);
+int64_t pair_partials_len(int64_t ne);
 // Last hidden activations, split for the fused forward (float32, H = 32 or 64):
 // act [ne][H / 32][4][3][8] bf16.
 hipError_t launch_radial_act(const RadialPack& L, int64_t ne, const void* ef, const void* pk, void* act,

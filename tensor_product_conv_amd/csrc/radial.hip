@@ -562,10 +562,18 @@ __device__ __forceinline__ void radial_last_pairs_x6(int64_t e0, int64_t ne, int
 // systems measured.
 template <typename T, int H, int NH, int S, bool VEC, bool PAIRS, bool X6>
 __global__ void __launch_bounds__(256, (sizeof(T) == 4 && X6 && H == 64) ? 3 : 1)
-k_radial_fwd(int64_t ne, int pc, const T* __restrict__ ef, const T* __restrict__ pk, RadialPack L,
-             T* __restrict__ R) {
+k_radial_fwd(int64_t ne, const int32_t* __restrict__ ne_dev, int pc, const T* __restrict__ ef,
+             const T* __restrict__ pk, RadialPack L, T* __restrict__ R) {
   constexpr int NB = H / 16, S4 = 4 * NB;
   const int lane = threadIdx.x % kWave;
+  // rows counted on the device (shared rows of edge pairs): the grid covers
+  // the largest count, and blocks past the actual one leave at once (every
+  // wave of such a block, so no barrier below waits for them)
+  if (ne_dev) {
+    const int64_t nd = __builtin_amdgcn_readfirstlane(*ne_dev);
+    ne = nd < ne ? nd : ne;
+    if (blockIdx.x * (int64_t)(blockDim.x / kWave) * (16 * S) >= ne) return;
+  }
   const int64_t e0 = (blockIdx.x * (int64_t)(blockDim.x / kWave) + threadIdx.x / kWave) * (16 * S);
   // the shared-weight path keeps waves without edges for its barriers
   constexpr bool kX6 = X6 && PAIRS && x6_shape(H, 32);
@@ -973,8 +981,8 @@ template <typename T>
 constexpr int kBwdStrips = std::is_same<T, float>::value ? 8 : 2;
 
 template <typename T, int H, int NH>
-hipError_t fwd_impl(int64_t ne, int pc, const T* ef, const T* pk, const RadialPack& L, T* R,
-                    hipStream_t s) {
+hipError_t fwd_impl(int64_t ne, const int32_t* ne_dev, int pc, const T* ef, const T* pk, const RadialPack& L,
+                    T* R, hipStream_t s) {
   const int64_t per_block = 4 * 16 * kFwdStrips;
   const unsigned blocks = (unsigned)((ne + per_block - 1) / per_block);
   const bool vec = std::is_same<T, float>::value && pc % 16 == 0 &&
@@ -982,16 +990,16 @@ hipError_t fwd_impl(int64_t ne, int pc, const T* ef, const T* pk, const RadialPa
   if constexpr (std::is_same<T, float>::value) {
     if (vec && pc % 32 == 0) {
       if (L.x6)
-        k_radial_fwd<T, H, NH, kFwdStrips, true, true, true><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
+        k_radial_fwd<T, H, NH, kFwdStrips, true, true, true><<<blocks, 256, 0, s>>>(ne, ne_dev, pc, ef, pk, L, R);
       else
-        k_radial_fwd<T, H, NH, kFwdStrips, true, true, false><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
+        k_radial_fwd<T, H, NH, kFwdStrips, true, true, false><<<blocks, 256, 0, s>>>(ne, ne_dev, pc, ef, pk, L, R);
       return hipGetLastError();
     }
   }
   if (vec)
-    k_radial_fwd<T, H, NH, kFwdStrips, true, false, false><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
+    k_radial_fwd<T, H, NH, kFwdStrips, true, false, false><<<blocks, 256, 0, s>>>(ne, ne_dev, pc, ef, pk, L, R);
   else
-    k_radial_fwd<T, H, NH, kFwdStrips, false, false, false><<<blocks, 256, 0, s>>>(ne, pc, ef, pk, L, R);
+    k_radial_fwd<T, H, NH, kFwdStrips, false, false, false><<<blocks, 256, 0, s>>>(ne, ne_dev, pc, ef, pk, L, R);
   return hipGetLastError();
 }
 
@@ -1033,11 +1041,11 @@ hipError_t bwd_mlp_impl(int64_t ne, const T* ef, const T* dA3, const T* pk, cons
 #define TPC_RADIAL_SHAPES(X) X(16, 1) X(16, 2) X(16, 3) X(32, 1) X(32, 2) X(32, 3) X(64, 1) X(64, 2) X(64, 3)
 
 template <typename T>
-hipError_t fwd_dispatch(const RadialPack& L, int64_t ne, const void* ef, const void* pk, void* R,
-                        hipStream_t s) {
-#define TPC_CASE(HH, NN)                                                                       \
-  if (L.H == HH && L.NH == NN)                                                                 \
-    return fwd_impl<T, HH, NN>(ne, L.pc, static_cast<const T*>(ef), static_cast<const T*>(pk), L, \
+hipError_t fwd_dispatch(const RadialPack& L, int64_t ne, const int32_t* ne_dev, const void* ef, const void* pk,
+                        void* R, hipStream_t s) {
+#define TPC_CASE(HH, NN)                                                                              \
+  if (L.H == HH && L.NH == NN)                                                                        \
+    return fwd_impl<T, HH, NN>(ne, ne_dev, L.pc, static_cast<const T*>(ef), static_cast<const T*>(pk), L, \
                                static_cast<T*>(R), s);
   TPC_RADIAL_SHAPES(TPC_CASE)
 #undef TPC_CASE
@@ -1095,10 +1103,11 @@ hipError_t launch_radial_pack(int dtype, const RadialPack& L, const void* const*
   return dtype == 1 ? pack_impl<double>(L, w, pk, s) : pack_impl<float>(L, w, pk, s);
 }
 
-hipError_t launch_radial_fwd(int dtype, const RadialPack& L, int64_t ne, const void* ef,
-                             const void* pk, void* R, hipStream_t s) {
+hipError_t launch_radial_fwd(int dtype, const RadialPack& L, int64_t ne, const int32_t* ne_dev,
+                             const void* ef, const void* pk, void* R, hipStream_t s) {
   if (ne <= 0) return hipSuccess;
-  return dtype == 1 ? fwd_dispatch<double>(L, ne, ef, pk, R, s) : fwd_dispatch<float>(L, ne, ef, pk, R, s);
+  return dtype == 1 ? fwd_dispatch<double>(L, ne, ne_dev, ef, pk, R, s)
+                    : fwd_dispatch<float>(L, ne, ne_dev, ef, pk, R, s);
 }
 
 hipError_t launch_radial_act(const RadialPack& L, int64_t ne, const void* ef, const void* pk, void* act,

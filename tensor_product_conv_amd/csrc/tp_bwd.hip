@@ -18,7 +18,7 @@ hipError_t bwd_launch(const TPArgs& a, hipStream_t s) {
       <<<(unsigned)((waves + kTPWavesPerBlock - 1) / kTPWavesPerBlock), kTPWave * kTPWavesPerBlock, 0, s>>>(
           a.row_ptr, a.src, a.row_begin, a.row_end, a.edge_begin, a.n_chunk_edges, a.C, (T)a.scale,
           static_cast<const T*>(a.h), static_cast<const T*>(a.Y), static_cast<const T*>(a.R),
-          static_cast<const T*>(a.G), static_cast<T*>(a.dR), static_cast<T*>(a.dY), static_cast<T*>(a.dh_edge));
+          a.Rrow, static_cast<const T*>(a.G), static_cast<T*>(a.dR), static_cast<T*>(a.dY), static_cast<T*>(a.dh_edge));
   return hipGetLastError();
 }
 

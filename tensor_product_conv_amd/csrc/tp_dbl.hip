@@ -22,13 +22,13 @@ hipError_t tp_dbl_cfg(const TPArgs& a, hipStream_t s) {
     k_tp_dbl_recv<T, L1, L2, L3, NG, MASK, NWC><<<blocks, kTPWave * kTPWavesPerBlock, 0, s>>>(    \
         a.row_ptr, a.src, a.row_begin, a.row_end, a.edge_begin, a.n_chunk_edges, a.C, sc,        \
         static_cast<const T*>(a.h), static_cast<const T*>(a.uh), static_cast<const T*>(a.Y),     \
-        static_cast<const T*>(a.uY), static_cast<const T*>(a.R), static_cast<const T*>(a.uR),    \
-        static_cast<const T*>(a.G), static_cast<T*>(a.g_hat), static_cast<T*>(a.w_hat),          \
+        static_cast<const T*>(a.uY), static_cast<const T*>(a.R), a.Rrow,                         \
+        static_cast<const T*>(a.uR), static_cast<const T*>(a.G), static_cast<T*>(a.g_hat), static_cast<T*>(a.w_hat),          \
         static_cast<T*>(a.dY));                                                                   \
     k_tp_dbl_send<T, L1, L2, L3, NG, MASK, NWC><<<blocks, kTPWave * kTPWavesPerBlock, 0, s>>>(    \
         a.row_ptr, a.src, a.rev, a.row_begin, a.row_end, a.edge_begin, a.C, sc,                  \
         static_cast<const T*>(a.Y), static_cast<const T*>(a.uY), static_cast<const T*>(a.R),     \
-        static_cast<const T*>(a.uR), static_cast<const T*>(a.G), static_cast<T*>(a.x_hat));      \
+        a.Rrow, static_cast<const T*>(a.uR), static_cast<const T*>(a.G), static_cast<T*>(a.x_hat));      \
   } while (0)
   if (a.C < 64) {
     TPC_GO(true, 1);

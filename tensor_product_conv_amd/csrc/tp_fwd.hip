@@ -30,7 +30,7 @@ hipError_t fwd_launch(const TPArgs& a, hipStream_t s) {
   k_tp_fwd<T, L1, L2, L3, SUM, 1, NG, MASK, NWC>                                                \
       <<<(unsigned)((rows * NG * NWC + kTPWavesPerBlock - 1) / kTPWavesPerBlock),               \
          kTPWave * kTPWavesPerBlock, 0, s>>>(a.row_ptr, a.src, a.row_begin, a.row_end,           \
-                                             a.edge_begin, a.C, sc, h, Y, R, out)
+                                             a.edge_begin, a.C, sc, h, Y, R, a.Rrow, out)
   if (masked) {
     TPC_GO(1, true, 1);
   } else if (a.C == 128) {

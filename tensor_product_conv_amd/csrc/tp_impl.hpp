@@ -98,6 +98,16 @@ struct RowIdx {
 #pragma unroll
     for (int q = 0; q < NWIN; ++q) v[q] = a[min(e_lo + 64 * q + lane, e_hi - 1)];
   }
+  // R rows of the row's edges: map[e - edge_begin] (shared rows of edge
+  // pairs), or e - edge_begin without a map
+  __device__ __forceinline__ void init_rows(const int32_t* __restrict__ map, int64_t edge_begin, int e_lo,
+                                            int e_hi, int lane) {
+#pragma unroll
+    for (int q = 0; q < NWIN; ++q) {
+      const int e = min(e_lo + 64 * q + lane, e_hi - 1);
+      v[q] = map ? map[e - edge_begin] : (int)(e - edge_begin);
+    }
+  }
   // entry of edge e_lo + k (k uniform, 0 <= k < 64 * NWIN)
   __device__ __forceinline__ int get(int k) const {
     int r = __builtin_amdgcn_readlane(v[0], k & 63);
@@ -109,6 +119,12 @@ struct RowIdx {
     return r;
   }
 };
+
+// Chunk-relative R row of edge e (a scalar load with a map), for rows too
+// long for the index windows.
+__device__ __forceinline__ int r_row(const int32_t* __restrict__ map, int64_t edge_begin, int e) {
+  return map ? uniform(map[e - edge_begin]) : (int)(e - edge_begin);
+}
 
 // compute(e, buf) over the edges [e_lo, e_hi) (non-empty) in order, with the
 // next edge's loads in flight in a second buffer.  Every prefetch is
@@ -220,7 +236,8 @@ template <typename T, int L1, int L2, int L3, bool SUM, int CPL, int NG, bool MA
 __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, int e_lo, int e_hi,
                                              int64_t edge_begin, int C, uint32_t c0, bool on,
                                              const T* __restrict__ h, const T* __restrict__ Y,
-                                             const T* __restrict__ R, T* __restrict__ oi, T scale) {
+                                             const T* __restrict__ R, const int32_t* __restrict__ Rrow,
+                                             T* __restrict__ oi, T scale) {
   constexpr int NP = kTable<L1, L2, L3, SUM>.np, DIN = kTable<L1, L2, L3, SUM>.din;
   constexpr int DSH = kTable<L1, L2, L3, SUM>.dsh, DOUT = kTable<L1, L2, L3, SUM>.dout;
   const int PC = NP * C;
@@ -245,9 +262,9 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
   };
   const int lane = threadIdx.x % kTPWave;
   const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
-  auto load_j = [&](int e, int j, Buf& b) __attribute__((always_inline)) {
+  auto load_j = [&](int e, int j, int rr, Buf& b) __attribute__((always_inline)) {
     const T* __restrict__ hj = h + (int64_t)j * DIN * C;
-    const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
+    const T* __restrict__ re = R + (int64_t)rr * PC;
     // only the rows of the l1 ranks this group's paths read
     static_for<DIN>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
@@ -268,11 +285,20 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
     tp_fwd_edge<T, L1, L2, L3, SUM, CPL, NG, G>(b.h, b.r, ye, acc);
   };
   if (e_hi - e_lo > 64 * kIdxWindows) {
-    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, uniform(src[e]), b); }, compute);
+    edge_loop<Buf>(e_lo, e_hi,
+                   [&](int e, Buf& b) __attribute__((always_inline)) {
+                     load_j(e, uniform(src[e]), r_row(Rrow, edge_begin, e), b);
+                   },
+                   compute);
   } else if (e_hi > e_lo) {
-    RowIdx<kIdxWindows> si;
+    RowIdx<kIdxWindows> si, qi;
     si.init(src, e_lo, e_hi, lane);
-    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, si.get(e - e_lo), b); }, compute);
+    qi.init_rows(Rrow, edge_begin, e_lo, e_hi, lane);
+    edge_loop<Buf>(e_lo, e_hi,
+                   [&](int e, Buf& b) __attribute__((always_inline)) {
+                     load_j(e, si.get(e - e_lo), qi.get(e - e_lo), b);
+                   },
+                   compute);
   }
   static_for<NP>([&](auto pc) {
     constexpr int p = decltype(pc)::value;
@@ -293,7 +319,8 @@ template <typename T, int L1, int L2, int L3, bool SUM, int CPL, int NG, bool MA
 __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
 k_tp_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, int64_t row_begin,
          int64_t row_end, int64_t edge_begin, int C, T scale, const T* __restrict__ h,
-         const T* __restrict__ Y, const T* __restrict__ R, T* __restrict__ out) {
+         const T* __restrict__ Y, const T* __restrict__ R, const int32_t* __restrict__ Rrow,
+         T* __restrict__ out) {
   constexpr int DOUT = kTable<L1, L2, L3, SUM>.dout;
   const int lane = threadIdx.x % kTPWave;
   const int64_t w = xcd_block() * kTPWavesPerBlock + threadIdx.x / kTPWave;
@@ -311,7 +338,7 @@ k_tp_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, i
     constexpr int G = decltype(gc)::value;
     if (g == G)
       tp_fwd_group<T, L1, L2, L3, SUM, CPL, NG, MASKED, G>(src, e_lo, e_hi, edge_begin, CC, c0, on, h, Y,
-                                                     R, oi, scale);
+                                                     R, Rrow, oi, scale);
   });
 }
 
@@ -423,6 +450,7 @@ __device__ __forceinline__ void tp_bwd_edge_group(const int32_t* __restrict__ sr
                                                   int64_t edge_begin, int64_t n_chunk_edges, int CC, uint32_t c0,
                                                   bool on, int part, T scale, const T* __restrict__ h,
                                                   const T* __restrict__ Y, const T* __restrict__ R,
+                                                  const int32_t* __restrict__ Rrow,
                                                   const T* __restrict__ Gr, T* __restrict__ dR,
                                                   T* __restrict__ dYp, T* __restrict__ dh_edge) {
   constexpr int NP = TBL.np, DIN = TBL.din, DSH = TBL.dsh, DOUT = TBL.dout;
@@ -451,9 +479,9 @@ __device__ __forceinline__ void tp_bwd_edge_group(const int32_t* __restrict__ sr
     T y;
   };
   const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
-  auto load_j = [&](int e, int j, Buf& b) __attribute__((always_inline)) {
+  auto load_j = [&](int e, int j, int rr, Buf& b) __attribute__((always_inline)) {
     const T* __restrict__ hj = h + (int64_t)j * DIN * CC;
-    const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
+    const T* __restrict__ re = R + (int64_t)rr * PC;
     static_for<DIN>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
       constexpr int l1 = m >= 9 ? 3 : m >= 4 ? 2 : m >= 1 ? 1 : 0;
@@ -536,13 +564,20 @@ __device__ __forceinline__ void tp_bwd_edge_group(const int32_t* __restrict__ sr
       dYp[((int64_t)part * n_chunk_edges + el) * DSH + (lane >> 2)] = scale * tot;
   };
   if (e_hi - e_lo > 64 * kIdxWindows) {
-    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, uniform(src[e]), b); },
+    edge_loop<Buf>(e_lo, e_hi,
+                   [&](int e, Buf& b) __attribute__((always_inline)) {
+                     load_j(e, uniform(src[e]), r_row(Rrow, edge_begin, e), b);
+                   },
                    compute);
   } else {
-    RowIdx<kIdxWindows> si;
+    RowIdx<kIdxWindows> si, qi;
     si.init(src, e_lo, e_hi, lane);
+    qi.init_rows(Rrow, edge_begin, e_lo, e_hi, lane);
     edge_loop<Buf>(e_lo, e_hi,
-                   [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, si.get(e - e_lo), b); }, compute);
+                   [&](int e, Buf& b) __attribute__((always_inline)) {
+                     load_j(e, si.get(e - e_lo), qi.get(e - e_lo), b);
+                   },
+                   compute);
   }
 }
 #undef TBL
@@ -554,7 +589,8 @@ template <typename T, int L1, int L2, int L3, bool SUM, bool MASKED, int NG, int
 __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
 k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, int64_t row_begin,
               int64_t row_end, int64_t edge_begin, int64_t n_chunk_edges, int C, T scale, const T* __restrict__ h,
-              const T* __restrict__ Y, const T* __restrict__ R, const T* __restrict__ Gr, T* __restrict__ dR,
+              const T* __restrict__ Y, const T* __restrict__ R, const int32_t* __restrict__ Rrow,
+              const T* __restrict__ Gr, T* __restrict__ dR,
               T* __restrict__ dYp, T* __restrict__ dh_edge) {
   const int lane = threadIdx.x % kTPWave;
   const int64_t w = xcd_block() * kTPWavesPerBlock + threadIdx.x / kTPWave;
@@ -573,7 +609,7 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
     constexpr int G = decltype(gc)::value;
     if (g == G)
       tp_bwd_edge_group<T, L1, L2, L3, SUM, MASKED, NG, G>(src, i, e_lo, e_hi, edge_begin, n_chunk_edges, CC, c0,
-                                                           on, part, scale, h, Y, R, Gr, dR, dYp, dh_edge);
+                                                           on, part, scale, h, Y, R, Rrow, Gr, dR, dYp, dh_edge);
   });
 }
 
@@ -682,8 +718,8 @@ template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int G>
 __device__ __forceinline__ void tp_dbl_recv_group(
     const int32_t* __restrict__ src, int i, int e_lo, int e_hi, int64_t edge_begin, int64_t n_chunk_edges,
     int CC, uint32_t c0, bool on, int part, T scale, const T* __restrict__ h, const T* __restrict__ uh,
-    const T* __restrict__ Y, const T* __restrict__ uY, const T* __restrict__ R, const T* __restrict__ uR,
-    const T* __restrict__ Gr, T* __restrict__ g_hat, T* __restrict__ w_hat, T* __restrict__ yhp) {
+    const T* __restrict__ Y, const T* __restrict__ uY, const T* __restrict__ R,
+    const int32_t* __restrict__ Rrow, const T* __restrict__ uR, const T* __restrict__ Gr, T* __restrict__ g_hat, T* __restrict__ w_hat, T* __restrict__ yhp) {
   constexpr int NP = TBL.np, DIN = TBL.din, DSH = TBL.dsh, DOUT = TBL.dout;
   constexpr int NK = BGR.nk[G] > 0 ? BGR.nk[G] : 1;
   static_assert(BGR.ok, "every wave group owns an l1 class");
@@ -736,10 +772,10 @@ __device__ __forceinline__ void tp_dbl_recv_group(
     T y, uy;
   };
   const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
-  auto load_j = [&](int e, int j, Buf& b) __attribute__((always_inline)) {
+  auto load_j = [&](int e, int j, int rr, Buf& b) __attribute__((always_inline)) {
     const T* __restrict__ hj = h + (int64_t)j * DIN * CC;
     const T* __restrict__ uhj = uh + (int64_t)j * DIN * CC;
-    const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
+    const T* __restrict__ re = R + (int64_t)rr * PC;
     const T* __restrict__ ure = uR + (int64_t)e * PC;
     static_for<DIN>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
@@ -839,12 +875,19 @@ __device__ __forceinline__ void tp_dbl_recv_group(
       yhp[((int64_t)part * n_chunk_edges + el) * DSH + (lane >> 2)] = tot;
   };
   if (e_hi - e_lo > 64 * kIdxWindows) {
-    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, uniform(src[e]), b); },
+    edge_loop<Buf>(e_lo, e_hi,
+                   [&](int e, Buf& b) __attribute__((always_inline)) {
+                     load_j(e, uniform(src[e]), r_row(Rrow, edge_begin, e), b);
+                   },
                    compute);
   } else if (e_hi > e_lo) {
-    RowIdx<kIdxWindows> si;
+    RowIdx<kIdxWindows> si, qi;
     si.init(src, e_lo, e_hi, lane);
-    edge_loop<Buf>(e_lo, e_hi, [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, si.get(e - e_lo), b); },
+    qi.init_rows(Rrow, edge_begin, e_lo, e_hi, lane);
+    edge_loop<Buf>(e_lo, e_hi,
+                   [&](int e, Buf& b) __attribute__((always_inline)) {
+                     load_j(e, si.get(e - e_lo), qi.get(e - e_lo), b);
+                   },
                    compute);
   }
   T* __restrict__ gh = g_hat + (int64_t)i * DOUT * CC;
@@ -858,8 +901,8 @@ template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int G>
 __device__ __forceinline__ void tp_dbl_send_group(
     const int32_t* __restrict__ src, const int32_t* __restrict__ rev, int i, int e_lo, int e_hi,
     int64_t edge_begin, int CC, uint32_t c0, bool on, T scale, const T* __restrict__ Y,
-    const T* __restrict__ uY, const T* __restrict__ R, const T* __restrict__ uR,
-    const T* __restrict__ Gr, T* __restrict__ x_hat) {
+    const T* __restrict__ uY, const T* __restrict__ R, const int32_t* __restrict__ Rrow,
+    const T* __restrict__ uR, const T* __restrict__ Gr, T* __restrict__ x_hat) {
   constexpr int NP = TBL.np, DIN = TBL.din, DSH = TBL.dsh, DOUT = TBL.dout;
   static_assert(BGR.ok, "every wave group owns an l1 class");
   const int PC = NP * CC;
@@ -874,9 +917,9 @@ __device__ __forceinline__ void tp_dbl_send_group(
     T y, uy;
   };
   const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
-  auto load_j = [&](int e, int j, int er, Buf& b) __attribute__((always_inline)) {
+  auto load_j = [&](int e, int j, int er, int rr, Buf& b) __attribute__((always_inline)) {
     const T* __restrict__ gj = Gr + (int64_t)j * DOUT * CC;
-    const T* __restrict__ re = R + ((int64_t)e - edge_begin) * PC;
+    const T* __restrict__ re = R + (int64_t)rr * PC;
     const T* __restrict__ urr = uR + (int64_t)er * PC;
     static_for<DOUT>([&](auto oc) {
       constexpr int o = decltype(oc)::value;
@@ -931,14 +974,19 @@ __device__ __forceinline__ void tp_dbl_send_group(
   };
   if (e_hi - e_lo > 64 * kIdxWindows) {
     edge_loop<Buf>(e_lo, e_hi,
-                   [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, uniform(src[e]), uniform(rev[e]), b); },
+                   [&](int e, Buf& b) __attribute__((always_inline)) {
+                     load_j(e, uniform(src[e]), uniform(rev[e]), r_row(Rrow, edge_begin, e), b);
+                   },
                    compute);
   } else if (e_hi > e_lo) {
-    RowIdx<kIdxWindows> si, ri;
+    RowIdx<kIdxWindows> si, ri, qi;
     si.init(src, e_lo, e_hi, lane);
     ri.init(rev, e_lo, e_hi, lane);
+    qi.init_rows(Rrow, edge_begin, e_lo, e_hi, lane);
     edge_loop<Buf>(e_lo, e_hi,
-                   [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, si.get(e - e_lo), ri.get(e - e_lo), b); },
+                   [&](int e, Buf& b) __attribute__((always_inline)) {
+                     load_j(e, si.get(e - e_lo), ri.get(e - e_lo), qi.get(e - e_lo), b);
+                   },
                    compute);
   }
   T* __restrict__ xi = x_hat + (int64_t)i * DIN * CC;
@@ -956,8 +1004,8 @@ __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
 k_tp_dbl_recv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, int64_t row_begin,
               int64_t row_end, int64_t edge_begin, int64_t n_chunk_edges, int C, T scale,
               const T* __restrict__ h, const T* __restrict__ uh, const T* __restrict__ Y,
-              const T* __restrict__ uY, const T* __restrict__ R, const T* __restrict__ uR,
-              const T* __restrict__ Gr, T* __restrict__ g_hat, T* __restrict__ w_hat, T* __restrict__ yhp) {
+              const T* __restrict__ uY, const T* __restrict__ R, const int32_t* __restrict__ Rrow,
+              const T* __restrict__ uR, const T* __restrict__ Gr, T* __restrict__ g_hat, T* __restrict__ w_hat, T* __restrict__ yhp) {
   const int lane = threadIdx.x % kTPWave;
   const int64_t w = xcd_block() * kTPWavesPerBlock + threadIdx.x / kTPWave;
   const int64_t row = row_begin + w / (NG * NWC);
@@ -973,7 +1021,7 @@ k_tp_dbl_recv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
     constexpr int G = decltype(gc)::value;
     if (g == G)
       tp_dbl_recv_group<T, L1, L2, L3, NG, MASKED, G>(src, i, e_lo, e_hi, edge_begin, n_chunk_edges, CC, c0, on,
-                                                      rem, scale, h, uh, Y, uY, R, uR, Gr, g_hat, w_hat, yhp);
+                                                      rem, scale, h, uh, Y, uY, R, Rrow, uR, Gr, g_hat, w_hat, yhp);
   });
 }
 
@@ -982,7 +1030,8 @@ __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
 k_tp_dbl_send(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src,
               const int32_t* __restrict__ rev, int64_t row_begin, int64_t row_end, int64_t edge_begin,
               int C, T scale, const T* __restrict__ Y, const T* __restrict__ uY, const T* __restrict__ R,
-              const T* __restrict__ uR, const T* __restrict__ Gr, T* __restrict__ x_hat) {
+              const int32_t* __restrict__ Rrow, const T* __restrict__ uR, const T* __restrict__ Gr,
+              T* __restrict__ x_hat) {
   const int lane = threadIdx.x % kTPWave;
   const int64_t w = xcd_block() * kTPWavesPerBlock + threadIdx.x / kTPWave;
   const int64_t row = row_begin + w / (NG * NWC);
@@ -998,7 +1047,7 @@ k_tp_dbl_send(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
     constexpr int G = decltype(gc)::value;
     if (g == G)
       tp_dbl_send_group<T, L1, L2, L3, NG, MASKED, G>(src, rev, i, e_lo, e_hi, edge_begin, CC, c0, on, scale, Y,
-                                                      uY, R, uR, Gr, x_hat);
+                                                      uY, R, Rrow, uR, Gr, x_hat);
   });
 }
 

@@ -34,12 +34,12 @@ def torch():
 class Case:
     """Inputs of configuration k on the GPU plus an oracle problem."""
 
-    def __init__(self, k, validate=False, with_grad=True, data=None):
+    def __init__(self, k, validate=False, with_grad=True, data=None, pair=False):
         t = torch()
         self.k = k
         self.d = data if data is not None else workloads.generate(k, with_grad=with_grad)
         self.cfg = self.d["cfg"]
-        self.ctx = tpc.Context(tpc.spec_for(self.cfg, validate))
+        self.ctx = tpc.Context(tpc.spec_for(self.cfg, validate, pair_radial=pair))
         self.layout = paths.Layout(self.cfg["l1max"], self.cfg["sh_lmax"], self.cfg["out_lmax"],
                                    self.cfg["C"], self.cfg.get("sum_paths", False))
         dev = "cuda"

@@ -130,7 +130,7 @@ def test_conv_argument_checks_run_before_device_work():
     lib, h = _raw(tpc.Context(_spec()))
     eb = tpc._EdgeBuffers()
     cell = (ctypes.c_double * 9)(*np.eye(3).reshape(-1).tolist())
-    st = lib.tpc_conv_fwd(h, 10, None, cell, None, None, None, 0, 11, 0, 5, None, None, 1.0, None,
+    st = lib.tpc_conv_fwd(h, 10, None, cell, None, None, None, None, 0, 11, 0, 5, None, None, 1.0, None,
                           ctypes.byref(eb), None, 0, None)
     assert st == 1
     m = lib.tpc_last_error().decode()
@@ -204,13 +204,44 @@ def test_fused_radial_selection_and_edge_buffer_checks():
     lib, h = _raw(fused)
     eb = tpc._EdgeBuffers()
     cell = (ctypes.c_double * 9)(*np.eye(3).reshape(-1).tolist())
-    st = lib.tpc_conv_fwd(h, 10, None, cell, None, None, None, 0, 10, 0, 5, None, None, 1.0, None,
+    st = lib.tpc_conv_fwd(h, 10, None, cell, None, None, None, None, 0, 10, 0, 5, None, None, 1.0, None,
                           ctypes.byref(eb), None, 0, None)
     assert st == 1
     m = lib.tpc_last_error().decode()
     assert "eb.A" in m and "eb.R" not in m
     lib, h = _raw(plain)
-    st = lib.tpc_conv_fwd(h, 10, None, cell, None, None, None, 0, 10, 0, 5, None, None, 1.0, None,
+    st = lib.tpc_conv_fwd(h, 10, None, cell, None, None, None, None, 0, 10, 0, 5, None, None, 1.0, None,
                           ctypes.byref(eb), None, 0, None)
     m = lib.tpc_last_error().decode()
     assert "eb.R" in m and "eb.A" not in m
+
+
+def test_pair_radial_selection_sizes_and_checks():
+    """Shared rows of R (spec.pair_radial): in effect for the unfused network
+    only; the forward then needs rev and eb.Rrow, and its workspace grows by
+    the rows' basis values."""
+    plain, pair = tpc.Context(_spec()), tpc.Context(_spec(pair_radial=1))
+    assert pair.pair_radial and not plain.pair_radial
+    assert pair.sizes["fwd_workspace_bytes_per_edge"] == 8 * 4
+    assert plain.sizes["fwd_workspace_bytes_per_edge"] == 0
+    ne = 100_000
+    grow = pair.workspace_bytes(tpc.OP_FWD, 0, ne) - plain.workspace_bytes(tpc.OP_FWD, 0, ne)
+    assert 32 * ne <= grow <= 32 * ne + 8 * (ne // 4096 + 2) + 512
+    # the fused forward and the tables keep one row per edge
+    assert not tpc.Context(tpc.spec_for(workloads.config(6), fuse_radial=True, pair_radial=True)).pair_radial
+    assert not tpc.Context(tpc.spec_for(workloads.config(1), table=(64, 8), pair_radial=True)).pair_radial
+    lib, h = _raw(pair)
+    eb = tpc._EdgeBuffers()
+    cell = (ctypes.c_double * 9)(*np.eye(3).reshape(-1).tolist())
+    st = lib.tpc_conv_fwd(h, 10, None, cell, None, None, None, None, 0, 10, 0, 5, None, None, 1.0, None,
+                          ctypes.byref(eb), None, 0, None)
+    assert st == 1
+    m = lib.tpc_last_error().decode()
+    assert "rev" in m and "eb.Rrow" in m
+    st = lib.tpc_conv_bwd(h, 10, 5, None, None, None, 0, 10, 0, 5, None, None, 1.0, None,
+                          ctypes.byref(eb), None, None, None, None, None, None, 0, None)
+    assert st == 1 and "eb.Rrow" in lib.tpc_last_error().decode()
+    lib, h = _raw(plain)
+    st = lib.tpc_conv_fwd(h, 10, None, cell, None, None, None, None, 0, 10, 0, 5, None, None, 1.0, None,
+                          ctypes.byref(eb), None, 0, None)
+    assert "eb.Rrow" not in lib.tpc_last_error().decode()

@@ -48,7 +48,7 @@ def test_full_parity(k):
     _, _, Y, ef, R = prob.edge_terms(np.arange(nl.n_edges))
     assert rel(res["eb"].Y.cpu().numpy(), Y) < tol
     assert rel(res["eb"].ef.cpu().numpy(), ef) < tol
-    assert rel(res["eb"].R.cpu().numpy(), R) < tol
+    assert rel(res["eb"].R_per_edge().cpu().numpy(), R) < tol
 
 
 def _sampled_check(case, nl, res, rows, atoms, edges):
@@ -80,13 +80,32 @@ def _samples(case, n_rows, seed, n_edge_rows=16):
     return rows, edges
 
 
+def _both_row_layouts(case, nl, chunks, rows, atoms, edges):
+    """The sampled check with one row of R per edge, then with the rows
+    shared by edge pairs (the layout bench.py times); the second must equal
+    the first bit for bit, since each row comes from the same arithmetic."""
+    t = torch()
+    res = run_chunked(case, nl, chunks=chunks, keep_edges=edges)
+    _sampled_check(case, nl, res, rows, atoms, edges)
+    keep = {k: res[k] for k in ("out", "dh", "forces", "g_edge")}
+    kept_dR = res["dR"]
+    del res
+    case.ctx = tpc.Context(tpc.spec_for(case.cfg, pair_radial=True))
+    assert case.ctx.pair_radial
+    res = run_chunked(case, nl, chunks=chunks, keep_edges=edges)
+    _sampled_check(case, nl, res, rows, atoms, edges)
+    for k, v in keep.items():
+        assert t.equal(res[k], v), k
+    for e in edges:
+        np.testing.assert_array_equal(res["dR"][int(e)], kept_dR[int(e)])
+
+
 def test_medium_parity_sampled():
     case = Case(3)
     nl = case.nbr()
     rows, edges = _samples(case, 96, 11)
     atoms = np.unique(np.concatenate([np.arange(64), _spread(rows, 32)]))   # includes the 0-63 slice
-    res = run_chunked(case, nl, chunks=1, keep_edges=edges)
-    _sampled_check(case, nl, res, rows, atoms, edges)
+    _both_row_layouts(case, nl, 1, rows, atoms, edges)
 
 
 @pytest.mark.timeout(300)   # the oracle's own 19.6 M-edge list takes about 40 s
@@ -95,14 +114,15 @@ def test_large_parity_sampled_chunked():
     nl = case.nbr()
     rows, edges = _samples(case, 40, 12)
     # the 2 receiver chunks bench.py times
-    res = run_chunked(case, nl, chunks=2, keep_edges=edges)
-    _sampled_check(case, nl, res, rows, _spread(rows, 24), edges)
+    _both_row_layouts(case, nl, 2, rows, _spread(rows, 24), edges)
 
 
-def test_chunked_equals_unchunked():
+@pytest.mark.parametrize("pair", [False, True])
+def test_chunked_equals_unchunked(pair):
     case = Case(1)
     nl = case.nbr()
     a = run_chunked(case, nl, chunks=1)
+    case.ctx = tpc.Context(tpc.spec_for(case.cfg, pair_radial=pair))
     b = run_chunked(case, nl, chunks=5)
     for key in ("out", "dh", "forces", "g_edge"):
         assert torch().equal(a[key], b[key]), key

@@ -65,12 +65,18 @@ def test_double_backward_chunked_and_deterministic():
     a = run_double(case, nl, u, chunks=1, keep_edges=np.arange(0, nl.n_edges, 101))
     b = run_double(case, nl, u, chunks=4, keep_edges=np.arange(0, nl.n_edges, 101))
     c = run_double(case, nl, u, chunks=1, keep_edges=np.arange(0, nl.n_edges, 101))
+    # rows of R shared by edge pairs, in 4 chunks: the same bits
+    case.ctx = tpc.Context(tpc.spec_for(case.cfg, pair_radial=True))
+    d = run_double(case, nl, u, chunks=4, keep_edges=np.arange(0, nl.n_edges, 101))
     for key in ("g_hat", "h_hat"):
         assert torch().equal(a[key], b[key]), key
         assert torch().equal(a[key], c[key]), key
+        assert torch().equal(a[key], d[key]), key
     for e in a["Y_hat"]:
         np.testing.assert_array_equal(a["Y_hat"][e], b["Y_hat"][e])
         np.testing.assert_array_equal(a["R_hat"][e], c["R_hat"][e])
+        np.testing.assert_array_equal(a["Y_hat"][e], d["Y_hat"][e])
+        np.testing.assert_array_equal(a["R_hat"][e], d["R_hat"][e])
 
 
 def test_double_backward_refuses_summed_outputs():

@@ -46,10 +46,10 @@ def _step(case, nl, b, s):
 KEYS = ("out", "dh", "forces", "g_edge")
 
 
-@pytest.mark.parametrize("chunks", [1, 3])
-def test_graph_replay_matches_eager(chunks):
+@pytest.mark.parametrize("chunks,pair", [(1, False), (3, False), (1, True), (3, True)])
+def test_graph_replay_matches_eager(chunks, pair):
     t = torch()
-    case = Case(1)
+    case = Case(1, pair=pair)
     nl = case.nbr()
     s = case.scale(nl)
     b = _buffers(case, nl, chunks)
@@ -75,6 +75,8 @@ def test_graph_replay_matches_eager(chunks):
         # own, and wait
         for x in [b[k] for k in KEYS] + [b["dR"], b["dh_edge"], b["eb"].Y, b["eb"].ef, b["eb"].rv, b["eb"].R]:
             x.fill_(float("nan"))
+        if b["eb"].Rrow is not None:
+            b["eb"].Rrow.fill_(0)     # a map the replay must rebuild (row 0: in bounds)
         case.ctx.conv_fwd(case.pos, case.cell, nl, case.h, case.W, 2.0 * s, out=t.empty_like(b["out"]))
         t.cuda.synchronize()
         say(f"[gpu] replay {rep} cfg=1 chunks={chunks}")

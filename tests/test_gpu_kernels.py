@@ -87,7 +87,7 @@ def test_instantiation_parity(dt, l1, l2, l3, C, summed, H, NH):
         "forces": rel(res["forces"].cpu().numpy(), b["F"]),
     }
     _, _, Y, ef, R = prob.edge_terms(np.arange(nl.n_edges))
-    errs["R"] = rel(res["eb"].R.cpu().numpy(), R)
+    errs["R"] = rel(res["eb"].R_per_edge().cpu().numpy(), R)
     if not summed:
         u = cotangents(case, nl.n_edges, seed + 500)
         dres = run_double(case, nl, u, keep_edges=np.arange(nl.n_edges))

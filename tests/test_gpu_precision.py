@@ -59,7 +59,7 @@ def test_cancelling_last_layer_within_the_float32_bound(fp32_only):
         a = radial.silu(a @ Wk)
     dRdr = radial.radial_weights_dr(r, W, case.cfg["r_cut"])
     bound = 2.0 * a.shape[1] * 2.0 ** -24 * (np.abs(a) @ np.abs(W[-1])) + 8.0 * 2.0 ** -24 * np.abs(r[:, None] * dRdr)
-    got = res["eb"].R.cpu().numpy().astype(np.float64)
+    got = res["eb"].R_per_edge().cpu().numpy().astype(np.float64)
     err = np.abs(got - R)
     ratio = float((err / bound).max())
     cancel = float(np.median((np.abs(a) @ np.abs(W[-1])) / np.maximum(np.abs(R), 1e-30)))

@@ -20,7 +20,7 @@ def _fwd_both(case, nl, s):
     ctx, lib = case.ctx, tpc.library()
     lib.tpc_conv_fwd_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                          ctypes.POINTER(ctypes.c_double), ctypes.c_void_p, ctypes.c_void_p,
-                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
                                          ctypes.c_double, ctypes.c_void_p, ctypes.POINTER(tpc._EdgeBuffers),
                                          ctypes.c_void_p]
@@ -36,7 +36,8 @@ def _fwd_both(case, nl, s):
     say(f"[gpu] tpc_conv_fwd_noalloc N={N} E={E}")
     st = lib.tpc_conv_fwd_noalloc(ctx._h, N, ctypes.c_void_p(case.pos.data_ptr()), tpc._cell_arg(case.cell),
                                   ctypes.c_void_p(nl.row_ptr.data_ptr()), ctypes.c_void_p(nl.src.data_ptr()),
-                                  ctypes.c_void_p(nl.shift.data_ptr()), 0, N, 0, E,
+                                  ctypes.c_void_p(nl.shift.data_ptr()), ctypes.c_void_p(nl.rev.data_ptr()),
+                                  0, N, 0, E,
                                   ctypes.c_void_p(case.h.data_ptr()), wp, float(s),
                                   ctypes.c_void_p(out.data_ptr()), ctypes.byref(ebc), tpc._stream())
     assert st == 0, lib.tpc_last_error().decode()
