@@ -147,7 +147,8 @@ typedef struct tpc_spec {
                                 waves per SIMD) and is there for callers
                                 short of memory. */
   int pair_radial;           /* 0 (default): one row of R per edge.  Nonzero,
-                                with the radial network unfused and no table:
+                                with the radial network unfused, no table and
+                                64 or 128 channels:
                                 an edge and its reverse share one row of R.
                                 The radial weights depend on the edge length
                                 only (FlashCart section 2, distance-dependent

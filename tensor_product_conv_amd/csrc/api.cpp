@@ -458,7 +458,9 @@ tpc_status tpc_ctx_create(const tpc_spec* spec, tpc_ctx** out) {
   c->tsize = s.dtype == TPC_F64 ? 8 : 4;
   c->table = s.radial_table_pieces > 0;
   c->fused = fused_radial_ok(s, tab, H);
-  c->pair = s.pair_radial != 0 && !c->fused && !c->table;
+  // shared rows are built for the unmasked tensor-product kernels (64 or 128
+  // channels)
+  c->pair = s.pair_radial != 0 && !c->fused && !c->table && s.channels >= 64;
   *out = c;
   return TPC_OK;
 }

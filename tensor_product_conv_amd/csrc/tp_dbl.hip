@@ -16,22 +16,29 @@ hipError_t tp_dbl_cfg(const TPArgs& a, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (a.sum_paths) return hipErrorInvalidValue;
   const T sc = (T)a.scale;
-#define TPC_GO(MASK, NWC)                                                                         \
+#define TPC_GO_P(MASK, NWC, PAIR)                                                                 \
   do {                                                                                            \
     const unsigned blocks = (unsigned)((rows * NG * NWC + kTPWavesPerBlock - 1) / kTPWavesPerBlock); \
-    k_tp_dbl_recv<T, L1, L2, L3, NG, MASK, NWC><<<blocks, kTPWave * kTPWavesPerBlock, 0, s>>>(    \
+    k_tp_dbl_recv<T, L1, L2, L3, NG, MASK, NWC, PAIR><<<blocks, kTPWave * kTPWavesPerBlock, 0, s>>>(    \
         a.row_ptr, a.src, a.row_begin, a.row_end, a.edge_begin, a.n_chunk_edges, a.C, sc,        \
         static_cast<const T*>(a.h), static_cast<const T*>(a.uh), static_cast<const T*>(a.Y),     \
         static_cast<const T*>(a.uY), static_cast<const T*>(a.R), a.Rrow,                         \
         static_cast<const T*>(a.uR), static_cast<const T*>(a.G), static_cast<T*>(a.g_hat), static_cast<T*>(a.w_hat),          \
         static_cast<T*>(a.dY));                                                                   \
-    k_tp_dbl_send<T, L1, L2, L3, NG, MASK, NWC><<<blocks, kTPWave * kTPWavesPerBlock, 0, s>>>(    \
+    k_tp_dbl_send<T, L1, L2, L3, NG, MASK, NWC, PAIR><<<blocks, kTPWave * kTPWavesPerBlock, 0, s>>>(    \
         a.row_ptr, a.src, a.rev, a.row_begin, a.row_end, a.edge_begin, a.C, sc,                  \
         static_cast<const T*>(a.Y), static_cast<const T*>(a.uY), static_cast<const T*>(a.R),     \
         a.Rrow, static_cast<const T*>(a.uR), static_cast<const T*>(a.G), static_cast<T*>(a.x_hat));      \
   } while (0)
+  // R rows shared by edge pairs (a.Rrow): unmasked channel counts only
+#define TPC_GO(MASK, NWC)                  \
+  do {                                     \
+    if (a.Rrow) TPC_GO_P(MASK, NWC, true); \
+    else TPC_GO_P(MASK, NWC, false);       \
+  } while (0)
   if (a.C < 64) {
-    TPC_GO(true, 1);
+    if (a.Rrow) return hipErrorInvalidValue;
+    TPC_GO_P(true, 1, false);
   } else if (a.C == 64) {
     TPC_GO(false, 1);
   } else if (a.C == 128) {
@@ -40,6 +47,7 @@ hipError_t tp_dbl_cfg(const TPArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   }
 #undef TPC_GO
+#undef TPC_GO_P
   return hipGetLastError();
 }
 

@@ -26,13 +26,21 @@ hipError_t fwd_launch(const TPArgs& a, hipStream_t s) {
   const T* Y = static_cast<const T*>(a.Y);
   const T* R = static_cast<const T*>(a.R);
   T* out = static_cast<T*>(a.out);
-#define TPC_GO(NG, MASK, NWC)                                                                    \
-  k_tp_fwd<T, L1, L2, L3, SUM, 1, NG, MASK, NWC>                                                \
+#define TPC_GO_P(NG, MASK, NWC, PAIR)                                                            \
+  k_tp_fwd<T, L1, L2, L3, SUM, 1, NG, MASK, NWC, PAIR>                                          \
       <<<(unsigned)((rows * NG * NWC + kTPWavesPerBlock - 1) / kTPWavesPerBlock),               \
          kTPWave * kTPWavesPerBlock, 0, s>>>(a.row_ptr, a.src, a.row_begin, a.row_end,           \
                                              a.edge_begin, a.C, sc, h, Y, R, a.Rrow, out)
+  // R rows shared by edge pairs (a.Rrow) are built for the unmasked channel
+  // counts only
+#define TPC_GO(NG, MASK, NWC)                         \
+  do {                                                \
+    if (a.Rrow) TPC_GO_P(NG, MASK, NWC, true);        \
+    else TPC_GO_P(NG, MASK, NWC, false);              \
+  } while (0)
   if (masked) {
-    TPC_GO(1, true, 1);
+    if (a.Rrow) return hipErrorInvalidValue;
+    TPC_GO_P(1, true, 1, false);
   } else if (a.C == 128) {
     TPC_GO(1, false, 2);
   } else {
@@ -41,6 +49,7 @@ hipError_t fwd_launch(const TPArgs& a, hipStream_t s) {
     else TPC_GO(1, false, 1);
   }
 #undef TPC_GO
+#undef TPC_GO_P
   return hipGetLastError();
 }
 

@@ -232,7 +232,7 @@ __device__ __forceinline__ void tp_fwd_edge(const T (&hh)[kTable<L1, L2, L3, SUM
   });
 }
 
-template <typename T, int L1, int L2, int L3, bool SUM, int CPL, int NG, bool MASKED, int G>
+template <typename T, int L1, int L2, int L3, bool SUM, int CPL, int NG, bool MASKED, int G, bool PAIR>
 __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, int e_lo, int e_hi,
                                              int64_t edge_begin, int C, uint32_t c0, bool on,
                                              const T* __restrict__ h, const T* __restrict__ Y,
@@ -264,7 +264,7 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
   const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
   auto load_j = [&](int e, int j, int rr, Buf& b) __attribute__((always_inline)) {
     const T* __restrict__ hj = h + (int64_t)j * DIN * C;
-    const T* __restrict__ re = R + (int64_t)rr * PC;
+    const T* __restrict__ re = PAIR ? R + (int64_t)rr * PC : R + ((int64_t)e - edge_begin) * PC;
     // only the rows of the l1 ranks this group's paths read
     static_for<DIN>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
@@ -287,18 +287,25 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
   if (e_hi - e_lo > 64 * kIdxWindows) {
     edge_loop<Buf>(e_lo, e_hi,
                    [&](int e, Buf& b) __attribute__((always_inline)) {
-                     load_j(e, uniform(src[e]), r_row(Rrow, edge_begin, e), b);
+                     load_j(e, uniform(src[e]), PAIR ? r_row(Rrow, edge_begin, e) : 0, b);
                    },
                    compute);
   } else if (e_hi > e_lo) {
-    RowIdx<kIdxWindows> si, qi;
+    RowIdx<kIdxWindows> si;
     si.init(src, e_lo, e_hi, lane);
-    qi.init_rows(Rrow, edge_begin, e_lo, e_hi, lane);
-    edge_loop<Buf>(e_lo, e_hi,
-                   [&](int e, Buf& b) __attribute__((always_inline)) {
-                     load_j(e, si.get(e - e_lo), qi.get(e - e_lo), b);
-                   },
-                   compute);
+    if constexpr (PAIR) {
+      RowIdx<kIdxWindows> qi;
+      qi.init_rows(Rrow, edge_begin, e_lo, e_hi, lane);
+      edge_loop<Buf>(e_lo, e_hi,
+                     [&](int e, Buf& b) __attribute__((always_inline)) {
+                       load_j(e, si.get(e - e_lo), qi.get(e - e_lo), b);
+                     },
+                     compute);
+    } else {
+      edge_loop<Buf>(e_lo, e_hi,
+                     [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, si.get(e - e_lo), 0, b); },
+                     compute);
+    }
   }
   static_for<NP>([&](auto pc) {
     constexpr int p = decltype(pc)::value;
@@ -315,7 +322,7 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
   });
 }
 
-template <typename T, int L1, int L2, int L3, bool SUM, int CPL, int NG, bool MASKED, int NWC = 1>
+template <typename T, int L1, int L2, int L3, bool SUM, int CPL, int NG, bool MASKED, int NWC, bool PAIR>
 __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
 k_tp_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, int64_t row_begin,
          int64_t row_end, int64_t edge_begin, int C, T scale, const T* __restrict__ h,
@@ -337,7 +344,7 @@ k_tp_fwd(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, i
   static_for<NG>([&](auto gc) {
     constexpr int G = decltype(gc)::value;
     if (g == G)
-      tp_fwd_group<T, L1, L2, L3, SUM, CPL, NG, MASKED, G>(src, e_lo, e_hi, edge_begin, CC, c0, on, h, Y,
+      tp_fwd_group<T, L1, L2, L3, SUM, CPL, NG, MASKED, G, PAIR>(src, e_lo, e_hi, edge_begin, CC, c0, on, h, Y,
                                                      R, Rrow, oi, scale);
   });
 }
@@ -445,7 +452,7 @@ __device__ __forceinline__ T wave_reduce_scatter16(const T (&v)[16]) {
 //                                      index)
 #define TBL kTable<L1, L2, L3, SUM>
 #define BGR kBwdGroups<L1, L2, L3, SUM, NG>
-template <typename T, int L1, int L2, int L3, bool SUM, bool MASKED, int NG, int G>
+template <typename T, int L1, int L2, int L3, bool SUM, bool MASKED, int NG, int G, bool PAIR>
 __device__ __forceinline__ void tp_bwd_edge_group(const int32_t* __restrict__ src, int i, int e_lo, int e_hi,
                                                   int64_t edge_begin, int64_t n_chunk_edges, int CC, uint32_t c0,
                                                   bool on, int part, T scale, const T* __restrict__ h,
@@ -481,7 +488,7 @@ __device__ __forceinline__ void tp_bwd_edge_group(const int32_t* __restrict__ sr
   const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
   auto load_j = [&](int e, int j, int rr, Buf& b) __attribute__((always_inline)) {
     const T* __restrict__ hj = h + (int64_t)j * DIN * CC;
-    const T* __restrict__ re = R + (int64_t)rr * PC;
+    const T* __restrict__ re = PAIR ? R + (int64_t)rr * PC : R + ((int64_t)e - edge_begin) * PC;
     static_for<DIN>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
       constexpr int l1 = m >= 9 ? 3 : m >= 4 ? 2 : m >= 1 ? 1 : 0;
@@ -566,18 +573,25 @@ __device__ __forceinline__ void tp_bwd_edge_group(const int32_t* __restrict__ sr
   if (e_hi - e_lo > 64 * kIdxWindows) {
     edge_loop<Buf>(e_lo, e_hi,
                    [&](int e, Buf& b) __attribute__((always_inline)) {
-                     load_j(e, uniform(src[e]), r_row(Rrow, edge_begin, e), b);
+                     load_j(e, uniform(src[e]), PAIR ? r_row(Rrow, edge_begin, e) : 0, b);
                    },
                    compute);
   } else {
-    RowIdx<kIdxWindows> si, qi;
+    RowIdx<kIdxWindows> si;
     si.init(src, e_lo, e_hi, lane);
-    qi.init_rows(Rrow, edge_begin, e_lo, e_hi, lane);
-    edge_loop<Buf>(e_lo, e_hi,
-                   [&](int e, Buf& b) __attribute__((always_inline)) {
-                     load_j(e, si.get(e - e_lo), qi.get(e - e_lo), b);
-                   },
-                   compute);
+    if constexpr (PAIR) {
+      RowIdx<kIdxWindows> qi;
+      qi.init_rows(Rrow, edge_begin, e_lo, e_hi, lane);
+      edge_loop<Buf>(e_lo, e_hi,
+                     [&](int e, Buf& b) __attribute__((always_inline)) {
+                       load_j(e, si.get(e - e_lo), qi.get(e - e_lo), b);
+                     },
+                     compute);
+    } else {
+      edge_loop<Buf>(e_lo, e_hi,
+                     [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, si.get(e - e_lo), 0, b); },
+                     compute);
+    }
   }
 }
 #undef TBL
@@ -585,7 +599,7 @@ __device__ __forceinline__ void tp_bwd_edge_group(const int32_t* __restrict__ sr
 
 // Wave w of the grid: row w / (NG * NWC), then group and channel slice;
 // partial dY slice (channel slice) * NG + group.
-template <typename T, int L1, int L2, int L3, bool SUM, bool MASKED, int NG, int NWC>
+template <typename T, int L1, int L2, int L3, bool SUM, bool MASKED, int NG, int NWC, bool PAIR>
 __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
 k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, int64_t row_begin,
               int64_t row_end, int64_t edge_begin, int64_t n_chunk_edges, int C, T scale, const T* __restrict__ h,
@@ -608,7 +622,7 @@ k_tp_bwd_edge(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
   static_for<NG>([&](auto gc) {
     constexpr int G = decltype(gc)::value;
     if (g == G)
-      tp_bwd_edge_group<T, L1, L2, L3, SUM, MASKED, NG, G>(src, i, e_lo, e_hi, edge_begin, n_chunk_edges, CC, c0,
+      tp_bwd_edge_group<T, L1, L2, L3, SUM, MASKED, NG, G, PAIR>(src, i, e_lo, e_hi, edge_begin, n_chunk_edges, CC, c0,
                                                            on, part, scale, h, Y, R, Rrow, Gr, dR, dYp, dh_edge);
   });
 }
@@ -714,7 +728,7 @@ k_dh_gather_chunk(int64_t n, int din_c, const int32_t* __restrict__ row_ptr, con
 // g_hat, so the waves of a row write disjoint rows.
 #define TBL kTable<L1, L2, L3, false>
 #define BGR kBwdGroups<L1, L2, L3, false, NG>
-template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int G>
+template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int G, bool PAIR>
 __device__ __forceinline__ void tp_dbl_recv_group(
     const int32_t* __restrict__ src, int i, int e_lo, int e_hi, int64_t edge_begin, int64_t n_chunk_edges,
     int CC, uint32_t c0, bool on, int part, T scale, const T* __restrict__ h, const T* __restrict__ uh,
@@ -775,7 +789,7 @@ __device__ __forceinline__ void tp_dbl_recv_group(
   auto load_j = [&](int e, int j, int rr, Buf& b) __attribute__((always_inline)) {
     const T* __restrict__ hj = h + (int64_t)j * DIN * CC;
     const T* __restrict__ uhj = uh + (int64_t)j * DIN * CC;
-    const T* __restrict__ re = R + (int64_t)rr * PC;
+    const T* __restrict__ re = PAIR ? R + (int64_t)rr * PC : R + ((int64_t)e - edge_begin) * PC;
     const T* __restrict__ ure = uR + (int64_t)e * PC;
     static_for<DIN>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
@@ -877,18 +891,25 @@ __device__ __forceinline__ void tp_dbl_recv_group(
   if (e_hi - e_lo > 64 * kIdxWindows) {
     edge_loop<Buf>(e_lo, e_hi,
                    [&](int e, Buf& b) __attribute__((always_inline)) {
-                     load_j(e, uniform(src[e]), r_row(Rrow, edge_begin, e), b);
+                     load_j(e, uniform(src[e]), PAIR ? r_row(Rrow, edge_begin, e) : 0, b);
                    },
                    compute);
   } else if (e_hi > e_lo) {
-    RowIdx<kIdxWindows> si, qi;
+    RowIdx<kIdxWindows> si;
     si.init(src, e_lo, e_hi, lane);
-    qi.init_rows(Rrow, edge_begin, e_lo, e_hi, lane);
-    edge_loop<Buf>(e_lo, e_hi,
-                   [&](int e, Buf& b) __attribute__((always_inline)) {
-                     load_j(e, si.get(e - e_lo), qi.get(e - e_lo), b);
-                   },
-                   compute);
+    if constexpr (PAIR) {
+      RowIdx<kIdxWindows> qi;
+      qi.init_rows(Rrow, edge_begin, e_lo, e_hi, lane);
+      edge_loop<Buf>(e_lo, e_hi,
+                     [&](int e, Buf& b) __attribute__((always_inline)) {
+                       load_j(e, si.get(e - e_lo), qi.get(e - e_lo), b);
+                     },
+                     compute);
+    } else {
+      edge_loop<Buf>(e_lo, e_hi,
+                     [&](int e, Buf& b) __attribute__((always_inline)) { load_j(e, si.get(e - e_lo), 0, b); },
+                     compute);
+    }
   }
   T* __restrict__ gh = g_hat + (int64_t)i * DOUT * CC;
   static_for<DOUT>([&](auto oc) {
@@ -897,7 +918,7 @@ __device__ __forceinline__ void tp_dbl_recv_group(
   });
 }
 
-template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int G>
+template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int G, bool PAIR>
 __device__ __forceinline__ void tp_dbl_send_group(
     const int32_t* __restrict__ src, const int32_t* __restrict__ rev, int i, int e_lo, int e_hi,
     int64_t edge_begin, int CC, uint32_t c0, bool on, T scale, const T* __restrict__ Y,
@@ -919,7 +940,7 @@ __device__ __forceinline__ void tp_dbl_send_group(
   const int ylane = (lane & 15) < DSH ? (lane & 15) : DSH - 1;
   auto load_j = [&](int e, int j, int er, int rr, Buf& b) __attribute__((always_inline)) {
     const T* __restrict__ gj = Gr + (int64_t)j * DOUT * CC;
-    const T* __restrict__ re = R + (int64_t)rr * PC;
+    const T* __restrict__ re = PAIR ? R + (int64_t)rr * PC : R + ((int64_t)e - edge_begin) * PC;
     const T* __restrict__ urr = uR + (int64_t)er * PC;
     static_for<DOUT>([&](auto oc) {
       constexpr int o = decltype(oc)::value;
@@ -975,19 +996,28 @@ __device__ __forceinline__ void tp_dbl_send_group(
   if (e_hi - e_lo > 64 * kIdxWindows) {
     edge_loop<Buf>(e_lo, e_hi,
                    [&](int e, Buf& b) __attribute__((always_inline)) {
-                     load_j(e, uniform(src[e]), uniform(rev[e]), r_row(Rrow, edge_begin, e), b);
+                     load_j(e, uniform(src[e]), uniform(rev[e]), PAIR ? r_row(Rrow, edge_begin, e) : 0, b);
                    },
                    compute);
   } else if (e_hi > e_lo) {
-    RowIdx<kIdxWindows> si, ri, qi;
+    RowIdx<kIdxWindows> si, ri;
     si.init(src, e_lo, e_hi, lane);
     ri.init(rev, e_lo, e_hi, lane);
-    qi.init_rows(Rrow, edge_begin, e_lo, e_hi, lane);
-    edge_loop<Buf>(e_lo, e_hi,
-                   [&](int e, Buf& b) __attribute__((always_inline)) {
-                     load_j(e, si.get(e - e_lo), ri.get(e - e_lo), qi.get(e - e_lo), b);
-                   },
-                   compute);
+    if constexpr (PAIR) {
+      RowIdx<kIdxWindows> qi;
+      qi.init_rows(Rrow, edge_begin, e_lo, e_hi, lane);
+      edge_loop<Buf>(e_lo, e_hi,
+                     [&](int e, Buf& b) __attribute__((always_inline)) {
+                       load_j(e, si.get(e - e_lo), ri.get(e - e_lo), qi.get(e - e_lo), b);
+                     },
+                     compute);
+    } else {
+      edge_loop<Buf>(e_lo, e_hi,
+                     [&](int e, Buf& b) __attribute__((always_inline)) {
+                       load_j(e, si.get(e - e_lo), ri.get(e - e_lo), 0, b);
+                     },
+                     compute);
+    }
   }
   T* __restrict__ xi = x_hat + (int64_t)i * DIN * CC;
   static_for<DIN>([&](auto mc) {
@@ -999,7 +1029,7 @@ __device__ __forceinline__ void tp_dbl_send_group(
 #undef TBL
 #undef BGR
 
-template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int NWC>
+template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int NWC, bool PAIR>
 __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
 k_tp_dbl_recv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src, int64_t row_begin,
               int64_t row_end, int64_t edge_begin, int64_t n_chunk_edges, int C, T scale,
@@ -1020,12 +1050,12 @@ k_tp_dbl_recv(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
   static_for<NG>([&](auto gc) {
     constexpr int G = decltype(gc)::value;
     if (g == G)
-      tp_dbl_recv_group<T, L1, L2, L3, NG, MASKED, G>(src, i, e_lo, e_hi, edge_begin, n_chunk_edges, CC, c0, on,
+      tp_dbl_recv_group<T, L1, L2, L3, NG, MASKED, G, PAIR>(src, i, e_lo, e_hi, edge_begin, n_chunk_edges, CC, c0, on,
                                                       rem, scale, h, uh, Y, uY, R, Rrow, uR, Gr, g_hat, w_hat, yhp);
   });
 }
 
-template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int NWC>
+template <typename T, int L1, int L2, int L3, int NG, bool MASKED, int NWC, bool PAIR>
 __global__ void __launch_bounds__(kTPWave * kTPWavesPerBlock)
 k_tp_dbl_send(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ src,
               const int32_t* __restrict__ rev, int64_t row_begin, int64_t row_end, int64_t edge_begin,
@@ -1046,7 +1076,7 @@ k_tp_dbl_send(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ s
   static_for<NG>([&](auto gc) {
     constexpr int G = decltype(gc)::value;
     if (g == G)
-      tp_dbl_send_group<T, L1, L2, L3, NG, MASKED, G>(src, rev, i, e_lo, e_hi, edge_begin, CC, c0, on, scale, Y,
+      tp_dbl_send_group<T, L1, L2, L3, NG, MASKED, G, PAIR>(src, rev, i, e_lo, e_hi, edge_begin, CC, c0, on, scale, Y,
                                                       uY, R, Rrow, uR, Gr, x_hat);
   });
 }

@@ -230,6 +230,9 @@ def test_pair_radial_selection_sizes_and_checks():
     # the fused forward and the tables keep one row per edge
     assert not tpc.Context(tpc.spec_for(workloads.config(6), fuse_radial=True, pair_radial=True)).pair_radial
     assert not tpc.Context(tpc.spec_for(workloads.config(1), table=(64, 8), pair_radial=True)).pair_radial
+    # nor do the masked kernels of fewer than 64 channels
+    assert not tpc.Context(_spec(pair_radial=1, channels=32,
+                                 layer_dims=[8, 64, 64, 64, 10 * 32])).pair_radial
     lib, h = _raw(pair)
     eb = tpc._EdgeBuffers()
     cell = (ctypes.c_double * 9)(*np.eye(3).reshape(-1).tolist())
