@@ -64,15 +64,21 @@ def test_row_map_and_rows(chunks):
 
 
 def test_rows_against_the_oracle():
-    case = Case(0, pair=True)                 # float64
+    import workloads
+    # the tiny geometry in float64 at 64 channels (shared rows take the
+    # unmasked kernels, 64 or 128 channels)
+    case = Case(0, data=workloads.variant(0, 64, 1, 2, 1, [16], "float64", 4242), pair=True)
     assert case.ctx.pair_radial
     nl = case.nbr()
-    _, eb = case.ctx.conv_fwd(case.pos, case.cell, nl, case.h, case.W, case.scale(nl))
+    out, eb = case.ctx.conv_fwd(case.pos, case.cell, nl, case.h, case.W, case.scale(nl))
     torch().cuda.synchronize()
     ref = case.oracle_csr()
+    for a, b in zip((nl.row_ptr.cpu().numpy(), nl.src.cpu().numpy(), nl.shift.cpu().numpy()), ref):
+        np.testing.assert_array_equal(a, b)
     prob = case.oracle(ref)
     _, _, _, _, R = prob.edge_terms(np.arange(nl.n_edges))
     assert rel(eb.R_per_edge().cpu().numpy(), R) < TOL["float64"]
+    assert rel(out.cpu().numpy(), prob.forward()) < TOL["float64"]
     assert int(eb.Rrow[nl.n_edges].item()) * 2 == nl.n_edges
 
 
