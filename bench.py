@@ -10,7 +10,8 @@ C = 128, node irreps 0e+1o+2e, harmonics l <= 3, outputs l <= 3, radial MLP
 atoms, C = 128) and the large fcc system (262,144 atoms, C = 64, about
 19.8 M edges, processed in 2 receiver chunks) are the other lines.  Inputs
 are resident in HBM before timing starts.  The metric is directed edges per
-second through the step.
+second through the step.  An edge and its reverse share one row of radial
+weights (spec.pair_radial); --per-edge-radial times one row per edge.
 
 Per-kernel durations come from HIP events the library records around each
 launch on the launch stream during the timed steps; the dominant kernel's

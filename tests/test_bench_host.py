@@ -137,3 +137,17 @@ def test_more_than_one_gpu_is_refused_before_any_work(capsys, monkeypatch):
     monkeypatch.setenv("WORLD_SIZE", "4")
     assert bench.main([]) == 2
     assert "WORLD_SIZE=4" in capsys.readouterr().out
+
+
+def test_radial_forward_counts_one_row_per_written_row(medium):
+    """With rows shared by edge pairs the radial network writes one row per
+    pair: its algorithmic bytes and flops follow the row count, and the
+    tensor products' reads of R (one row per edge) do not change."""
+    cfg, ctx = medium
+    N, E = 32768, 2_934_240
+    per_edge = bench.algorithmic("radial_fwd", N, E, cfg, ctx)
+    shared = bench.algorithmic("radial_fwd", N, E, dict(cfg, _R_rows=E // 2), ctx)
+    assert shared[0] * 2 == per_edge[0] and shared[1] * 2 == per_edge[1]
+    assert per_edge[0] == E * 4 * (8 + ctx.r_width)
+    for k in ("tp_fwd", "tp_bwd_edge"):
+        assert bench.algorithmic(k, N, E, dict(cfg, _R_rows=E // 2), ctx) == bench.algorithmic(k, N, E, cfg, ctx)
