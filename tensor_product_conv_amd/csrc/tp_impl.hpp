@@ -274,7 +274,12 @@ __device__ __forceinline__ void tp_fwd_group(const int32_t* __restrict__ src, in
     });
     static_for<NP>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
-      if constexpr (kGroups<L1, L2, L3, SUM, NG, CPL>.group[p] == G) ld_vec_nt<T, CPL>(re, p * C + c0, on, b.r[p], MASKED);
+      // a shared row is read twice (once per edge of its pair), so it is
+      // loaded through the caches, where the partner row may still find it
+      if constexpr (kGroups<L1, L2, L3, SUM, NG, CPL>.group[p] == G) {
+        if constexpr (PAIR) ld_vec<T, CPL>(re, p * C + c0, on, b.r[p], MASKED);
+        else ld_vec_nt<T, CPL>(re, p * C + c0, on, b.r[p], MASKED);
+      }
     });
     b.y = Y[((int64_t)e - edge_begin) * DSH + ylane];
   };
@@ -496,7 +501,8 @@ __device__ __forceinline__ void tp_bwd_edge_group(const int32_t* __restrict__ sr
     });
     static_for<NP>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
-      if constexpr (BGR.group[p] == G) b.r[p] = ldc_nt<NWM>(re, p * CC + c0, on);
+      // shared rows through the caches (read once per edge of the pair)
+      if constexpr (BGR.group[p] == G) b.r[p] = PAIR ? ldc<NWM>(re, p * CC + c0, on) : ldc_nt<NWM>(re, p * CC + c0, on);
     });
     b.y = Y[((int64_t)e - edge_begin) * DSH + ylane];
   };
