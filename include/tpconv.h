@@ -339,6 +339,7 @@ tpc_status tpc_conv_fwd_noalloc(const tpc_ctx* ctx, int64_t n_atoms, const doubl
  *   rev       [n_edges] int32 from tpc_nbr_build
  *   grad_out  G [n_atoms][d_out][C], device
  *   eb        per-edge buffers of the same chunk, as written by tpc_conv_fwd
+ *             (with info.pair_radial its Rrow map too: each edge's row of R)
  *   dR        [E_chunk][P*C] device, nullable (then kept in the workspace):
  *             dL/dR, the inner product of G with the unweighted product
  *             (FlashCart section 3, "Symbolic derivatives")
@@ -393,7 +394,9 @@ tpc_status tpc_conv_bwd(const tpc_ctx* ctx, int64_t n_atoms, int64_t n_edges,
  * edge's cotangents are read at rev[e]); every sum has a fixed order, no
  * atomics.
  *   rev       [n_edges] int32 from tpc_nbr_build
- *   h, grad_out, eb (Y and R of the chunk)   as for tpc_conv_bwd
+ *   h, grad_out, eb (Y and R of the chunk, and Rrow with info.pair_radial)
+ *             as for tpc_conv_bwd; R_hat stays per edge (a caller that wants
+ *             the gradient of a shared row adds the two edges' rows)
  *   u_dh      [n_atoms][d_in][C] device
  *   u_dY      [n_edges][d_sh] device, every edge (absolute index: the sender
  *             side reads it at reverse edges outside the chunk)
