@@ -808,8 +808,7 @@ __device__ __forceinline__ void tp_dbl_recv_group(
     static_for<NP>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
       if constexpr (BGR.group[p] == G) {
-        // shared rows through the caches (read once per edge of the pair)
-        b.r[p] = PAIR ? ldc<MASKED ? 0 : 1>(re, p * CC + c0, on) : ldc_nt<MASKED ? 0 : 1>(re, p * CC + c0, on);
+        b.r[p] = ldc_nt<MASKED ? 0 : 1>(re, p * CC + c0, on);
         b.ur[p] = ldc_nt<MASKED ? 0 : 1>(ure, p * CC + c0, on);
       }
     });
@@ -956,7 +955,7 @@ __device__ __forceinline__ void tp_dbl_send_group(
     static_for<NP>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
       if constexpr (BGR.group[p] == G) {
-        b.r[p] = PAIR ? ldc<MASKED ? 0 : 1>(re, p * CC + c0, on) : ldc_nt<MASKED ? 0 : 1>(re, p * CC + c0, on);
+        b.r[p] = ldc_nt<MASKED ? 0 : 1>(re, p * CC + c0, on);
         b.ur[p] = ldc<MASKED ? 0 : 1>(urr, p * CC + c0, on);
       }
     });
